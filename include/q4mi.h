@@ -1,0 +1,213 @@
+/*
+ * q4mi.h -- C ABI of libq4mi.so: W4A16 skinny GEMMs (NVFP4 and MLX-style
+ * affine 4-bit) and a grouped top-k MoE layer for AMD MI355X (gfx950).
+ *
+ * Pages that define the operations:
+ *   [README] gemma-cuda-hybrid README, "Everything it has" and "Why it's
+ *            NVIDIA-only": NVFP4 W4A16 decode (E2M1 codes, E4M3 scale per
+ *            16 weights, fp32 global scale), one GEMM for every M <= 16
+ *            product, weights repacked offline into the matrix-unit operand
+ *            order, a grouped MoE over 128 experts top-8 plus one shared.
+ *   [ISSUE]  TensorFold issue "Proposal: Gemma 4 on CUDA", "Why now":
+ *            qlinear's MLX affine 4-bit path (groups of 64), activation rows
+ *            with 64-value group sums, tree_round's argmax; "Gates": the
+ *            float64 bound per kernel.
+ *   [DOC]    TensorSharp docs, Gemma 4, 3.2 "Per-layer (MoE)", 4.6 "MoE"
+ *            and 14 "Completed: Expert-batched FFN (GEGLU)": router matmul,
+ *            softmax, top-k, gated expert FFN, weighted combine.
+ *
+ * Conventions for every entry point:
+ *   - Status: Q4_OK (0) or a negative Q4_ERR_*; q4_last_error() then holds a
+ *     message naming the refused argument (thread-local, valid until this
+ *     thread's next call).  On any error nothing has been enqueued, except
+ *     Q4_ERR_HIP, which reports a failed launch.
+ *   - Memory: the caller owns every buffer.  "host" pointers are CPU memory,
+ *     "device" pointers are GPU memory of the current HIP device, 16-byte
+ *     aligned.  Inputs are read only; outputs are fully overwritten and must
+ *     not alias inputs.  The library allocates and frees nothing and never
+ *     synchronizes: GPU entry points enqueue on `stream` (a hipStream_t; NULL
+ *     is the null stream) and return.
+ *   - Canonical weight layouts (row n = one output, groups run along K):
+ *       NVFP4 codes  u8[N][K/2], element 2j in the low nibble of byte j;
+ *             scales u8[N][K/16] (OCP E4M3FN bytes); global scale fp32.
+ *       affine codes u8[N][K/2] (same nibble order); scale, bias bf16
+ *             (uint16 bit patterns) [N][K/64]; w = q*scale + bias.
+ *     The packed layouts produced by the repack calls are private to the
+ *     library; only their byte sizes are part of the ABI.
+ *   - Entries are re-entrant.  Two calls that share a workspace must not run
+ *     concurrently.
+ */
+#ifndef Q4MI_H
+#define Q4MI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4MI_ABI_VERSION 1
+
+enum {
+  Q4_OK = 0,
+  Q4_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad enum value        */
+  Q4_ERR_UNSUPPORTED = -2, /* shape outside what the kernels handle          */
+  Q4_ERR_ALIGNMENT = -3,   /* device pointer not 16-byte aligned             */
+  Q4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query    */
+  Q4_ERR_HIP = -5          /* the HIP runtime reported an error at launch    */
+};
+
+enum { Q4_F16 = 1, Q4_BF16 = 2, Q4_F32 = 3 };
+
+/* Version of this header's ABI (Q4MI_ABI_VERSION). */
+int q4_abi_version(void);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* q4_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Offline repack (host memory in and out, pure CPU, deterministic).
+ * [README]: the weights are reordered once, offline, into the order in
+ * which the matrix unit consumes them, so that the hot loop issues only wide
+ * contiguous loads.  Here the order is that of the gfx950 16x16x32 MFMA B
+ * operand: per 16 output rows, 128-k tiles of 1152 bytes (1 KiB of codes
+ * where each lane's 16 bytes are one 16-byte load, then the tile's scales),
+ * and one 576-byte half tile when K % 128 == 64.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the packed NVFP4 matrix [N][K]; 0 if N % 16 != 0, K % 16 != 0 or
+ * either is not positive.  K is padded internally to a multiple of 64 with
+ * zero codes and zero scales (which contribute exactly 0). */
+size_t q4_nvfp4_packed_bytes(int64_t N, int64_t K);
+
+/* Pack canonical NVFP4 (host codes u8[N][K/2], host scales u8[N][K/16])
+ * into host `packed` of `packed_bytes` >= q4_nvfp4_packed_bytes(N, K).
+ * Errors: INVALID_ARG (null, sizes), UNSUPPORTED (N % 16, K % 16). */
+int q4_nvfp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                    void* packed, size_t packed_bytes);
+
+/* Inverse of q4_nvfp4_repack (host memory), for tests and inspection. */
+int q4_nvfp4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales);
+
+/* Bytes of the packed affine matrix [N][K]; 0 unless N % 16 == 0 and K % 64 == 0. */
+size_t q4_affine4_packed_bytes(int64_t N, int64_t K);
+
+/* Pack canonical affine 4-bit (host codes u8[N][K/2], scale and bias as bf16
+ * bit patterns u16[N][K/64]) into host `packed`.  [ISSUE "Why now"]. */
+int q4_affine4_repack(const uint8_t* codes, const uint16_t* scale_bf16, const uint16_t* bias_bf16,
+                      int64_t N, int64_t K, void* packed, size_t packed_bytes);
+
+/* Inverse of q4_affine4_repack (host memory). */
+int q4_affine4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes,
+                      uint16_t* scale_bf16, uint16_t* bias_bf16);
+
+/* ---------------------------------------------------------------------------
+ * Skinny GEMMs.  y[m][n] = sum_k a[m][k] * w[n][k], 1 <= M <= 16.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace qgemm_nvfp4 needs (0 unless want_argmax). */
+size_t qgemm_nvfp4_workspace_bytes(int M, int64_t K, int64_t N, int want_argmax);
+
+/* NVFP4 W4A16 GEMM [README "Everything it has": the M <= 16 GEMM with
+ * in-register FP4 -> f16 dequant; "Why it's NVIDIA-only": E2M1 x E4M3/16 x
+ * fp32 global].  Each weight is e2m1(code) * e4m3(scale) * global_scale.
+ *   w_packed  device, from q4_nvfp4_repack of the [N][K] weights
+ *   a         device f16 [M][K] row-major
+ *   out       device [M][N] row-major of out_dtype (Q4_F32, Q4_F16 or Q4_BF16)
+ *   argmax    device int32[M] or NULL.  If set, argmax[m] is the index of the
+ *             largest value of row m of `out` as stored, lowest index on ties,
+ *             NaN values skipped (-1 if the whole row is NaN) -- tree_round's
+ *             argmax of [ISSUE "Why now"], fused into the GEMM.
+ *   ws        device workspace of ws_bytes >= the query; it must be zero-filled
+ *             before its first use and is left zero-filled by every call.
+ * Errors: INVALID_ARG, UNSUPPORTED (M outside 1..16, N % 16, K % 16),
+ * ALIGNMENT, WORKSPACE, HIP. */
+int qgemm_nvfp4(const void* w_packed, float global_scale, const void* a, int M, int64_t K,
+                int64_t N, void* out, int out_dtype, int32_t* argmax, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* MLX-style affine 4-bit W4A16 GEMM [ISSUE "Why now": qlinear's affine
+ * path in groups of 64 with activation group sums].  w = q*scale + bias per
+ * 64 weights along K; the product is computed as
+ *   sum_g scale[n,g] * sum_{k in g} a[m,k] q[n,k] + bias[n,g] * sum_{k in g} a[m,k].
+ *   w_packed  device, from q4_affine4_repack
+ *   a         device bf16 [M][K] row-major
+ *   out       device [M][N] of out_dtype (Q4_F32 or Q4_BF16)
+ * Errors: INVALID_ARG, UNSUPPORTED (M outside 1..16, N % 16, K % 64),
+ * ALIGNMENT, HIP. */
+int qgemm_affine4(const void* w_packed, const void* a, int M, int64_t K, int64_t N, void* out,
+                  int out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Top-k MoE.  [DOC 3.2, 4.6]; [README]: 128 experts, top-8, one shared.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace moe_route_topk needs. */
+size_t moe_route_workspace_bytes(int T, int D, int E);
+
+/* Router: logits[t][e] = sum_d x[t][d] * w_router[d][e] in fp32; the k
+ * experts with the largest logits (decreasing, ties to the lower index);
+ * their softmax probabilities over all E experts (renormalized to sum 1 over
+ * the k if `renormalize`).
+ *   x        device f16 [T][D];  w_router device fp32 [D][E]
+ *   logits   device fp32 [T][E] or NULL
+ *   topk_idx device int32 [T][k];  topk_w device fp32 [T][k]
+ *   ws       device workspace (zero-filled before first use, left zero-filled)
+ * Errors: INVALID_ARG, UNSUPPORTED (T outside 1..64, E outside 1..256,
+ * k > E or k > 16, D % 8), ALIGNMENT, WORKSPACE, HIP. */
+int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k,
+                   int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* Expert weights of one MoE layer.  Experts 0..E-1 are routed; if has_shared,
+ * expert E is the shared expert that every token uses with weight 1.
+ * gate/up are [F][D] and down is [D][F] per expert, each packed with
+ * q4_nvfp4_repack and stored expert after expert (stride
+ * q4_nvfp4_packed_bytes of the matrix).  g_* are device fp32 arrays of the
+ * per-matrix global scales, one per expert (E + has_shared entries). */
+typedef struct {
+  int E, has_shared, D, F;
+  const void* gate_packed;
+  const void* up_packed;
+  const void* down_packed;
+  const float* g_gate;
+  const float* g_up;
+  const float* g_down;
+} q4_moe_desc;
+
+/* Bytes of device workspace moe_grouped_qgemm needs for T tokens, top-k. */
+size_t moe_workspace_bytes(const q4_moe_desc* w, int T, int k);
+
+/* Grouped MoE expert FFN [README "Everything it has": grouped, weight-resident
+ * MoE without atomics; DOC 14: expert-batched GEGLU].  For each token t:
+ *   y[t] = sum_{j<k} topk_w[t][j] * FFN_{topk_idx[t][j]}(x[t]) + FFN_shared(x[t])
+ *   FFN_e(v) = W_down,e (gelu_tanh(W_gate,e v) * (W_up,e v))
+ * The (token, slot) pairs are grouped by expert on the device so each active
+ * expert's weights are streamed once; h is kept in f16 between the two
+ * projections; the combine sums in a fixed order (deterministic).
+ *   x        device f16 [T][D]; topk_idx device int32 [T][k] (each in 0..E-1);
+ *   topk_w   device fp32 [T][k]; y device [T][D] of out_dtype (Q4_F32, Q4_F16)
+ *   ws       device workspace of ws_bytes >= moe_workspace_bytes
+ * Errors: INVALID_ARG, UNSUPPORTED (T outside 1..16, k outside 1..E,
+ * D % 64, F % 64), ALIGNMENT, WORKSPACE, HIP.  Out-of-range expert indices
+ * are not checked on the device: their pairs are dropped. */
+int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
+                      const float* topk_w, int T, int k, void* y, int out_dtype, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Test exports: the same device dequantization the GEMMs use, written out.
+ * ------------------------------------------------------------------------- */
+
+/* out[n][k] (device fp32 [N][K]) = fp32(e2m1 * e4m3 * g) from the packed matrix. */
+int q4_dequant_nvfp4(const void* w_packed, float global_scale, int64_t N, int64_t K, float* out,
+                     void* stream);
+
+/* out[n][k] (device fp32 [N][K]) = fmaf(q, scale, bias) from the packed matrix. */
+int q4_dequant_affine4(const void* w_packed, int64_t N, int64_t K, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4MI_H */

@@ -1,0 +1,294 @@
+"""Python binding of libq4mi (W4A16 skinny GEMM and top-k MoE for MI355X).
+
+Argument marshalling only: every function below forwards to the C entry point
+of the same name in ``libq4mi.so`` (declared in ``include/q4mi.h``), passing
+tensor data pointers, sizes and ``torch.cuda.current_stream()``.  Device
+memory comes from torch; all arithmetic happens in the library's HIP kernels
+(GPU entry points) or its C++ host code (repack).  If the shared library is
+missing, importing this package raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq4mi.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_w4a16_skinny_amd.build` "
+                      "(or __graft_entry__.build()) before using the library")
+_lib = C.CDLL(LIB_PATH)
+
+Q4_OK, Q4_ERR_INVALID_ARG, Q4_ERR_UNSUPPORTED, Q4_ERR_ALIGNMENT, Q4_ERR_WORKSPACE, Q4_ERR_HIP = 0, -1, -2, -3, -4, -5
+Q4_F16, Q4_BF16, Q4_F32 = 1, 2, 3
+
+_vp, _i64, _i32, _sz, _f32 = C.c_void_p, C.c_int64, C.c_int, C.c_size_t, C.c_float
+
+
+class q4_moe_desc(C.Structure):
+    _fields_ = [("E", C.c_int), ("has_shared", C.c_int), ("D", C.c_int), ("F", C.c_int),
+                ("gate_packed", _vp), ("up_packed", _vp), ("down_packed", _vp),
+                ("g_gate", _vp), ("g_up", _vp), ("g_down", _vp)]
+
+
+_SIGS = {
+    "q4_abi_version": (_i32, []),
+    "q4_last_error": (C.c_char_p, []),
+    "q4_nvfp4_packed_bytes": (_sz, [_i64, _i64]),
+    "q4_nvfp4_repack": (_i32, [_vp, _vp, _i64, _i64, _vp, _sz]),
+    "q4_nvfp4_unpack": (_i32, [_vp, _i64, _i64, _vp, _vp]),
+    "q4_affine4_packed_bytes": (_sz, [_i64, _i64]),
+    "q4_affine4_repack": (_i32, [_vp, _vp, _vp, _i64, _i64, _vp, _sz]),
+    "q4_affine4_unpack": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "qgemm_nvfp4_workspace_bytes": (_sz, [_i32, _i64, _i64, _i32]),
+    "qgemm_nvfp4": (_i32, [_vp, _f32, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "qgemm_affine4": (_i32, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp]),
+    "moe_route_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_route_topk": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_workspace_bytes": (_sz, [C.POINTER(q4_moe_desc), _i32, _i32]),
+    "moe_grouped_qgemm": (_i32, [C.POINTER(q4_moe_desc), _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "q4_dequant_nvfp4": (_i32, [_vp, _f32, _i64, _i64, _vp, _vp]),
+    "q4_dequant_affine4": (_i32, [_vp, _i64, _i64, _vp, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def _check(status: int):
+    if status != Q4_OK:
+        raise Q4Error(status, _lib.q4_last_error().decode())
+
+
+def abi_version() -> int:
+    return _lib.q4_abi_version()
+
+
+def raw():
+    """The ctypes handle of libq4mi.so (for tests that call the C ABI directly)."""
+    return _lib
+
+
+# ---------------------------------------------------------------- host repack
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(_vp)
+
+
+def q4_nvfp4_packed_bytes(N: int, K: int) -> int:
+    return _lib.q4_nvfp4_packed_bytes(N, K)
+
+
+def q4_nvfp4_repack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    if scales.shape != (N, K // 16):
+        raise ValueError("scales must be [N][K/16]")
+    nb = _lib.q4_nvfp4_packed_bytes(N, K)
+    out = np.empty(max(nb, 1), np.uint8)
+    _check(_lib.q4_nvfp4_repack(_np_ptr(codes), _np_ptr(scales), N, K, _np_ptr(out), nb))
+    return out[:nb]
+
+
+def q4_nvfp4_unpack(packed: np.ndarray, N: int, K: int):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.zeros((N, K // 16), np.uint8)
+    _check(_lib.q4_nvfp4_unpack(_np_ptr(packed), N, K, _np_ptr(codes), _np_ptr(scales)))
+    return codes, scales
+
+
+def q4_affine4_packed_bytes(N: int, K: int) -> int:
+    return _lib.q4_affine4_packed_bytes(N, K)
+
+
+def q4_affine4_repack(codes: np.ndarray, scale_bf16: np.ndarray, bias_bf16: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    s = np.ascontiguousarray(scale_bf16, np.uint16)
+    b = np.ascontiguousarray(bias_bf16, np.uint16)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    if s.shape != (N, K // 64) or b.shape != (N, K // 64):
+        raise ValueError("scale/bias must be [N][K/64]")
+    nb = _lib.q4_affine4_packed_bytes(N, K)
+    out = np.empty(max(nb, 1), np.uint8)
+    _check(_lib.q4_affine4_repack(_np_ptr(codes), _np_ptr(s), _np_ptr(b), N, K, _np_ptr(out), nb))
+    return out[:nb]
+
+
+def q4_affine4_unpack(packed: np.ndarray, N: int, K: int):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    codes = np.zeros((N, K // 2), np.uint8)
+    s = np.zeros((N, K // 64), np.uint16)
+    b = np.zeros((N, K // 64), np.uint16)
+    _check(_lib.q4_affine4_unpack(_np_ptr(packed), N, K, _np_ptr(codes), _np_ptr(s), _np_ptr(b)))
+    return codes, s, b
+
+
+# ---------------------------------------------------------------- device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _vp(_torch().cuda.current_stream().cuda_stream)
+
+
+def _tptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+_DT = {}
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if not _DT:
+        _DT.update({torch.float16: Q4_F16, torch.bfloat16: Q4_BF16, torch.float32: Q4_F32})
+    return _DT[dt]
+
+
+def to_device(arr: np.ndarray, device="cuda"):
+    """Copy a host array (any dtype) into a new device tensor with the same bytes."""
+    torch = _torch()
+    arr = np.ascontiguousarray(arr)
+    t = torch.from_numpy(arr.view(np.uint8).reshape(-1).copy())
+    return t.to(device)
+
+
+_WS = {}
+
+
+def workspace(nbytes: int, device=None):
+    """A zero-filled device workspace shared by calls on this device (grown on demand).
+
+    The library leaves every workspace zero-filled when a call completes, so
+    one buffer serves all calls issued in stream order."""
+    torch = _torch()
+    dev = torch.device(device if device is not None else "cuda")
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    key = (dev.type, dev.index)
+    cur = _WS.get(key)
+    if cur is None or cur.numel() < nbytes:
+        cur = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _WS[key] = cur
+    return cur
+
+
+def qgemm_nvfp4(w_packed, global_scale: float, a, N: int, out=None, out_dtype=None, want_argmax=False):
+    """y = a . W^T for NVFP4 W [N][K] packed on the device; a f16 [M][K].
+
+    Returns ``out`` (and the int32 argmax per row if ``want_argmax``)."""
+    torch = _torch()
+    M, K = a.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    amax = torch.empty((16,), dtype=torch.int32, device=a.device) if want_argmax else None
+    wsb = _lib.qgemm_nvfp4_workspace_bytes(M, K, N, 1 if want_argmax else 0)
+    ws = workspace(wsb, a.device) if wsb else None
+    _check(_lib.qgemm_nvfp4(_tptr(w_packed), float(global_scale), _tptr(a), M, K, N, _tptr(out),
+                            _dtype_code(out.dtype), _tptr(amax), _tptr(ws), wsb, _stream()))
+    return (out, amax[:M]) if want_argmax else out
+
+
+def qgemm_affine4(w_packed, a, N: int, out=None, out_dtype=None):
+    """y = a . W^T for affine 4-bit W [N][K] packed on the device; a bf16 [M][K]."""
+    torch = _torch()
+    M, K = a.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    _check(_lib.qgemm_affine4(_tptr(w_packed), _tptr(a), M, K, N, _tptr(out), _dtype_code(out.dtype), _stream()))
+    return out
+
+
+def moe_route_topk(x, w_router, k: int, renormalize: bool = False, want_logits: bool = True):
+    """Router: (logits fp32 [T][E] or None, idx int32 [T][k], weights fp32 [T][k])."""
+    torch = _torch()
+    T, D = x.shape
+    E = w_router.shape[1]
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    wsb = _lib.moe_route_workspace_bytes(T, D, E)
+    ws = workspace(wsb, x.device)
+    _check(_lib.moe_route_topk(_tptr(x), _tptr(w_router), T, D, E, k, int(bool(renormalize)), _tptr(logits),
+                               _tptr(idx), _tptr(w), _tptr(ws), wsb, _stream()))
+    return logits, idx, w
+
+
+@dataclass
+class MoeWeights:
+    """Device-resident expert weights of one MoE layer (see q4_moe_desc)."""
+    E: int
+    has_shared: bool
+    D: int
+    F: int
+    gate: object   # uint8 device tensors: packed matrices, expert after expert
+    up: object
+    down: object
+    g_gate: object  # fp32 device tensors [E + has_shared]
+    g_up: object
+    g_down: object
+
+    def desc(self) -> q4_moe_desc:
+        return q4_moe_desc(self.E, int(self.has_shared), self.D, self.F, self.gate.data_ptr(), self.up.data_ptr(),
+                           self.down.data_ptr(), self.g_gate.data_ptr(), self.g_up.data_ptr(),
+                           self.g_down.data_ptr())
+
+
+def moe_pack_experts(gate, up, down, E: int, has_shared: bool, device="cuda") -> MoeWeights:
+    """Repack per-expert canonical NVFP4 (codes, scales, g) triples with q4_nvfp4_repack
+    and upload them expert after expert."""
+    torch = _torch()
+    F, D = gate[0][0].shape[0], gate[0][0].shape[1] * 2
+    blobs = []
+    for mats in (gate, up, down):
+        blobs.append(np.concatenate([q4_nvfp4_repack(c, s) for (c, s, _) in mats]))
+    gs = [np.array([float(g) for (_, _, g) in mats], np.float32) for mats in (gate, up, down)]
+    return MoeWeights(E, has_shared, D, F, *(to_device(b, device) for b in blobs),
+                      *(torch.from_numpy(g).to(device) for g in gs))
+
+
+def moe_grouped_qgemm(weights: MoeWeights, x, topk_idx, topk_w, out=None, out_dtype=None):
+    """Grouped MoE layer: y [T][D] = sum_j w * FFN_idx(x) + FFN_shared(x)."""
+    torch = _torch()
+    T, D = x.shape
+    k = topk_idx.shape[1]
+    if out is None:
+        out = torch.empty((T, D), dtype=out_dtype or torch.float32, device=x.device)
+    d = weights.desc()
+    wsb = _lib.moe_workspace_bytes(C.byref(d), T, k)
+    ws = workspace(wsb, x.device)
+    _check(_lib.moe_grouped_qgemm(C.byref(d), _tptr(x), _tptr(topk_idx), _tptr(topk_w), T, k, _tptr(out),
+                                  _dtype_code(out.dtype), _tptr(ws), wsb, _stream()))
+    return out
+
+
+def q4_dequant_nvfp4(w_packed, global_scale: float, N: int, K: int):
+    torch = _torch()
+    out = torch.empty((N, K), dtype=torch.float32, device=w_packed.device)
+    _check(_lib.q4_dequant_nvfp4(_tptr(w_packed), float(global_scale), N, K, _tptr(out), _stream()))
+    return out
+
+
+def q4_dequant_affine4(w_packed, N: int, K: int):
+    torch = _torch()
+    out = torch.empty((N, K), dtype=torch.float32, device=w_packed.device)
+    _check(_lib.q4_dequant_affine4(_tptr(w_packed), N, K, _tptr(out), _stream()))
+    return out

@@ -1,0 +1,460 @@
+// Host side of libq4mi: argument validation, offline repack/unpack, workspace
+// queries, and the extern "C" entry points that enqueue the HIP kernels.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "q4mi.h"
+#include "q4mi_internal.h"
+
+using namespace q4mi;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return Q4_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                              \
+  do {                                                                              \
+    if (!(p)) return fail(Q4_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #p);     \
+  } while (0)
+#define REQUIRE_ALIGNED(p)                                                          \
+  do {                                                                              \
+    if (!aligned16(p))                                                              \
+      return fail(Q4_ERR_ALIGNMENT, "%s: %s is not 16-byte aligned", __func__, #p); \
+  } while (0)
+
+int check_nk(const char* fn, int64_t N, int64_t K, int kmult) {
+  if (N <= 0 || K <= 0) return fail(Q4_ERR_INVALID_ARG, "%s: N=%lld and K=%lld must be positive", fn, (long long)N, (long long)K);
+  if (N % 16) return fail(Q4_ERR_UNSUPPORTED, "%s: N=%lld is not a multiple of 16", fn, (long long)N);
+  if (K % kmult) return fail(Q4_ERR_UNSUPPORTED, "%s: K=%lld is not a multiple of %d", fn, (long long)K, kmult);
+  if (N > (int64_t(1) << 30) || K > (int64_t(1) << 24))
+    return fail(Q4_ERR_UNSUPPORTED, "%s: N=%lld or K=%lld too large", fn, (long long)N, (long long)K);
+  return Q4_OK;
+}
+
+// ---- NVFP4 repack --------------------------------------------------------
+// code byte (n, j) covers k = 2j (low nibble) and 2j + 1 (high nibble)
+inline uint8_t code_byte(const uint8_t* codes, int64_t K, int64_t n, int64_t kk) {
+  // kk is an even k; zero beyond K (padding)
+  return kk < K ? codes[n * (K / 2) + kk / 2] : uint8_t(0);
+}
+inline uint8_t scale_byte(const uint8_t* scales, int64_t K, int64_t n, int64_t grp) {
+  return grp < K / 16 ? scales[n * (K / 16) + grp] : uint8_t(0);
+}
+
+// Visit every (packed byte offset, canonical source) of one NVFP4 matrix.
+// `code(off, n, kk)` handles one code byte (k = kk, kk+1); `scale(off, n, grp)` one scale byte.
+template <class FC, class FS>
+void nvfp4_walk(int64_t N, int64_t K, FC code, FS scale) {
+  const int64_t nfull = full_tiles(K);
+  const bool half = has_half_tile(K);
+  const int64_t pb = panel_bytes(K);
+  for (int64_t p = 0; p < N / 16; ++p) {
+    for (int64_t t = 0; t < nfull + (half ? 1 : 0); ++t) {
+      const bool is_half = t == nfull;
+      const int64_t base = p * pb + t * kTileBytes;
+      const int64_t kb = t * kTileK;
+      const int steps = is_half ? 2 : 4;
+      const int lane_bytes = steps * 4;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int o = lane >> 4, c = lane & 15;
+        const int64_t n = p * 16 + c;
+        for (int i = 0; i < steps; ++i)
+          for (int b = 0; b < 4; ++b)
+            code(base + lane * lane_bytes + i * 4 + b, n, kb + 32 * i + 8 * o + 2 * b);
+      }
+      // scales: word (c, h) holds, in byte i, the scale of group kb/16 + 2i + h
+      const int64_t sbase = base + (is_half ? kHalfCodeBytes : kTileCodeBytes);
+      for (int c = 0; c < 16; ++c)
+        for (int h = 0; h < 2; ++h)
+          for (int i = 0; i < steps; ++i)
+            scale(sbase + (c * 2 + h) * steps + i, p * 16 + c, kb / 16 + 2 * i + h);
+    }
+  }
+}
+
+// Affine: lane code dword i holds 8 codes e0..e7 (k = kb + 32i + 8o + j) with
+// e_{2s} at nibble s and e_{2s+1} at nibble s + 4, so that
+// ((d >> 4s) & 0x000F000F) is the pair (e_2s, e_2s+1) in the two 16-bit halves.
+template <class FC, class FSB>
+void affine_walk(int64_t N, int64_t K, FC code, FSB sb) {
+  const int64_t nfull = full_tiles(K);
+  const bool half = has_half_tile(K);
+  const int64_t pb = panel_bytes(K);
+  for (int64_t p = 0; p < N / 16; ++p) {
+    for (int64_t t = 0; t < nfull + (half ? 1 : 0); ++t) {
+      const bool is_half = t == nfull;
+      const int64_t base = p * pb + t * kTileBytes;
+      const int64_t kb = t * kTileK;
+      const int steps = is_half ? 2 : 4;
+      const int lane_bytes = steps * 4;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int o = lane >> 4, c = lane & 15;
+        const int64_t n = p * 16 + c;
+        for (int i = 0; i < steps; ++i)
+          code(base + lane * lane_bytes + i * 4, n, kb + 32 * i + 8 * o);
+      }
+      const int64_t sbase = base + (is_half ? kHalfCodeBytes : kTileCodeBytes);
+      const int groups = is_half ? 1 : 2;
+      for (int c = 0; c < 16; ++c)
+        for (int gi = 0; gi < groups; ++gi)
+          sb(sbase + (c * groups + gi) * 4, p * 16 + c, kb / 64 + gi);
+    }
+  }
+}
+
+inline uint32_t affine_word_from_codes(const uint8_t e[8]) {
+  uint32_t d = 0;
+  for (int s = 0; s < 4; ++s) {
+    d |= uint32_t(e[2 * s] & 15) << (4 * s);
+    d |= uint32_t(e[2 * s + 1] & 15) << (16 + 4 * s);
+  }
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4_abi_version(void) { return Q4MI_ABI_VERSION; }
+
+const char* q4_last_error(void) { return g_last_error.c_str(); }
+
+size_t q4_nvfp4_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 16 || K % 16) return 0;
+  return size_t(N / 16) * size_t(panel_bytes(K));
+}
+
+int q4_nvfp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, void* packed,
+                    size_t packed_bytes) {
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE_PTR(packed);
+  if (int rc = check_nk(__func__, N, K, 16)) return rc;
+  if (packed_bytes < q4_nvfp4_packed_bytes(N, K))
+    return fail(Q4_ERR_INVALID_ARG, "%s: packed_bytes=%zu < %zu", __func__, packed_bytes, q4_nvfp4_packed_bytes(N, K));
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  nvfp4_walk(N, K,
+             [&](int64_t off, int64_t n, int64_t kk) { out[off] = code_byte(codes, K, n, kk); },
+             [&](int64_t off, int64_t n, int64_t grp) { out[off] = scale_byte(scales, K, n, grp); });
+  return ok();
+}
+
+int q4_nvfp4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales) {
+  REQUIRE_PTR(packed);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  if (int rc = check_nk(__func__, N, K, 16)) return rc;
+  const uint8_t* in = static_cast<const uint8_t*>(packed);
+  nvfp4_walk(N, K,
+             [&](int64_t off, int64_t n, int64_t kk) {
+               if (kk < K) codes[n * (K / 2) + kk / 2] = in[off];
+             },
+             [&](int64_t off, int64_t n, int64_t grp) {
+               if (grp < K / 16) scales[n * (K / 16) + grp] = in[off];
+             });
+  return ok();
+}
+
+size_t q4_affine4_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 16 || K % 64) return 0;
+  return size_t(N / 16) * size_t(panel_bytes(K));
+}
+
+int q4_affine4_repack(const uint8_t* codes, const uint16_t* scale_bf16, const uint16_t* bias_bf16,
+                      int64_t N, int64_t K, void* packed, size_t packed_bytes) {
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scale_bf16);
+  REQUIRE_PTR(bias_bf16);
+  REQUIRE_PTR(packed);
+  if (int rc = check_nk(__func__, N, K, 64)) return rc;
+  if (packed_bytes < q4_affine4_packed_bytes(N, K))
+    return fail(Q4_ERR_INVALID_ARG, "%s: packed_bytes=%zu < %zu", __func__, packed_bytes, q4_affine4_packed_bytes(N, K));
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  const int64_t G = K / 64;
+  affine_walk(
+      N, K,
+      [&](int64_t off, int64_t n, int64_t k0) {
+        uint8_t e[8];
+        for (int j = 0; j < 8; ++j) {
+          const uint8_t byte = codes[n * (K / 2) + (k0 + j) / 2];
+          e[j] = ((k0 + j) & 1) ? uint8_t(byte >> 4) : uint8_t(byte & 15);
+        }
+        const uint32_t d = affine_word_from_codes(e);
+        std::memcpy(out + off, &d, 4);
+      },
+      [&](int64_t off, int64_t n, int64_t grp) {
+        const uint16_t s = scale_bf16[n * G + grp], b = bias_bf16[n * G + grp];
+        std::memcpy(out + off, &s, 2);
+        std::memcpy(out + off + 2, &b, 2);
+      });
+  return ok();
+}
+
+int q4_affine4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes, uint16_t* scale_bf16,
+                      uint16_t* bias_bf16) {
+  REQUIRE_PTR(packed);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scale_bf16);
+  REQUIRE_PTR(bias_bf16);
+  if (int rc = check_nk(__func__, N, K, 64)) return rc;
+  const uint8_t* in = static_cast<const uint8_t*>(packed);
+  const int64_t G = K / 64;
+  affine_walk(
+      N, K,
+      [&](int64_t off, int64_t n, int64_t k0) {
+        uint32_t d;
+        std::memcpy(&d, in + off, 4);
+        for (int s = 0; s < 4; ++s) {
+          const uint8_t lo = (d >> (4 * s)) & 15, hi = (d >> (16 + 4 * s)) & 15;
+          // elements 2s and 2s+1 form one canonical byte (2s even)
+          codes[n * (K / 2) + (k0 + 2 * s) / 2] = uint8_t(lo | (hi << 4));
+        }
+      },
+      [&](int64_t off, int64_t n, int64_t grp) {
+        std::memcpy(&scale_bf16[n * G + grp], in + off, 2);
+        std::memcpy(&bias_bf16[n * G + grp], in + off + 2, 2);
+      });
+  return ok();
+}
+
+// ---- GEMMs ---------------------------------------------------------------
+
+size_t qgemm_nvfp4_workspace_bytes(int M, int64_t K, int64_t N, int want_argmax) {
+  (void)M;
+  (void)K;
+  (void)N;
+  return want_argmax ? 256 : 0;  // counter (+pad) and 16 packed keys
+}
+
+static int gemm_common(int fmt, const char* fn, const void* w_packed, float gscale, const void* a, int M,
+                       int64_t K, int64_t N, void* out, int out_dtype, int32_t* argmax, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!w_packed) return fail(Q4_ERR_INVALID_ARG, "%s: w_packed is NULL", fn);
+  if (!a) return fail(Q4_ERR_INVALID_ARG, "%s: a is NULL", fn);
+  if (!out) return fail(Q4_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  if (M < 1 || M > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: M=%d outside 1..16 (skinny GEMM only)", fn, M);
+  if (int rc = check_nk(fn, N, K, fmt == kNvfp4 ? 16 : 64)) return rc;
+  if (fmt == kNvfp4 && out_dtype != Q4_F32 && out_dtype != Q4_F16 && out_dtype != Q4_BF16)
+    return fail(Q4_ERR_INVALID_ARG, "%s: out_dtype=%d is not Q4_F32, Q4_F16 or Q4_BF16", fn, out_dtype);
+  if (fmt == kAffine && out_dtype != Q4_F32 && out_dtype != Q4_BF16)
+    return fail(Q4_ERR_INVALID_ARG, "%s: out_dtype=%d is not Q4_F32 or Q4_BF16", fn, out_dtype);
+  if (!aligned16(w_packed)) return fail(Q4_ERR_ALIGNMENT, "%s: w_packed is not 16-byte aligned", fn);
+  if (!aligned16(a)) return fail(Q4_ERR_ALIGNMENT, "%s: a is not 16-byte aligned", fn);
+  if (!aligned16(out)) return fail(Q4_ERR_ALIGNMENT, "%s: out is not 16-byte aligned", fn);
+  if (argmax) {
+    if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: argmax requested but ws is NULL", fn);
+    if (ws_bytes < qgemm_nvfp4_workspace_bytes(M, K, N, 1))
+      return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", fn, ws_bytes, qgemm_nvfp4_workspace_bytes(M, K, N, 1));
+    if (!aligned16(ws)) return fail(Q4_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+    if (!aligned16(argmax)) return fail(Q4_ERR_ALIGNMENT, "%s: argmax is not 16-byte aligned", fn);
+  }
+  GemmArgs g{};
+  g.w = static_cast<const uint8_t*>(w_packed);
+  g.panel_bytes = panel_bytes(K);
+  g.a = static_cast<const uint16_t*>(a);
+  g.M = M;
+  g.K = int(K);
+  g.N = int(N);
+  g.nfull = int(full_tiles(K));
+  g.half = has_half_tile(K) ? 1 : 0;
+  g.k_exact = (K % 64) == 0;
+  g.gscale = gscale;
+  g.out = out;
+  g.out_dtype = out_dtype;
+  g.argmax = argmax;
+  g.counter = argmax ? static_cast<unsigned*>(ws) : nullptr;
+  g.keys = argmax ? reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + 16) : nullptr;
+  const GemmCfg cfg = choose_gemm_cfg(fmt, M, K, N);
+  if (int e = launch_gemm(fmt, g, cfg, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
+  return ok();
+}
+
+int qgemm_nvfp4(const void* w_packed, float global_scale, const void* a, int M, int64_t K, int64_t N, void* out,
+                int out_dtype, int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+  return gemm_common(kNvfp4, __func__, w_packed, global_scale, a, M, K, N, out, out_dtype, argmax, ws, ws_bytes,
+                     stream);
+}
+
+int qgemm_affine4(const void* w_packed, const void* a, int M, int64_t K, int64_t N, void* out, int out_dtype,
+                  void* stream) {
+  return gemm_common(kAffine, __func__, w_packed, 1.0f, a, M, K, N, out, out_dtype, nullptr, nullptr, 0, stream);
+}
+
+int q4_dequant_nvfp4(const void* w_packed, float global_scale, int64_t N, int64_t K, float* out, void* stream) {
+  REQUIRE_PTR(w_packed);
+  REQUIRE_PTR(out);
+  if (int rc = check_nk(__func__, N, K, 16)) return rc;
+  REQUIRE_ALIGNED(w_packed);
+  REQUIRE_ALIGNED(out);
+  if (int e = launch_dequant(kNvfp4, static_cast<const uint8_t*>(w_packed), panel_bytes(K), N, K, global_scale, out,
+                             stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
+}
+
+int q4_dequant_affine4(const void* w_packed, int64_t N, int64_t K, float* out, void* stream) {
+  REQUIRE_PTR(w_packed);
+  REQUIRE_PTR(out);
+  if (int rc = check_nk(__func__, N, K, 64)) return rc;
+  REQUIRE_ALIGNED(w_packed);
+  REQUIRE_ALIGNED(out);
+  if (int e = launch_dequant(kAffine, static_cast<const uint8_t*>(w_packed), panel_bytes(K), N, K, 1.0f, out, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
+}
+
+// ---- router --------------------------------------------------------------
+
+static int route_blocks(int D) {
+  // workgroups splitting D: about 64 rows of W_r each, at most 64 partial sums
+  int nb = (D + 63) / 64;
+  if (nb > 64) nb = 64;
+  if (nb < 1) nb = 1;
+  return nb;
+}
+
+size_t moe_route_workspace_bytes(int T, int D, int E) {
+  if (T < 1 || D < 1 || E < 1) return 0;
+  return 256 + size_t(route_blocks(D)) * size_t(T) * size_t(E) * sizeof(float);
+}
+
+int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k, int renormalize, float* logits,
+                   int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  if (T < 1 || D < 1 || E < 1 || k < 1)
+    return fail(Q4_ERR_INVALID_ARG, "%s: T=%d D=%d E=%d k=%d must be positive", __func__, T, D, E, k);
+  if (T > 64) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d > 64", __func__, T);
+  if (E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", __func__, E);
+  if (k > E || k > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d must be <= E=%d and <= 16", __func__, k, E);
+  if (D % 8) return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d is not a multiple of 8", __func__, D);
+  if (E % 4) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d is not a multiple of 4", __func__, E);
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(w_router);
+  REQUIRE_ALIGNED(topk_idx);
+  REQUIRE_ALIGNED(topk_w);
+  if (logits) REQUIRE_ALIGNED(logits);
+  if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
+  REQUIRE_ALIGNED(ws);
+  if (ws_bytes < moe_route_workspace_bytes(T, D, E))
+    return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, moe_route_workspace_bytes(T, D, E));
+  RouteArgs r{};
+  r.x = static_cast<const uint16_t*>(x);
+  r.wr = w_router;
+  r.T = T;
+  r.D = D;
+  r.E = E;
+  r.k = k;
+  r.renormalize = renormalize ? 1 : 0;
+  r.logits = logits;
+  r.idx = topk_idx;
+  r.w = topk_w;
+  r.counter = static_cast<unsigned*>(ws);
+  r.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
+  r.nblk = route_blocks(D);
+  if (int e = launch_route(r, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
+}
+
+// ---- grouped MoE ---------------------------------------------------------
+
+static size_t moe_ws_layout(const q4_moe_desc* w, int T, int k, size_t* h_off, size_t* o_off) {
+  const size_t npairs = size_t(T) * size_t(k) + (w->has_shared ? size_t(T) : 0);
+  const size_t hbytes = (npairs * size_t(w->F) * 2 + 255) / 256 * 256;
+  const size_t obytes = (npairs * size_t(w->D) * 4 + 255) / 256 * 256;
+  *h_off = 0;
+  *o_off = hbytes;
+  return hbytes + obytes;
+}
+
+size_t moe_workspace_bytes(const q4_moe_desc* w, int T, int k) {
+  if (!w || T < 1 || k < 1 || w->D < 1 || w->F < 1) return 0;
+  size_t h, o;
+  return moe_ws_layout(w, T, k, &h, &o);
+}
+
+int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_idx, const float* topk_w, int T,
+                      int k, void* y, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(w->gate_packed);
+  REQUIRE_PTR(w->up_packed);
+  REQUIRE_PTR(w->down_packed);
+  REQUIRE_PTR(w->g_gate);
+  REQUIRE_PTR(w->g_up);
+  REQUIRE_PTR(w->g_down);
+  if (w->E < 1 || w->D < 1 || w->F < 1 || (w->has_shared != 0 && w->has_shared != 1))
+    return fail(Q4_ERR_INVALID_ARG, "%s: bad descriptor (E=%d D=%d F=%d has_shared=%d)", __func__, w->E, w->D, w->F,
+                w->has_shared);
+  if (T < 1 || T > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d outside 1..16", __func__, T);
+  if (k < 1 || k > w->E) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d outside 1..E=%d", __func__, k, w->E);
+  if (w->D % 64 || w->F % 64)
+    return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d and F=%d must be multiples of 64", __func__, w->D, w->F);
+  if (w->E > 1024) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 1024", __func__, w->E);
+  if (out_dtype != Q4_F32 && out_dtype != Q4_F16)
+    return fail(Q4_ERR_INVALID_ARG, "%s: out_dtype=%d is not Q4_F32 or Q4_F16", __func__, out_dtype);
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(topk_idx);
+  REQUIRE_ALIGNED(topk_w);
+  REQUIRE_ALIGNED(y);
+  REQUIRE_ALIGNED(w->gate_packed);
+  REQUIRE_ALIGNED(w->up_packed);
+  REQUIRE_ALIGNED(w->down_packed);
+  if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
+  REQUIRE_ALIGNED(ws);
+  size_t h_off, o_off;
+  const size_t need = moe_ws_layout(w, T, k, &h_off, &o_off);
+  if (ws_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, need);
+  MoeArgs m{};
+  m.E = w->E;
+  m.has_shared = w->has_shared;
+  m.D = w->D;
+  m.F = w->F;
+  m.T = T;
+  m.k = k;
+  m.gate = static_cast<const uint8_t*>(w->gate_packed);
+  m.up = static_cast<const uint8_t*>(w->up_packed);
+  m.down = static_cast<const uint8_t*>(w->down_packed);
+  m.gate_stride = int64_t(q4_nvfp4_packed_bytes(w->F, w->D));
+  m.down_stride = int64_t(q4_nvfp4_packed_bytes(w->D, w->F));
+  m.gate_panel_bytes = panel_bytes(w->D);
+  m.down_panel_bytes = panel_bytes(w->F);
+  m.g_gate = w->g_gate;
+  m.g_up = w->g_up;
+  m.g_down = w->g_down;
+  m.x = static_cast<const uint16_t*>(x);
+  m.idx = topk_idx;
+  m.tw = topk_w;
+  m.y = y;
+  m.out_dtype = out_dtype;
+  m.h = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + h_off);
+  m.o = reinterpret_cast<float*>(static_cast<char*>(ws) + o_off);
+  if (int e = launch_moe(m, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol, its
+offline repack is a bijection with the documented placement, and every
+refusal returns its status before anything reaches a GPU."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import moe_w4a16_skinny_amd as q4
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "q4mi.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert len(declared) >= 17
+    lib = C.CDLL(q4.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(q4.EXPORTED)
+    assert q4.abi_version() == 1
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (32, 64), (16, 704), (48, 2816), (16, 80), (32, 176), (16, 16)])
+def test_nvfp4_repack_round_trip(N, K):
+    rng = np.random.default_rng(N * 1000 + K)
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (N, K // 16), dtype=np.uint8)
+    packed = q4.q4_nvfp4_repack(codes, scales)
+    Kp = (K + 63) // 64 * 64
+    assert packed.size == q4.q4_nvfp4_packed_bytes(N, K) == (N // 16) * ((Kp // 128) * 1152 + (Kp % 128 // 64) * 576)
+    if K % 64 == 0:  # no padding: exactly the algorithmic bytes
+        assert packed.size == N * K // 2 + N * K // 16
+    c2, s2 = q4.q4_nvfp4_unpack(packed, N, K)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+    # every byte of the canonical input lands in a distinct packed byte
+    assert np.count_nonzero(packed) <= codes.size + scales.size
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (32, 64), (16, 5120), (48, 704)])
+def test_affine_repack_round_trip(N, K):
+    codes, s, b = synth.affine_weights(N + K, N, K)
+    packed = q4.q4_affine4_repack(codes, s, b)
+    assert packed.size == q4.q4_affine4_packed_bytes(N, K) == N * K // 2 + N * (K // 64) * 4
+    c2, s2, b2 = q4.q4_affine4_unpack(packed, N, K)
+    assert np.array_equal(codes, c2) and np.array_equal(s, s2) and np.array_equal(b, b2)
+
+
+def test_nvfp4_placement_matches_operand_layout():
+    """A single code at (n, k) lands in lane (k%32)//8 * 16 + n%16 of its tile,
+    code dword (k%128)//32, byte (k%8)//2, nibble k%2; its scale in word
+    (n%16, (k%32)//16), byte (k%128)//32."""
+    N, K = 32, 384
+    for (n, k) in [(0, 0), (5, 37), (17, 200), (31, 383), (16, 129)]:
+        q = np.zeros((N, K), np.uint8)
+        q[n, k] = 0x7
+        sc = np.zeros((N, K // 16), np.uint8)
+        sc[n, k // 16] = 0x38
+        packed = q4.q4_nvfp4_repack(synth.pack_nibbles(q), sc)
+        pb = (K // 128) * 1152
+        tile = (n // 16) * pb + (k // 128) * 1152
+        lane = ((k % 32) // 8) * 16 + n % 16
+        byte = tile + lane * 16 + ((k % 128) // 32) * 4 + (k % 8) // 2
+        nz = np.flatnonzero(packed)
+        assert len(nz) == 2
+        assert nz[0] == byte and packed[byte] == (0x7 << (4 * (k % 2)))
+        sbyte = tile + 1024 + ((n % 16) * 2 + (k % 32) // 16) * 4 + (k % 128) // 32
+        assert nz[1] == sbyte and packed[sbyte] == 0x38
+
+
+def test_affine_placement_matches_operand_layout():
+    """Element k of column n: lane (k%32)//8*16 + n%16, dword (k%128)//32, element
+    j = k%8 at nibble j//2 (+4 if j is odd); scale/bias of group k//64 at
+    tile + 1024 + (n%16)*8 + ((k%128)//64)*4."""
+    N, K = 16, 256
+    for (n, k) in [(0, 0), (3, 9), (15, 255), (7, 130)]:
+        q = np.zeros((N, K), np.uint8)
+        q[n, k] = 0xB
+        s = np.zeros((N, K // 64), np.uint16)
+        b = np.zeros((N, K // 64), np.uint16)
+        s[n, k // 64] = 0x3F80
+        b[n, k // 64] = 0x4000
+        packed = q4.q4_affine4_repack(synth.pack_nibbles(q), s, b)
+        tile = (k // 128) * 1152
+        lane = ((k % 32) // 8) * 16 + n
+        j = k % 8
+        word = tile + lane * 16 + ((k % 128) // 32) * 4
+        shift = 4 * (j // 2) + (16 if j % 2 else 0)
+        val = int.from_bytes(packed[word:word + 4].tobytes(), "little")
+        assert val == 0xB << shift
+        sb = tile + 1024 + n * 8 + ((k % 128) // 64) * 4
+        assert packed[sb:sb + 4].tobytes() == bytes([0x80, 0x3F, 0x00, 0x40])
+        assert np.count_nonzero(packed) == 1 + 3
+
+
+def _err(status):
+    return q4.raw().q4_last_error().decode()
+
+
+def test_gemm_refusals_without_gpu():
+    lib = q4.raw()
+    buf = (C.c_uint8 * 4096)()
+    base = C.addressof(buf)
+    al = (base + 15) & ~15
+    p = C.c_void_p(al)
+    mis = C.c_void_p(al + 4)
+    cases = [
+        (lambda: lib.qgemm_nvfp4(None, 1.0, p, 1, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_INVALID_ARG, "w_packed"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 0, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "M=0"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 17, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "M=17"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 24, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "N=24"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 72, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "K=72"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, 9, None, None, 0, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
+        (lambda: lib.qgemm_nvfp4(mis, 1.0, p, 1, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_ALIGNMENT, "w_packed"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, mis, 1, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_ALIGNMENT, "a is"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, q4.Q4_F32, p, None, 0, None), q4.Q4_ERR_WORKSPACE, "ws"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, q4.Q4_F32, p, p, 8, None), q4.Q4_ERR_WORKSPACE, "ws_bytes"),
+        (lambda: lib.qgemm_affine4(p, p, 1, 96, 16, p, q4.Q4_F32, None), q4.Q4_ERR_UNSUPPORTED, "K=96"),
+        (lambda: lib.qgemm_affine4(p, p, 1, 128, 16, p, q4.Q4_F16, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
+        (lambda: lib.q4_dequant_nvfp4(p, 1.0, 15, 64, p, None), q4.Q4_ERR_UNSUPPORTED, "N=15"),
+    ]
+    for call, code, needle in cases:
+        assert call() == code, needle
+        assert needle in _err(code), (needle, _err(code))
+
+
+def test_router_and_moe_refusals_without_gpu():
+    lib = q4.raw()
+    buf = (C.c_uint8 * 4096)()
+    p = C.c_void_p((C.addressof(buf) + 15) & ~15)
+    ws = lib.moe_route_workspace_bytes(16, 2816, 128)
+    assert ws >= 256 + 16 * 128 * 4
+    cases = [
+        (lambda: lib.moe_route_topk(p, p, 65, 64, 128, 8, 0, None, p, p, p, 1 << 30, None), q4.Q4_ERR_UNSUPPORTED, "T=65"),
+        (lambda: lib.moe_route_topk(p, p, 4, 64, 8, 9, 0, None, p, p, p, 1 << 30, None), q4.Q4_ERR_UNSUPPORTED, "k=9"),
+        (lambda: lib.moe_route_topk(p, p, 4, 60, 8, 2, 0, None, p, p, p, 1 << 30, None), q4.Q4_ERR_UNSUPPORTED, "D=60"),
+        (lambda: lib.moe_route_topk(p, p, 4, 64, 8, 2, 0, None, p, p, None, 0, None), q4.Q4_ERR_WORKSPACE, "ws"),
+        (lambda: lib.moe_route_topk(p, p, 4, 64, 8, 2, 0, None, p, p, p, 16, None), q4.Q4_ERR_WORKSPACE, "ws_bytes"),
+        (lambda: lib.moe_route_topk(None, p, 4, 64, 8, 2, 0, None, p, p, p, 1 << 30, None), q4.Q4_ERR_INVALID_ARG, "x"),
+    ]
+    for call, code, needle in cases:
+        assert call() == code, needle
+        assert needle in _err(code), (needle, _err(code))
+    d = q4.q4_moe_desc(128, 1, 2816, 704, p.value, p.value, p.value, p.value, p.value, p.value)
+    need = lib.moe_workspace_bytes(C.byref(d), 16, 8)
+    assert need >= 144 * 704 * 2 + 144 * 2816 * 4
+    mcases = [
+        (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 17, 8, p, q4.Q4_F32, p, need, None), q4.Q4_ERR_UNSUPPORTED, "T=17"),
+        (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 16, 129, p, q4.Q4_F32, p, need, None), q4.Q4_ERR_UNSUPPORTED, "k=129"),
+        (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 16, 8, p, q4.Q4_BF16, p, need, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
+        (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 16, 8, p, q4.Q4_F32, p, need - 1, None), q4.Q4_ERR_WORKSPACE, "ws_bytes"),
+        (lambda: lib.moe_grouped_qgemm(None, p, p, p, 16, 8, p, q4.Q4_F32, p, need, None), q4.Q4_ERR_INVALID_ARG, "w is NULL"),
+    ]
+    for call, code, needle in mcases:
+        assert call() == code, needle
+        assert needle in _err(code), (needle, _err(code))
+    bad = q4.q4_moe_desc(128, 1, 2800, 704, p.value, p.value, p.value, p.value, p.value, p.value)
+    assert lib.moe_grouped_qgemm(C.byref(bad), p, p, p, 16, 8, p, q4.Q4_F32, p, 1 << 30, None) == q4.Q4_ERR_UNSUPPORTED
+
+
+def test_repack_refusals():
+    with pytest.raises(q4.Q4Error) as ei:
+        q4.q4_nvfp4_repack(np.zeros((24, 32), np.uint8), np.zeros((24, 4), np.uint8))
+    assert ei.value.status == q4.Q4_ERR_UNSUPPORTED and "N=24" in str(ei.value)
+    with pytest.raises(q4.Q4Error) as ei:
+        q4.q4_affine4_repack(np.zeros((16, 48), np.uint8), np.zeros((16, 1), np.uint16), np.zeros((16, 1), np.uint16))
+    assert ei.value.status == q4.Q4_ERR_UNSUPPORTED and "K=96" in str(ei.value)
+    assert q4.q4_nvfp4_packed_bytes(16, 24) == 0 and q4.q4_affine4_packed_bytes(16, 96) == 0
