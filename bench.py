@@ -1,0 +1,257 @@
+"""Benchmark of the W4A16 skinny GEMM / top-8 MoE hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  A step is one pass of the path over one batch of
+synthetic, seeded inputs: one qgemm call for the GEMM workloads, one router
+call plus one grouped-MoE call for the MoE workload.  The weights are
+resident in HBM before timing starts and rotate over enough distinct device
+copies (>= 2 GiB in total) that neither the 256 MB Infinity Cache nor L2 can
+serve them, so every step streams its weights from HBM.
+
+value      = algorithmic weight bytes per step * K / wall time of the K steps
+roofline   = algorithmic bytes of the dominant kernel / its mean duration,
+             timed with HIP events around each launch on the launch stream,
+             against the 8 TB/s HBM peak
+cpu_baseline = the float64 CPU oracle on a bounded sample of the same
+             workload, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "weight-stream HBM GB/s (% of ~8 TB/s) for W4A16 GEMM M=1/16 & top-8 MoE"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "nvfp4_verify_m16_k4096_n8192"
+ROTATE_BYTES = 2 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--hot", action="store_true", help="no weight rotation (cache-resident weights)")
+    ap.add_argument("--copy-kernel", type=int, default=0,
+                    help="instead of the path, time a device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def threads_used():
+    try:
+        from threadpoolctl import threadpool_info
+        n = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        n = 1
+    return int(n)
+
+
+# ------------------------------------------------------------------ workloads
+
+class GemmWork:
+    def __init__(self, name, spec, hot):
+        import numpy as np
+        import torch
+
+        import moe_w4a16_skinny_amd as q4
+        import synth
+        self.name, self.spec = name, spec
+        self.q4 = q4
+        M, K, N = spec["M"], spec["K"], spec["N"]
+        self.M, self.K, self.N = M, K, N
+        t0 = time.time()
+        if spec["kind"] == "nvfp4":
+            inp = synth.nvfp4_gemm(spec["seed"], M, K, N)
+            packed = q4.q4_nvfp4_repack(inp.codes, inp.scales)
+            self.a = torch.from_numpy(inp.a).cuda()
+            self.g = float(inp.g)
+            self.alg_bytes = N * K // 2 + N * K // 16 + 4
+            self.dtype = "f16"
+        else:
+            inp = synth.affine_gemm(spec["seed"], M, K, N)
+            packed = q4.q4_affine4_repack(inp.codes, inp.scale, inp.bias)
+            self.a = torch.from_numpy(inp.a.view(np.int16)).cuda().view(torch.bfloat16)
+            self.alg_bytes = N * K // 2 + 2 * N * (K // 64) * 2
+            self.dtype = "bf16"
+        self.inp = inp
+        log(f"[bench] {name}: inputs generated and packed in {time.time() - t0:.1f}s")
+        nb = packed.size
+        self.copies = 1 if hot else max(2, -(-ROTATE_BYTES // nb))
+        self.stride = -(-nb // 256) * 256
+        base = torch.from_numpy(packed).cuda()
+        self.wbuf = torch.empty(self.copies * self.stride, dtype=torch.uint8, device="cuda")
+        for i in range(self.copies):
+            self.wbuf[i * self.stride:i * self.stride + nb].copy_(base)
+        del base
+        out_dt = {"f32": torch.float32, "f16": torch.float16}[spec.get("out", "f32")]
+        self.out = torch.empty((M, N), dtype=out_dt, device="cuda")
+        self.want_argmax = bool(spec.get("argmax"))
+        self.amax = torch.empty(16, dtype=torch.int32, device="cuda")
+        self.ws = q4.workspace(256)
+        self.i = 0
+        self.kernel_names = ["qgemm_kernel"]
+
+    def step(self):
+        import ctypes as C
+        q4 = self.q4
+        lib = q4.raw()
+        w = C.c_void_p(self.wbuf.data_ptr() + (self.i % self.copies) * self.stride)
+        self.i += 1
+        s = q4._stream()
+        if self.spec["kind"] == "nvfp4":
+            rc = lib.qgemm_nvfp4(w, self.g, C.c_void_p(self.a.data_ptr()), self.M, self.K, self.N,
+                                 C.c_void_p(self.out.data_ptr()), q4._dtype_code(self.out.dtype),
+                                 C.c_void_p(self.amax.data_ptr()) if self.want_argmax else None,
+                                 C.c_void_p(self.ws.data_ptr()), self.ws.numel(), s)
+        else:
+            rc = lib.qgemm_affine4(w, C.c_void_p(self.a.data_ptr()), self.M, self.K, self.N,
+                                   C.c_void_p(self.out.data_ptr()), q4._dtype_code(self.out.dtype), s)
+        if rc != 0:
+            q4._check(rc)
+
+    def config(self):
+        return {"workload": self.name, "M": self.M, "K": self.K, "N": self.N,
+                "weights": self.spec["kind"], "out": self.spec.get("out", "f32"),
+                "fused_argmax": self.want_argmax, "weight_copies_rotated": self.copies}
+
+    def cpu_oracle_sample(self, seconds):
+        """Time the oracle on row blocks of the same weights for about `seconds`."""
+        import oracle
+        inp = self.inp
+        N = self.N
+        rows = min(N, 2048)
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            r0 = (done * rows) % N
+            r1 = min(N, r0 + rows)
+            if self.spec["kind"] == "nvfp4":
+                oracle.nvfp4_gemm_ref(inp.codes[r0:r1], inp.scales[r0:r1], inp.g, inp.a, want_bound=False)
+            else:
+                oracle.affine_gemm_ref(inp.codes[r0:r1], inp.scale[r0:r1], inp.bias[r0:r1], inp.a,
+                                       want_bound=False)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        bytes_done = done * rows * self.alg_bytes / N
+        return bytes_done / el / 1e9, f"{done} oracle GEMMs of {rows} weight rows (M={self.M}, K={self.K}) " \
+                                      f"in {el:.1f}s"
+
+
+class CopyWork:
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+
+    def __init__(self, mib):
+        import torch
+        self.nbytes = mib << 20
+        self.src = torch.ones(self.nbytes // 4, dtype=torch.float32, device="cuda")
+        self.dst = torch.empty_like(self.src)
+        self.alg_bytes = 2 * self.nbytes
+        self.kernel_names = ["copy"]
+        self.dtype = "f32"
+
+    def step(self):
+        self.dst.copy_(self.src)
+
+    def config(self):
+        return {"workload": f"device_copy_{self.nbytes >> 20}MiB"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding of this path "
+              "is described in the design notes and not launched here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import synth
+
+    if args.copy_kernel:
+        work = CopyWork(args.copy_kernel)
+        name = work.config()["workload"]
+    else:
+        name = args.workload
+        spec = synth.WORKLOADS[name]
+        if spec["kind"] == "moe":
+            from moe_bench import MoeWork  # noqa: F401  (added with the MoE kernels)
+            work = MoeWork(name, spec, args.hot)
+        else:
+            work = GemmWork(name, spec, args.hot)
+
+    for _ in range(args.warmup):
+        work.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(K):
+        work.step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e-3 for i in range(K)]   # seconds per launch
+    per.sort()
+    mean_launch = sum(per) / K
+    median_launch = per[K // 2]
+
+    value = work.alg_bytes * K / wall / 1e9
+    achieved = work.alg_bytes / mean_launch / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": work.dtype,
+        "data": "synthetic (seeded; NVFP4 / affine 4-bit weights drawn and encoded by the workload recipe)",
+        "config": work.config(),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": work.kernel_names[0],
+            "alg_bytes_per_launch": work.alg_bytes,
+            "mean_launch_us": round(mean_launch * 1e6, 3),
+            "median_launch_us": round(median_launch * 1e6, 3),
+        },
+    }
+    if not args.no_cpu_baseline and not args.copy_kernel:
+        gbs, sample = work.cpu_oracle_sample(args.cpu_seconds)
+        rec["cpu_baseline"] = {"value": round(gbs, 4), "unit": "GB/s", "cores": threads_used(),
+                               "kind": "oracle", "sample": sample}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -155,7 +155,8 @@ size_t moe_route_workspace_bytes(int T, int D, int E);
  *   topk_idx device int32 [T][k];  topk_w device fp32 [T][k]
  *   ws       device workspace (zero-filled before first use, left zero-filled)
  * Errors: INVALID_ARG, UNSUPPORTED (T outside 1..64, E outside 1..256,
- * k > E or k > 16, D % 8), ALIGNMENT, WORKSPACE, HIP. */
+ * roundup(T, 8) * E > 4096, k > E or k > 16, D % 8), ALIGNMENT, WORKSPACE,
+ * HIP. */
 int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k,
                    int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
                    size_t ws_bytes, void* stream);
@@ -188,10 +189,13 @@ size_t moe_workspace_bytes(const q4_moe_desc* w, int T, int k);
  * projections; the combine sums in a fixed order (deterministic).
  *   x        device f16 [T][D]; topk_idx device int32 [T][k] (each in 0..E-1);
  *   topk_w   device fp32 [T][k]; y device [T][D] of out_dtype (Q4_F32, Q4_F16)
- *   ws       device workspace of ws_bytes >= moe_workspace_bytes
+ *   ws       device workspace of ws_bytes >= moe_workspace_bytes (scratch for
+ *            h and the per-pair expert outputs; no zero-fill needed)
  * Errors: INVALID_ARG, UNSUPPORTED (T outside 1..16, k outside 1..E,
- * D % 64, F % 64), ALIGNMENT, WORKSPACE, HIP.  Out-of-range expert indices
- * are not checked on the device: their pairs are dropped. */
+ * D % 64, F % 64, E > 1024), ALIGNMENT, WORKSPACE, HIP.  Expert indices live
+ * on the device and are not validated: pairs whose index is outside 0..E-1
+ * are dropped, and so are pairs beyond the 16th routed to one expert (only
+ * possible if a token names the same expert twice). */
 int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws,
                       size_t ws_bytes, void* stream);

@@ -349,7 +349,8 @@ int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, in
   if (E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", __func__, E);
   if (k > E || k > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d must be <= E=%d and <= 16", __func__, k, E);
   if (D % 8) return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d is not a multiple of 8", __func__, D);
-  if (E % 4) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d is not a multiple of 4", __func__, E);
+  if ((T + 7) / 8 * 8 * E > 4096)
+    return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d (rounded up to a multiple of 8) times E=%d exceeds 4096", __func__, T, E);
   REQUIRE_ALIGNED(x);
   REQUIRE_ALIGNED(w_router);
   REQUIRE_ALIGNED(topk_idx);

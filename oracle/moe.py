@@ -159,25 +159,29 @@ def moe_abs_bound(moe, idx, w, gemm_rel: float = 1e-3, combine_rel: float = 1e-6
               G_j = sum_k |x_k Wg[j,k]|,  U_j = sum_k |x_k Wu[j,k]|
       bound = sum_e |w_e| (gemm_rel * sum_j |h_j Wd[n,j]| + sum_j |Wd[n,j]| dh_j)
               + combine_rel * sum_e |w_e o_e[n]|
+
+    Each expert's weights are decoded once for all the tokens routed to it.
     """
     x = np.asarray(moe.x, np.float64)
     T, D = x.shape
     k = idx.shape[1]
-    bound = np.zeros((T, D))
-    cache = {}
+    users = {}
     for t in range(T):
-        experts = [(int(idx[t, j]), float(w[t, j])) for j in range(k)]
-        if moe.has_shared:
-            experts.append((moe.E, 1.0))
-        xt = x[t:t + 1]
-        for e, we in experts:
-            if e not in cache:
-                cache[e] = _expert_mats(moe, e)
-            wg, wu, wd = cache[e]
-            g, u, h, o = _ffn(xt, wg, wu, wd)
-            G = np.abs(xt) @ np.abs(wg).T
-            U = np.abs(xt) @ np.abs(wu).T
-            dh = gemm_rel * (np.abs(gelu_tanh_deriv(g) * u) * G + np.abs(gelu_tanh(g)) * U)
-            term = gemm_rel * (np.abs(h) @ np.abs(wd).T) + dh @ np.abs(wd).T
-            bound[t] += abs(we) * term[0] + combine_rel * abs(we * o[0])
+        for j in range(k):
+            users.setdefault(int(idx[t, j]), []).append((t, float(w[t, j])))
+    if moe.has_shared:
+        users[moe.E] = [(t, 1.0) for t in range(T)]
+    bound = np.zeros((T, D))
+    for e in sorted(users):
+        wg, wu, wd = _expert_mats(moe, e)
+        rows = [t for t, _ in users[e]]
+        we = np.array([v for _, v in users[e]])
+        xr = x[rows]
+        g, u, h, o = _ffn(xr, wg, wu, wd)
+        G = np.abs(xr) @ np.abs(wg).T
+        U = np.abs(xr) @ np.abs(wu).T
+        dh = gemm_rel * (np.abs(gelu_tanh_deriv(g) * u) * G + np.abs(gelu_tanh(g)) * U)
+        term = gemm_rel * (np.abs(h) @ np.abs(wd).T) + dh @ np.abs(wd).T
+        contrib = np.abs(we)[:, None] * term + combine_rel * np.abs(we[:, None] * o)
+        np.add.at(bound, rows, contrib)
     return bound

@@ -1,0 +1,198 @@
+"""GPU parity of the router and the grouped MoE layer against the oracle.
+
+Bars: router top-k indices bit-exact (the decision taken on fp32 logits, ties
+to the lower index; oracle near-ties within the fp32 logit error are checked
+for validity instead), weights within 1e-6, logits within the fp32
+summation bound; the MoE layer within the composed first-order bound of the
+per-GEMM 1e-3 * sum|a w| criterion (oracle.moe_abs_bound); repeated calls
+bitwise identical."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def q4():
+    import moe_w4a16_skinny_amd as m
+    return m
+
+
+def note(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def logit_tol(x, wr):
+    # fp32 accumulation of D products: |err| <= D * 2^-24 * sum|x w| (worst case), plus slack
+    D = x.shape[1]
+    return (D * 2.0 ** -24) * (np.abs(x.astype(np.float64)) @ np.abs(wr.astype(np.float64))) + 1e-12
+
+
+def check_router(x, wr, k, renormalize=False):
+    m = q4()
+    logits, idx, w = m.moe_route_topk(dev(x), dev(wr), k, renormalize=renormalize)
+    torch.cuda.synchronize()
+    lref, iref, wref = oracle.route_topk(x, wr, k, renormalize=renormalize)
+    tol = logit_tol(x, wr)
+    lg = logits.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(lg - lref) <= tol), "router logits outside the fp32 summation bound"
+    ig, wg = idx.cpu().numpy(), w.cpu().numpy()
+    near = 0
+    for t in range(x.shape[0]):
+        if np.array_equal(ig[t], iref[t]):
+            assert np.max(np.abs(wg[t] - wref[t])) <= 1e-6
+            continue
+        # only acceptable if the oracle ranking has a near tie inside the top k+1
+        l32 = lref[t]
+        order = np.lexsort((np.arange(len(l32)), -l32))
+        kk = min(k + 1, len(l32))
+        gaps = np.diff(-l32[order[:kk]])
+        assert np.min(gaps) <= 2 * np.max(tol[t]), f"token {t}: top-k differs without a near tie"
+        # the GPU's choice must be consistent with its own logits
+        own = np.lexsort((np.arange(len(lg[t])), -lg[t]))[:k]
+        assert np.array_equal(ig[t], own)
+        near += 1
+    if near:
+        note(f"router: {near} token(s) with near-tied logits (either order valid)")
+    # the GPU's indices are its own top-k of its own logits, exactly
+    for t in range(x.shape[0]):
+        own = np.lexsort((np.arange(lg.shape[1]), -lg[t]))[:k]
+        assert np.array_equal(ig[t], own)
+    return ig, wg
+
+
+def test_router_gemma_shape():
+    moe_x = synth.act_f16(104, 16, 2816)
+    wr = synth._rng(104, synth.TAG_ROUTER).standard_normal((2816, 128), dtype=np.float32) * np.float32(0.02)
+    check_router(moe_x, wr, 8)
+    check_router(moe_x, wr, 8, renormalize=True)
+
+
+@pytest.mark.parametrize("T,D,E,k", [(1, 64, 8, 1), (3, 64, 16, 4), (64, 512, 64, 16), (16, 8192, 128, 8),
+                                     (5, 200, 12, 12), (32, 2816, 128, 8), (8, 64, 256, 2)])
+def test_router_shapes(T, D, E, k):
+    rng = np.random.default_rng(T * 131 + D + E + k)
+    x = rng.standard_normal((T, D)).astype(np.float16)
+    wr = (rng.standard_normal((D, E)) * 0.02).astype(np.float32)
+    check_router(x, wr, k)
+
+
+def test_router_zero_matrix_and_ties():
+    m = q4()
+    x = np.random.default_rng(0).standard_normal((4, 256)).astype(np.float16)
+    _, idx, w = m.moe_route_topk(dev(x), dev(np.zeros((256, 128), np.float32)), 8)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(8, dtype=np.int32), (4, 1)))
+    assert np.all(w.cpu().numpy() == np.float32(1.0 / 128))
+    xp = np.abs(x)
+    wr = (np.random.default_rng(1).standard_normal((256, 32)) * 0.02).astype(np.float32)
+    wr[:, 3] = 0.05               # duplicate columns with the largest logits ->
+    wr[:, 20] = 0.05              # bitwise-equal logits at the top
+    logits, idx, _ = m.moe_route_topk(dev(xp), dev(wr), 16)
+    torch.cuda.synchronize()
+    lg, ig = logits.cpu().numpy(), idx.cpu().numpy()
+    assert np.array_equal(lg[:, 3], lg[:, 20])
+    assert np.all(ig[:, 0] == 3) and np.all(ig[:, 1] == 20)   # lower index first
+
+
+# ---------------------------------------------------------------- MoE layer
+
+_CACHE = {}
+
+
+def layer(seed, **kw):
+    key = (seed, tuple(sorted(kw.items())))
+    if key not in _CACHE:
+        moe = synth.moe_layer(seed, **kw)
+        _CACHE.clear()
+        _CACHE[key] = (moe, q4().moe_pack_experts(moe.gate, moe.up, moe.down, moe.E, moe.has_shared))
+    return _CACHE[key]
+
+
+def run_moe(moe, mw, idx, w, out_dtype=torch.float32):
+    y = q4().moe_grouped_qgemm(mw, dev(moe.x), dev(idx.astype(np.int32)), dev(w.astype(np.float32)),
+                               out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def check_moe(moe, mw, idx, w, out_dtype=torch.float32, what=""):
+    w32 = w.astype(np.float32).astype(np.float64)   # the kernel uses the fp32 weights it is given
+    y = run_moe(moe, mw, idx, w32, out_dtype)
+    ref, _ = oracle.moe_ref_grouped(moe, idx, w32)
+    bnd = oracle.moe_abs_bound(moe, idx, w32)
+    if out_dtype == torch.float16:
+        bnd = bnd + np.abs(ref) * 2.0 ** -11
+    err = np.abs(y - ref)
+    worst = np.max(err / bnd)
+    note(f"moe {what}: worst err/bound {worst:.3e}")
+    assert np.all(np.isfinite(y)) and np.all(err <= bnd), f"{what}: worst err/bound {worst:.3e}"
+    return y
+
+
+def test_moe_gemma_layer_oracle_routing():
+    note("generating the 129-expert layer")
+    moe, mw = layer(104)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    note(f"active experts: {len(set(idx.ravel().tolist()))} + shared")
+    y1 = check_moe(moe, mw, idx, w, what="gemma T=16 E=128+1 top-8")
+    y2 = run_moe(moe, mw, idx, w.astype(np.float32).astype(np.float64))
+    assert np.array_equal(y1, y2), "MoE not deterministic"
+
+
+def test_moe_gemma_layer_gpu_router_end_to_end():
+    m = q4()
+    moe, mw = layer(104)
+    _, idx, w = m.moe_route_topk(dev(moe.x), dev(moe.w_router), moe.k, want_logits=False)
+    y = m.moe_grouped_qgemm(mw, dev(moe.x), idx, w)
+    torch.cuda.synchronize()
+    _, iref, wref = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    assert np.array_equal(idx.cpu().numpy(), iref)
+    w32 = w.cpu().numpy().astype(np.float64)
+    ref, _ = oracle.moe_ref_grouped(moe, iref, w32)
+    bnd = oracle.moe_abs_bound(moe, iref, w32)
+    assert np.all(np.abs(y.cpu().numpy() - ref) <= bnd)
+
+
+def test_moe_all_tokens_same_experts_f16_out():
+    moe, mw = layer(104)
+    T = moe.T
+    idx = np.tile(np.array([5, 77, 3, 127, 0, 64, 100, 9], np.int32), (T, 1))   # 16 rows per expert
+    w = np.random.default_rng(2).uniform(0.01, 0.2, (T, 8))
+    check_moe(moe, mw, idx, w, what="8 experts x 16 tokens")
+    check_moe(moe, mw, idx, w, out_dtype=torch.float16, what="f16 out")
+
+
+@pytest.mark.parametrize("T,D,E,F,k,shared", [(1, 128, 4, 64, 1, True), (5, 192, 6, 192, 3, False),
+                                               (16, 256, 8, 128, 8, True), (16, 128, 3, 704, 2, True),
+                                               (7, 2816, 16, 704, 4, True), (2, 64, 1, 64, 1, False)])
+def test_moe_small_layers(T, D, E, F, k, shared):
+    moe, mw = layer(900 + T + D + E + F + k, T=T, D=D, E=E, F=F, k=k, has_shared=shared)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    check_moe(moe, mw, idx, w, what=f"T={T} D={D} E={E} F={F} k={k} shared={shared}")
+
+
+def test_moe_invalid_index_dropped():
+    moe, mw = layer(950, T=4, D=128, E=6, F=64, k=2, has_shared=True)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    bad = idx.copy()
+    bad[1, 1] = 6          # == E: not an expert
+    bad[2, 0] = -3
+    y = run_moe(moe, mw, bad, w.astype(np.float32).astype(np.float64))
+    w0 = w.astype(np.float32).astype(np.float64).copy()
+    w0[1, 1] = 0.0
+    w0[2, 0] = 0.0
+    ref, _ = oracle.moe_ref_grouped(moe, idx, w0)   # same as dropping those two pairs
+    bnd = oracle.moe_abs_bound(moe, idx, w0) + 1e-12
+    assert np.all(np.abs(y - ref) <= bnd)
