@@ -101,7 +101,11 @@ class GemmWork:
         self.out = torch.empty((M, N), dtype=out_dt, device="cuda")
         self.want_argmax = bool(spec.get("argmax"))
         self.amax = torch.empty(16, dtype=torch.int32, device="cuda")
-        self.ws = q4.workspace(256)
+        if spec["kind"] == "nvfp4":
+            self.wsb = q4.raw().qgemm_nvfp4_workspace_bytes(M, K, N, int(bool(spec.get("argmax"))))
+        else:
+            self.wsb = q4.raw().qgemm_affine4_workspace_bytes(M, K, N)
+        self.ws = q4.workspace(max(self.wsb, 256))
         self.i = 0
         self.kernel_names = ["qgemm_kernel"]
 
@@ -119,7 +123,8 @@ class GemmWork:
                                  C.c_void_p(self.ws.data_ptr()), self.ws.numel(), s)
         else:
             rc = lib.qgemm_affine4(w, C.c_void_p(self.a.data_ptr()), self.M, self.K, self.N,
-                                   C.c_void_p(self.out.data_ptr()), q4._dtype_code(self.out.dtype), s)
+                                   C.c_void_p(self.out.data_ptr()), q4._dtype_code(self.out.dtype),
+                                   C.c_void_p(self.ws.data_ptr()), self.ws.numel(), s)
         if rc != 0:
             q4._check(rc)
 
@@ -151,6 +156,64 @@ class GemmWork:
         bytes_done = done * rows * self.alg_bytes / N
         return bytes_done / el / 1e9, f"{done} oracle GEMMs of {rows} weight rows (M={self.M}, K={self.K}) " \
                                       f"in {el:.1f}s"
+
+
+class MoeWork:
+    """One step = moe_route_topk + moe_grouped_qgemm on the 128 + 1 expert layer."""
+
+    def __init__(self, name, spec, hot):
+        import numpy as np
+        import torch
+
+        import moe_w4a16_skinny_amd as q4
+        import synth
+        self.name, self.spec, self.q4 = name, spec, q4
+        t0 = time.time()
+        moe = synth.moe_layer(spec["seed"], T=spec["T"], D=spec["D"], E=spec["E"], F=spec["F"], k=spec["k"],
+                              has_shared=spec["has_shared"])
+        self.moe = moe
+        mw = q4.moe_pack_experts(moe.gate, moe.up, moe.down, moe.E, moe.has_shared)
+        log(f"[bench] {name}: layer generated and packed in {time.time() - t0:.1f}s")
+        self.x = torch.from_numpy(moe.x).cuda()
+        self.wr = torch.from_numpy(moe.w_router).cuda()
+        layer_bytes = mw.gate.numel() + mw.up.numel() + mw.down.numel()
+        self.copies = 1 if hot else max(2, -(-ROTATE_BYTES // layer_bytes))
+        self.layers = [mw]
+        for _ in range(self.copies - 1):
+            self.layers.append(q4.MoeWeights(mw.E, mw.has_shared, mw.D, mw.F, mw.gate.clone(), mw.up.clone(),
+                                              mw.down.clone(), mw.g_gate, mw.g_up, mw.g_down))
+        self.out = torch.empty((moe.T, moe.D), dtype=torch.float32, device="cuda")
+        self.i = 0
+        # algorithmic bytes: router matrix + every expert that receives a token + the shared one
+        _, idx, _ = q4.moe_route_topk(self.x, self.wr, moe.k, want_logits=False)
+        torch.cuda.synchronize()
+        self.active = len(set(idx.cpu().numpy().ravel().tolist()))
+        per_matrix = moe.F * moe.D // 2 + moe.F * moe.D // 16 + 4
+        self.alg_bytes = moe.D * moe.E * 4 + (self.active + int(moe.has_shared)) * 3 * per_matrix
+        self.kernel_names = ["moe step: route_kernel + moe_gate_up_kernel + moe_down_kernel + moe_combine_kernel"]
+        self.dtype = "f16"
+
+    def step(self):
+        q4 = self.q4
+        mw = self.layers[self.i % self.copies]
+        self.i += 1
+        _, idx, w = q4.moe_route_topk(self.x, self.wr, self.moe.k, want_logits=False)
+        q4.moe_grouped_qgemm(mw, self.x, idx, w, out=self.out)
+
+    def config(self):
+        m = self.moe
+        return {"workload": self.name, "T": m.T, "D": m.D, "E": m.E, "shared_experts": int(m.has_shared),
+                "F": m.F, "top_k": m.k, "active_experts": self.active, "weights": "nvfp4",
+                "weight_copies_rotated": self.copies}
+
+    def cpu_oracle_sample(self, seconds):
+        import oracle
+        m = self.moe
+        t0 = time.perf_counter()
+        _, idx, w = oracle.route_topk(m.x, m.w_router, m.k)
+        oracle.moe_ref_grouped(m, idx, w)
+        el = time.perf_counter() - t0
+        return self.alg_bytes / el / 1e9, f"1 full oracle layer (router + {self.active}+1 experts, T={m.T}) in {el:.1f}s"
 
 
 class CopyWork:
@@ -191,7 +254,6 @@ def main():
         name = args.workload
         spec = synth.WORKLOADS[name]
         if spec["kind"] == "moe":
-            from moe_bench import MoeWork  # noqa: F401  (added with the MoE kernels)
             work = MoeWork(name, spec, args.hot)
         else:
             work = GemmWork(name, spec, args.hot)
@@ -215,6 +277,19 @@ def main():
     per.sort()
     mean_launch = sum(per) / K
     median_launch = per[K // 2]
+
+    # dispatch interval of a trivial kernel launched the same way (stream-ordered, back to back)
+    tiny = torch.zeros(1, device="cuda")
+    for _ in range(20):
+        tiny.add_(1.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(200):
+        tiny.add_(1.0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    launch_interval = e0.elapsed_time(e1) * 1e-3 / 200
 
     value = work.alg_bytes * K / wall / 1e9
     achieved = work.alg_bytes / mean_launch / 1e9
@@ -244,6 +319,7 @@ def main():
             "alg_bytes_per_launch": work.alg_bytes,
             "mean_launch_us": round(mean_launch * 1e6, 3),
             "median_launch_us": round(median_launch * 1e6, 3),
+            "empty_kernel_interval_us": round(launch_interval * 1e6, 3),
         },
     }
     if not args.no_cpu_baseline and not args.copy_kernel:

@@ -34,8 +34,14 @@
  *             (uint16 bit patterns) [N][K/64]; w = q*scale + bias.
  *     The packed layouts produced by the repack calls are private to the
  *     library; only their byte sizes are part of the ABI.
- *   - Entries are re-entrant.  Two calls that share a workspace must not run
- *     concurrently.
+ *   - Workspaces: an entry point that needs device scratch takes (ws,
+ *     ws_bytes) and has a *_workspace_bytes query.  A workspace must be
+ *     zero-filled before its first use.  Its first 32 KiB hold only counters,
+ *     which every call leaves at zero; scratch lives above them.  One buffer
+ *     of the largest queried size can therefore serve every entry point, as
+ *     long as the calls that share it are ordered on one stream (calls that
+ *     overlap in time on a shared workspace race).
+ *   - Entries are re-entrant.
  */
 #ifndef Q4MI_H
 #define Q4MI_H
@@ -106,8 +112,14 @@ int q4_affine4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes,
  * Skinny GEMMs.  y[m][n] = sum_k a[m][k] * w[n][k], 1 <= M <= 16.
  * ------------------------------------------------------------------------- */
 
-/* Bytes of device workspace qgemm_nvfp4 needs (0 unless want_argmax). */
+/* Bytes of device workspace qgemm_nvfp4 needs for this shape (0 if none):
+ * the fused argmax's counter and keys, and, for shapes whose K is split
+ * across workgroups, the fp32 partial sums and their arrival counters.
+ * Depends only on (M, K, N, want_argmax) and the Q4MI_GEMM_CFG override. */
 size_t qgemm_nvfp4_workspace_bytes(int M, int64_t K, int64_t N, int want_argmax);
+
+/* Same for qgemm_affine4. */
+size_t qgemm_affine4_workspace_bytes(int M, int64_t K, int64_t N);
 
 /* NVFP4 W4A16 GEMM [README "Everything it has": the M <= 16 GEMM with
  * in-register FP4 -> f16 dequant; "Why it's NVIDIA-only": E2M1 x E4M3/16 x
@@ -119,8 +131,9 @@ size_t qgemm_nvfp4_workspace_bytes(int M, int64_t K, int64_t N, int want_argmax)
  *             largest value of row m of `out` as stored, lowest index on ties,
  *             NaN values skipped (-1 if the whole row is NaN) -- tree_round's
  *             argmax of [ISSUE "Why now"], fused into the GEMM.
- *   ws        device workspace of ws_bytes >= the query; it must be zero-filled
- *             before its first use and is left zero-filled by every call.
+ *   ws        device workspace of ws_bytes >= the query (NULL if the query is
+ *             0); it must be zero-filled before its first use, and every call
+ *             leaves its counters at zero again.
  * Errors: INVALID_ARG, UNSUPPORTED (M outside 1..16, N % 16, K % 16),
  * ALIGNMENT, WORKSPACE, HIP. */
 int qgemm_nvfp4(const void* w_packed, float global_scale, const void* a, int M, int64_t K,
@@ -134,10 +147,12 @@ int qgemm_nvfp4(const void* w_packed, float global_scale, const void* a, int M, 
  *   w_packed  device, from q4_affine4_repack
  *   a         device bf16 [M][K] row-major
  *   out       device [M][N] of out_dtype (Q4_F32 or Q4_BF16)
+ *   ws        device workspace of ws_bytes >= qgemm_affine4_workspace_bytes
+ *             (NULL if that is 0), zero-filled before first use as above
  * Errors: INVALID_ARG, UNSUPPORTED (M outside 1..16, N % 16, K % 64),
- * ALIGNMENT, HIP. */
+ * ALIGNMENT, WORKSPACE, HIP. */
 int qgemm_affine4(const void* w_packed, const void* a, int M, int64_t K, int64_t N, void* out,
-                  int out_dtype, void* stream);
+                  int out_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Top-k MoE.  [DOC 3.2, 4.6]; [README]: 128 experts, top-8, one shared.
@@ -191,7 +206,7 @@ size_t moe_workspace_bytes(const q4_moe_desc* w, int T, int k);
  *   topk_w   device fp32 [T][k]; y device [T][D] of out_dtype (Q4_F32, Q4_F16)
  *   ws       device workspace of ws_bytes >= moe_workspace_bytes (scratch for
  *            h and the per-pair expert outputs; no zero-fill needed)
- * Errors: INVALID_ARG, UNSUPPORTED (T outside 1..16, k outside 1..E,
+ * Errors: INVALID_ARG, UNSUPPORTED (T outside 1..16, k outside 1..min(E, 64),
  * D % 64, F % 64, E > 1024), ALIGNMENT, WORKSPACE, HIP.  Expert indices live
  * on the device and are not validated: pairs whose index is outside 0..E-1
  * are dropped, and so are pairs beyond the 16th routed to one expert (only

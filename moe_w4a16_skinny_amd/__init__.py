@@ -46,7 +46,8 @@ _SIGS = {
     "q4_affine4_unpack": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "qgemm_nvfp4_workspace_bytes": (_sz, [_i32, _i64, _i64, _i32]),
     "qgemm_nvfp4": (_i32, [_vp, _f32, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
-    "qgemm_affine4": (_i32, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp]),
+    "qgemm_affine4_workspace_bytes": (_sz, [_i32, _i64, _i64]),
+    "qgemm_affine4": (_i32, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _sz, _vp]),
     "moe_route_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_route_topk": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_workspace_bytes": (_sz, [C.POINTER(q4_moe_desc), _i32, _i32]),
@@ -213,7 +214,10 @@ def qgemm_affine4(w_packed, a, N: int, out=None, out_dtype=None):
     M, K = a.shape
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
-    _check(_lib.qgemm_affine4(_tptr(w_packed), _tptr(a), M, K, N, _tptr(out), _dtype_code(out.dtype), _stream()))
+    wsb = _lib.qgemm_affine4_workspace_bytes(M, K, N)
+    ws = workspace(wsb, a.device) if wsb else None
+    _check(_lib.qgemm_affine4(_tptr(w_packed), _tptr(a), M, K, N, _tptr(out), _dtype_code(out.dtype), _tptr(ws),
+                              wsb, _stream()))
     return out
 
 

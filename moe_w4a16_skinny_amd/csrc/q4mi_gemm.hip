@@ -7,13 +7,17 @@
 // CUDA", "Why now": qlinear's affine 4-bit path with 64-value group sums.]
 //
 // Design (gfx950):
-//  * One wave owns P panels of 16 output columns and a contiguous range of
-//    128-k tiles; KW waves of a workgroup split K and reduce through LDS in a
-//    fixed order; PW independent wave groups share a workgroup.
+//  * A workgroup owns a block of PB panels (16 output columns each) and one
+//    of KS ranges of 128-k tiles.  It stages that k-range of the activations
+//    in LDS once, in MFMA operand order, then its W waves stream groups of P
+//    panels (round-robin inside the block) through the k-range; the register
+//    ring keeps D tiles of weight loads in flight across group boundaries.
 //  * Per tile each lane issues one 16-byte non-temporal load of codes per
-//    panel (1 KiB contiguous per wave) plus one small scale load, and four
-//    16-byte loads of activations (L2-resident, shared by the P panels).
-//  * Loads run D tiles ahead of the math (register ring).
+//    panel (1 KiB contiguous per wave) plus one small scale load; the four
+//    activation operands come from LDS with conflict-free ds_read_b128.
+//  * KS > 1: each workgroup writes fp32 partial sums to the workspace; the
+//    last of the KS workgroups of a block (arrival counter) adds them in
+//    ks order (deterministic) and applies the epilogue.
 //  * NVFP4: v_cvt_scalef32_pk_f16_fp4 turns 2 codes into 2 f16 (scale operand
 //    1.0: the hardware applies only its power-of-two part), then one
 //    v_pk_mul_f16 by the E4M3 group scale (decoded by v_cvt_scalef32_pk_f16_fp8).
@@ -37,116 +41,168 @@ namespace q4mi {
 namespace {
 using namespace dev;
 
-struct KParams {
+struct KP2 {
   GemmArgs g;
-  int nmain;      // full tiles needing no k bound check
-  int tail;       // 0 none, 1 half tile, 2 full tile crossing K
   int npanels;
+  int ntiles;      // packed tiles per panel, half tile included
+  int half_t;      // packed index of the half tile, -1 if none
+  int KS, KR;      // k-splits and tiles per split
+  int KW;          // waves splitting a workgroup's k-range (one group per wave if > 1)
+  int PB;          // panels per workgroup block
+  int nblocks;     // panel blocks
+  float* partial;  // [KS][M][N] fp32 (KS > 1)
+  unsigned* bcnt;  // [nblocks] arrival counters (KS > 1), left at zero
 };
 
-template <int FMT, int P, int KW, int PW, int D>
-__global__ __launch_bounds__(64 * KW * PW) void qgemm_kernel(KParams kp) {
+constexpr int kMaxKS = 8;  // partial sums summed per output by the last workgroup
+
+template <int FMT, int P, int W, int D>
+__global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
+  extern __shared__ u32x4 alds[];
+  __shared__ unsigned long long sbest[16];
+  __shared__ int s_last;
+  __shared__ float red[W][P][4][64];  // intra-workgroup k-split partials (KW > 1)
   const GemmArgs& g = kp.g;
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int kw = wid % KW;
-  const int pw = wid / KW;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = lane >> 4;
   const int c = lane & 15;
-
-  const int panel0 = (blockIdx.x * PW + pw) * P;
-  const uint8_t* pbase[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    int pi = panel0 + p;
-    pi = pi < kp.npanels ? pi : kp.npanels - 1;  // clamp: loads stay in bounds, stores are skipped
-    pbase[p] = g.w + static_cast<size_t>(pi) * static_cast<size_t>(g.panel_bytes);
-  }
-  const bool arow_ok = c < g.M;
-  const uint16_t* arow = g.a + static_cast<size_t>(arow_ok ? c : 0) * static_cast<size_t>(g.K);
-
-  // this wave's tiles: [t0, t1) of the checked-free range
-  const int per = (kp.nmain + KW - 1) / KW;
-  const int t0 = kw * per;
-  const int t1 = min(kp.nmain, t0 + per);
-  const int nt = t1 > t0 ? t1 - t0 : 0;
-
-  f32x4 acc[P][2];
-#pragma unroll
-  for (int p = 0; p < P; ++p) acc[p][0] = acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  dev::wave_accumulate<FMT, P, D>(acc, pbase, arow, arow_ok, g.K, t0, nt,
-                                  kw == KW - 1 ? kp.tail : 0, kp.nmain);
-
-  f32x4 res[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) res[p] = acc[p][0] + acc[p][1];
-
+  const int KS = kp.KS, KW = kp.KW;
+  const int PWv = W / KW;                                  // wave columns (panel groups in parallel)
+  const int kw = w % KW, pw = w / KW;
+  const int ks = blockIdx.x % KS;
+  const int pb = blockIdx.x / KS;
+  const int kt0 = ks * kp.KR;
+  const int KRg = min(kp.ntiles, kt0 + kp.KR) - kt0;       // this workgroup's tiles
+  const int KRw = (KRg + KW - 1) / KW;                     // per k-split wave
+  const int wt0 = min(KRg, kw * KRw);
+  const int wtn = min(KRg, wt0 + KRw) - wt0;
+  const int p0 = pb * kp.PB;
+  const int pend = min(kp.npanels, p0 + kp.PB);
+  const int ngb = (pend - p0 + P - 1) / P;                 // panel groups in the block
+  const int ng = ngb > pw ? (ngb - pw + PWv - 1) / PWv : 0; // this wave's: pw, pw + PWv, ...
   const int M = g.M;
   const float gs = g.gscale;
-  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};  // argmax keys for rows 4o + r
 
-  if constexpr (KW == 1) {
+  if (threadIdx.x < 16) sbest[threadIdx.x] = 0ull;
+  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+
+  // final value of output (m, n) -> stored, argmax key kept
+  auto finish = [&](int r, int m, int n, float v) {
+    const float y = store_out(g.out, g.out_dtype, static_cast<size_t>(m) * g.N + n, gs * v);
+    const unsigned long long key = argmax_key(y, n);
+    best[r] = key > best[r] ? key : best[r];
+  };
+  auto gbase = [&](int gi, int p) -> const uint8_t* {
+    int panel = p0 + (pw + gi * PWv) * P + p;
+    panel = panel < kp.npanels ? panel : kp.npanels - 1;   // in-bounds load, store skipped
+    return g.w + static_cast<size_t>(panel) * static_cast<size_t>(g.panel_bytes);
+  };
+  auto pre = [&]() {
+    stage_a_lds(alds, g.a, M, g.K, kt0, KRg);
+    __syncthreads();
+  };
+  f32x4 keep[P];  // KW > 1: this wave's single group, reduced after the stream
+#pragma unroll
+  for (int p = 0; p < P; ++p) keep[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto epi = [&](int gi, f32x4 (&acc)[P][2]) {
+    if (KW > 1) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) keep[p] = acc[p][0] + acc[p][1];
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int pi = panel0 + p;
-      if (pi >= kp.npanels) continue;
-      const int n = pi * 16 + c;
+      const int panel = p0 + (pw + gi * PWv) * P + p;
+      if (panel >= pend) continue;
+      const int n = panel * 16 + c;
+      const f32x4 v = acc[p][0] + acc[p][1];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * o + r;
-        if (m < M) {
-          const float v = store_out(g.out, g.out_dtype, static_cast<size_t>(m) * g.N + n, gs * res[p][r]);
-          const unsigned long long key = argmax_key(v, n);
-          best[r] = key > best[r] ? key : best[r];
-        }
+        if (m >= M) continue;
+        if (KS == 1)
+          finish(r, m, n, v[r]);
+        else
+          kp.partial[(static_cast<size_t>(ks) * M + m) * g.N + n] = v[r];
       }
     }
-  } else {
-    __shared__ float red[KW][PW][P][4][64];
+  };
+  stream_groups<FMT, P, D, true>(ng, wtn, kt0 + wt0, kp.half_t, alds + static_cast<size_t>(wt0) * 4 * 64, nullptr,
+                                 false, g.K, gbase, pre, epi);
+
+  if (KW > 1) {  // one group per wave: sum the KW k-slices in order
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[kw][pw][p][r][lane] = res[p][r];
+      for (int r = 0; r < 4; ++r) red[w][p][r][lane] = keep[p][r];
     __syncthreads();
-    // the P x 4 (panel, accumulator row) items of the group are shared out
-    // over its KW waves; each item is summed over the KW partials in order
+    if (kw == 0 && ng > 0) {
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp)
+      for (int p = 0; p < P; ++p) {
+        const int panel = p0 + pw * P + p;
+        if (panel >= pend) continue;
+        const int n = panel * 16 + c;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if ((pp * 4 + r) % KW != kw) continue;
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < KW; ++j) s += red[j][pw][pp][r][lane];
-        const int pi = panel0 + pp;
-        const int m = 4 * o + r;
-        if (pi < kp.npanels && m < M) {
-          const int n = pi * 16 + c;
-          const float v = store_out(g.out, g.out_dtype, static_cast<size_t>(m) * g.N + n, gs * s);
-          const unsigned long long key = argmax_key(v, n);
-          best[r] = key > best[r] ? key : best[r];
+        for (int r = 0; r < 4; ++r) {
+          const int m = 4 * o + r;
+          if (m >= M) continue;
+          float v = 0.f;
+          for (int j = 0; j < KW; ++j) v += red[pw * KW + j][p][r][lane];
+          if (KS == 1)
+            finish(r, m, n, v);
+          else
+            kp.partial[(static_cast<size_t>(ks) * M + m) * g.N + n] = v;
         }
       }
+    }
   }
 
-  if (g.argmax) {
-    __shared__ unsigned long long sbest[16];
-    if (threadIdx.x < 16) sbest[threadIdx.x] = 0ull;
+  bool final_wg = true;  // does this workgroup hold final values of its block?
+  if (KS > 1) {
+    __syncthreads();  // every wave's partial stores have reached L2
+    if (threadIdx.x == 0) s_last = arrive(kp.bcnt + pb) == static_cast<unsigned>(KS - 1);
     __syncthreads();
+    final_wg = s_last != 0;
+    if (final_wg) {
+      const int ncols = (pend - p0) * 16;
+      // all KS partials of an item are loaded together, then summed in ks order
+      for (int q = threadIdx.x; q < M * ncols; q += 64 * W) {
+        const int m = q / ncols;
+        const int n = p0 * 16 + (q - m * ncols);
+        float v[kMaxKS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const unsigned long long k = max_key_16(best[r]);
-      if (c == 0 && k != 0ull) atomicMax(&sbest[4 * o + r], k);
+        for (int j = 0; j < kMaxKS; ++j)
+          v[j] = j < KS ? load_coherent(kp.partial + (static_cast<size_t>(j) * M + m) * g.N + n) : 0.f;
+        float sacc = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxKS; ++j) sacc += v[j];
+        const float y = store_out(g.out, g.out_dtype, static_cast<size_t>(m) * g.N + n, gs * sacc);
+        if (g.argmax) {
+          const unsigned long long key = argmax_key(y, n);
+          if (key) atomicMax(&sbest[m], key);
+        }
+      }
+      if (threadIdx.x == 0) atomicExch(kp.bcnt + pb, 0u);
+    }
+  }
+
+  if (g.argmax && final_wg) {
+    if (KS == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const unsigned long long k = max_key_16(best[r]);
+        if (c == 0 && k != 0ull) atomicMax(&sbest[4 * o + r], k);
+      }
     }
     __syncthreads();
     if (threadIdx.x < 16 && static_cast<int>(threadIdx.x) < M && sbest[threadIdx.x] != 0ull)
       atomicMax(g.keys + threadIdx.x, sbest[threadIdx.x]);
-    __threadfence();
     __syncthreads();
     if (threadIdx.x == 0) {
-      const unsigned prev = atomicAdd(g.counter, 1u);
-      if (prev == gridDim.x - 1) {
-        __threadfence();
+      const unsigned prev = arrive(g.counter);
+      if (prev == static_cast<unsigned>(kp.nblocks - 1)) {
+        // keys are read with atomics, which act at the coherence point
         for (int m = 0; m < M; ++m) {
           const unsigned long long k = atomicExch(g.keys + m, 0ull);
           g.argmax[m] = k == 0ull ? -1 : static_cast<int>(0xFFFFFFFFu - static_cast<unsigned>(k & 0xFFFFFFFFull));
@@ -207,26 +263,36 @@ __global__ __launch_bounds__(64) void dequant_kernel(const uint8_t* __restrict__
   }
 }
 
-template <int FMT, int P, int KW, int PW, int D>
-int launch_cfg(const KParams& kp, hipStream_t s) {
-  const int nwg = (kp.npanels + P * PW - 1) / (P * PW);
-  hipLaunchKernelGGL((qgemm_kernel<FMT, P, KW, PW, D>), dim3(nwg), dim3(64 * KW * PW), 0, s, kp);
+
+template <int FMT, int P, int W, int D>
+int launch_cfg(const KP2& kp, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(kp.KR) * 4 * 64 * sizeof(u32x4);
+  static size_t lds_allowed = 48 * 1024;  // per instantiation: raise the dynamic LDS limit on demand
+  if (lds > lds_allowed) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm2_kernel<FMT, P, W, D>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // do not leave the error for the next call
+      return static_cast<int>(e);
+    }
+    lds_allowed = lds;
+  }
+  hipLaunchKernelGGL((qgemm2_kernel<FMT, P, W, D>), dim3(kp.nblocks * kp.KS), dim3(64 * W), lds, s, kp);
   return static_cast<int>(hipGetLastError());
 }
 
 template <int FMT>
-int launch_fmt(const KParams& kp, const GemmCfg& cfg, hipStream_t s) {
-#define Q4_CFG(P_, KW_, PW_, D_) \
-  if (cfg.P == P_ && cfg.KW == KW_ && cfg.PW == PW_) return launch_cfg<FMT, P_, KW_, PW_, D_>(kp, s);
-  Q4_CFG(1, 8, 1, 4)
-  Q4_CFG(1, 4, 1, 4)
-  Q4_CFG(2, 8, 1, 4)
-  Q4_CFG(2, 4, 1, 4)
-  Q4_CFG(2, 2, 1, 4)
-  Q4_CFG(2, 1, 4, 4)
-  Q4_CFG(4, 1, 4, 3)
-  Q4_CFG(4, 2, 1, 3)
-  Q4_CFG(4, 1, 2, 3)
+int launch_fmt(const KP2& kp, const GemmCfg& cfg, hipStream_t s) {
+#define Q4_CFG(P_, W_, D_) \
+  if (cfg.P == P_ && cfg.W == W_ && cfg.D == D_) return launch_cfg<FMT, P_, W_, D_>(kp, s);
+  Q4_CFG(1, 4, 4)
+  Q4_CFG(2, 4, 4)
+  Q4_CFG(2, 8, 4)
+  Q4_CFG(4, 4, 4)
+  Q4_CFG(4, 8, 4)
+  Q4_CFG(2, 4, 8)
+  Q4_CFG(2, 8, 8)
+  Q4_CFG(4, 4, 6)
 #undef Q4_CFG
   return static_cast<int>(hipErrorInvalidConfiguration);
 }
@@ -236,36 +302,72 @@ int launch_fmt(const KParams& kp, const GemmCfg& cfg, hipStream_t s) {
 GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
   (void)fmt;
   (void)M;
-  if (const char* e = std::getenv("Q4MI_GEMM_CFG")) {  // "P,KW,PW" for A/B measurements
-    GemmCfg c{};
-    if (std::sscanf(e, "%d,%d,%d", &c.P, &c.KW, &c.PW) == 3) return c;
+  const int npanels = static_cast<int>(N / 16);
+  const int ntiles = static_cast<int>(full_tiles(K) + (has_half_tile(K) ? 1 : 0));
+  GemmCfg c{};
+  if (const char* e = std::getenv("Q4MI_GEMM_CFG")) {  // "P,W,D,KS,KW,PB" for A/B measurements
+    if (std::sscanf(e, "%d,%d,%d,%d,%d,%d", &c.P, &c.W, &c.D, &c.KS, &c.KW, &c.PB) == 6) {
+      c.KS = c.KS < 1 ? 1 : (c.KS > ntiles ? ntiles : (c.KS > kMaxKS ? kMaxKS : c.KS));
+      c.KW = (c.KW >= 1 && c.W % c.KW == 0) ? c.KW : 1;
+      if (c.KW > 1 && c.PB > c.P * (c.W / c.KW)) c.PB = c.P * (c.W / c.KW);  // one group per wave
+      return c;
+    }
   }
-  const int64_t npanels = N / 16;
-  const int64_t ntiles = (K + kTileK - 1) / kTileK;
-  if (npanels >= 8192) return {4, 1, 4};
-  if (npanels >= 2048) return {2, 1, 4};
-  if (npanels < 256 && ntiles >= 4) return {1, 8, 1};
-  if (ntiles >= 16) return {2, 8, 1};
-  if (ntiles >= 8) return {2, 4, 1};
-  return {2, 2, 1};
+  c.P = 2;
+  c.W = 8;
+  c.D = 4;
+  c.KW = 1;
+  c.KS = 1;
+  // LDS holds a workgroup's k-range of activations, 4 KiB per tile: at most 32 tiles (128 KiB)
+  while ((ntiles + c.KS - 1) / c.KS > 32) c.KS *= 2;
+  if (npanels >= 4096) {
+    // large N: one k-range, persistent blocks over 256 workgroups
+    while ((ntiles + c.KS - 1) / c.KS > 24) c.KS *= 2;
+    c.PB = ((npanels + 255) / 256 + c.P * c.W - 1) / (c.P * c.W) * (c.P * c.W);
+  } else {
+    // small N: 8 waves split each workgroup's k-range over one group of 2 panels
+    c.KW = 8;
+    c.PB = 2;
+    while (c.KS * ((npanels + 1) / 2) < 256 && (ntiles + 2 * c.KS - 1) / (2 * c.KS) >= 8) c.KS *= 2;
+  }
+  if (c.KS > kMaxKS) c.KS = kMaxKS;
+  if (c.KS > ntiles) c.KS = ntiles;
+  if (c.KS > 1 && (npanels + c.PB - 1) / c.PB > kMaxSplitBlocks) c.KS = 1;
+  return c;
 }
 
-int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* stream) {
-  KParams kp{};
+size_t gemm_workspace(int fmt, int M, int64_t K, int64_t N) {
+  const GemmCfg c = choose_gemm_cfg(fmt, M, K, N);
+  const int ntiles = static_cast<int>(full_tiles(K) + (has_half_tile(K) ? 1 : 0));
+  const int KR = (ntiles + c.KS - 1) / c.KS;
+  const int KS = (ntiles + KR - 1) / KR;
+  size_t bytes = kWsCounterBytes;
+  if (KS > 1) bytes += static_cast<size_t>(KS) * M * N * 4;
+  return bytes;
+}
+
+int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* stream) {
+  KP2 kp{};
   kp.g = g;
   kp.npanels = g.N / 16;
-  // tiles entirely inside K need no bound checks; the last one may not be
-  const int full_in = g.K / kTileK;
-  if (g.half) {
-    kp.nmain = g.nfull;
-    kp.tail = 1;
-  } else if (full_in < g.nfull) {
-    kp.nmain = full_in;
-    kp.tail = 2;
-  } else {
-    kp.nmain = g.nfull;
-    kp.tail = 0;
+  kp.ntiles = g.nfull + g.half;
+  kp.half_t = g.half ? g.nfull : -1;
+  kp.KS = cfg.KS;
+  kp.KR = (kp.ntiles + cfg.KS - 1) / cfg.KS;
+  kp.KS = (kp.ntiles + kp.KR - 1) / kp.KR;  // no empty k-range
+  kp.KW = cfg.KW;
+  kp.PB = cfg.PB;
+  kp.nblocks = (kp.npanels + cfg.PB - 1) / cfg.PB;
+  if (kp.KS > kMaxKS) return static_cast<int>(hipErrorInvalidConfiguration);
+  if (kp.KW < 1 || cfg.W % kp.KW != 0 || (kp.KW > 1 && kp.PB > cfg.P * (cfg.W / kp.KW)))
+    return static_cast<int>(hipErrorInvalidConfiguration);
+  if (kp.KS > 1) {
+    if (kp.nblocks > kMaxSplitBlocks) return static_cast<int>(hipErrorInvalidConfiguration);
+    kp.bcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsBlockCounters);
+    kp.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
   }
+  if (kp.KR * 4096 + static_cast<int>(sizeof(float)) * cfg.W * cfg.P * 256 > 156 * 1024)
+    return static_cast<int>(hipErrorInvalidConfiguration);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return fmt == kNvfp4 ? launch_fmt<kNvfp4>(kp, cfg, s) : launch_fmt<kAffine>(kp, cfg, s);
 }

@@ -239,10 +239,15 @@ int q4_affine4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes, 
 // ---- GEMMs ---------------------------------------------------------------
 
 size_t qgemm_nvfp4_workspace_bytes(int M, int64_t K, int64_t N, int want_argmax) {
-  (void)M;
-  (void)K;
-  (void)N;
-  return want_argmax ? 256 : 0;  // counter (+pad) and 16 packed keys
+  if (M < 1 || M > 16 || N <= 0 || K <= 0 || N % 16 || K % 16) return 0;
+  const size_t b = gemm_workspace(kNvfp4, M, K, N);
+  return (b > kWsCounterBytes || want_argmax) ? b : 0;  // counters alone serve only the argmax
+}
+
+size_t qgemm_affine4_workspace_bytes(int M, int64_t K, int64_t N) {
+  if (M < 1 || M > 16 || N <= 0 || K <= 0 || N % 16 || K % 64) return 0;
+  const size_t b = gemm_workspace(kAffine, M, K, N);
+  return b > kWsCounterBytes ? b : 0;
 }
 
 static int gemm_common(int fmt, const char* fn, const void* w_packed, float gscale, const void* a, int M,
@@ -260,13 +265,14 @@ static int gemm_common(int fmt, const char* fn, const void* w_packed, float gsca
   if (!aligned16(w_packed)) return fail(Q4_ERR_ALIGNMENT, "%s: w_packed is not 16-byte aligned", fn);
   if (!aligned16(a)) return fail(Q4_ERR_ALIGNMENT, "%s: a is not 16-byte aligned", fn);
   if (!aligned16(out)) return fail(Q4_ERR_ALIGNMENT, "%s: out is not 16-byte aligned", fn);
-  if (argmax) {
-    if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: argmax requested but ws is NULL", fn);
-    if (ws_bytes < qgemm_nvfp4_workspace_bytes(M, K, N, 1))
-      return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", fn, ws_bytes, qgemm_nvfp4_workspace_bytes(M, K, N, 1));
+  const size_t need = fmt == kNvfp4 ? qgemm_nvfp4_workspace_bytes(M, K, N, argmax != nullptr)
+                                    : qgemm_affine4_workspace_bytes(M, K, N);
+  if (need) {
+    if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL but %zu bytes are needed", fn, need);
+    if (ws_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", fn, ws_bytes, need);
     if (!aligned16(ws)) return fail(Q4_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
-    if (!aligned16(argmax)) return fail(Q4_ERR_ALIGNMENT, "%s: argmax is not 16-byte aligned", fn);
   }
+  if (argmax && !aligned16(argmax)) return fail(Q4_ERR_ALIGNMENT, "%s: argmax is not 16-byte aligned", fn);
   GemmArgs g{};
   g.w = static_cast<const uint8_t*>(w_packed);
   g.panel_bytes = panel_bytes(K);
@@ -281,10 +287,11 @@ static int gemm_common(int fmt, const char* fn, const void* w_packed, float gsca
   g.out = out;
   g.out_dtype = out_dtype;
   g.argmax = argmax;
-  g.counter = argmax ? static_cast<unsigned*>(ws) : nullptr;
-  g.keys = argmax ? reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + 16) : nullptr;
+  g.counter = argmax ? reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsArgmaxCounter) : nullptr;
+  g.keys = argmax ? reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + kWsArgmaxKeys) : nullptr;
   const GemmCfg cfg = choose_gemm_cfg(fmt, M, K, N);
-  if (int e = launch_gemm(fmt, g, cfg, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
+  if (int e = launch_gemm(fmt, g, cfg, ws, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
   return ok();
 }
 
@@ -295,8 +302,8 @@ int qgemm_nvfp4(const void* w_packed, float global_scale, const void* a, int M, 
 }
 
 int qgemm_affine4(const void* w_packed, const void* a, int M, int64_t K, int64_t N, void* out, int out_dtype,
-                  void* stream) {
-  return gemm_common(kAffine, __func__, w_packed, 1.0f, a, M, K, N, out, out_dtype, nullptr, nullptr, 0, stream);
+                  void* ws, size_t ws_bytes, void* stream) {
+  return gemm_common(kAffine, __func__, w_packed, 1.0f, a, M, K, N, out, out_dtype, nullptr, ws, ws_bytes, stream);
 }
 
 int q4_dequant_nvfp4(const void* w_packed, float global_scale, int64_t N, int64_t K, float* out, void* stream) {
@@ -324,17 +331,11 @@ int q4_dequant_affine4(const void* w_packed, int64_t N, int64_t K, float* out, v
 
 // ---- router --------------------------------------------------------------
 
-static int route_blocks(int D) {
-  // workgroups splitting D: about 64 rows of W_r each, at most 64 partial sums
-  int nb = (D + 63) / 64;
-  if (nb > 64) nb = 64;
-  if (nb < 1) nb = 1;
-  return nb;
-}
+static int route_blocks(int T, int D, int E) { return (D + route_rows(T, D, E) - 1) / route_rows(T, D, E); }
 
 size_t moe_route_workspace_bytes(int T, int D, int E) {
   if (T < 1 || D < 1 || E < 1) return 0;
-  return 256 + size_t(route_blocks(D)) * size_t(T) * size_t(E) * sizeof(float);
+  return kWsCounterBytes + size_t(route_blocks(T, D, E)) * size_t(T) * size_t(E) * sizeof(float);
 }
 
 int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k, int renormalize, float* logits,
@@ -349,6 +350,8 @@ int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, in
   if (E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", __func__, E);
   if (k > E || k > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d must be <= E=%d and <= 16", __func__, k, E);
   if (D % 8) return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d is not a multiple of 8", __func__, D);
+  if (route_lds_bytes(T, D, E) > 150 * 1024)
+    return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d too large for E=%d (router block exceeds LDS)", __func__, D, E);
   if ((T + 7) / 8 * 8 * E > 4096)
     return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d (rounded up to a multiple of 8) times E=%d exceeds 4096", __func__, T, E);
   REQUIRE_ALIGNED(x);
@@ -371,9 +374,9 @@ int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, in
   r.logits = logits;
   r.idx = topk_idx;
   r.w = topk_w;
-  r.counter = static_cast<unsigned*>(ws);
-  r.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
-  r.nblk = route_blocks(D);
+  r.counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsRouteCounter);
+  r.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
+  r.nblk = route_blocks(T, D, E);
   if (int e = launch_route(r, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   return ok();
 }
@@ -384,9 +387,9 @@ static size_t moe_ws_layout(const q4_moe_desc* w, int T, int k, size_t* h_off, s
   const size_t npairs = size_t(T) * size_t(k) + (w->has_shared ? size_t(T) : 0);
   const size_t hbytes = (npairs * size_t(w->F) * 2 + 255) / 256 * 256;
   const size_t obytes = (npairs * size_t(w->D) * 4 + 255) / 256 * 256;
-  *h_off = 0;
-  *o_off = hbytes;
-  return hbytes + obytes;
+  *h_off = kWsCounterBytes;
+  *o_off = kWsCounterBytes + hbytes;
+  return kWsCounterBytes + hbytes + obytes;
 }
 
 size_t moe_workspace_bytes(const q4_moe_desc* w, int T, int k) {
@@ -412,7 +415,7 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
     return fail(Q4_ERR_INVALID_ARG, "%s: bad descriptor (E=%d D=%d F=%d has_shared=%d)", __func__, w->E, w->D, w->F,
                 w->has_shared);
   if (T < 1 || T > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d outside 1..16", __func__, T);
-  if (k < 1 || k > w->E) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d outside 1..E=%d", __func__, k, w->E);
+  if (k < 1 || k > w->E || k > 64) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d outside 1..min(E=%d, 64)", __func__, k, w->E);
   if (w->D % 64 || w->F % 64)
     return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d and F=%d must be multiples of 64", __func__, w->D, w->F);
   if (w->E > 1024) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 1024", __func__, w->E);

@@ -13,6 +13,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__HIPCC__)
+#define Q4_HD __host__ __device__
+#else
+#define Q4_HD
+#endif
+
 namespace q4mi {
 
 constexpr int kTileK = 128;
@@ -22,14 +28,25 @@ constexpr int kHalfBytes = 576;
 constexpr int kHalfCodeBytes = 512;
 
 // K padded to the 64-k granularity of the packed layout
-inline int64_t padded_k(int64_t K) { return (K + 63) / 64 * 64; }
-inline int64_t full_tiles(int64_t K) { return padded_k(K) / kTileK; }
-inline bool has_half_tile(int64_t K) { return padded_k(K) % kTileK != 0; }
-inline int64_t panel_bytes(int64_t K) {
+Q4_HD inline int64_t padded_k(int64_t K) { return (K + 63) / 64 * 64; }
+Q4_HD inline int64_t full_tiles(int64_t K) { return padded_k(K) / kTileK; }
+Q4_HD inline bool has_half_tile(int64_t K) { return padded_k(K) % kTileK != 0; }
+Q4_HD inline int64_t panel_bytes(int64_t K) {
   return full_tiles(K) * kTileBytes + (has_half_tile(K) ? kHalfBytes : 0);
 }
 
 enum Fmt { kNvfp4 = 0, kAffine = 1 };
+
+// Workspace layout shared by every entry point, so that one zero-filled
+// buffer can serve all of them: the first kWsCounterBytes hold only counters
+// and keys that each call returns to zero; scratch (partial sums, h, o)
+// starts at kWsCounterBytes.
+constexpr size_t kWsCounterBytes = 32768;
+constexpr size_t kWsRouteCounter = 0;        // u32: router arrival counter
+constexpr size_t kWsArgmaxCounter = 64;      // u32: GEMM argmax completion counter
+constexpr size_t kWsArgmaxKeys = 128;        // u64[16]: GEMM argmax keys
+constexpr size_t kWsBlockCounters = 1024;    // u32[]: GEMM split-K arrival counters
+constexpr int kMaxSplitBlocks = static_cast<int>((kWsCounterBytes - kWsBlockCounters) / 4);
 
 struct GemmArgs {
   const uint8_t* w;          // packed weights
@@ -48,16 +65,37 @@ struct GemmArgs {
 };
 
 struct GemmCfg {
-  int P;   // panels per wave
-  int KW;  // waves splitting K inside a workgroup
-  int PW;  // independent panel groups (waves) per workgroup
+  int P;   // panels per wave group
+  int W;   // waves per workgroup
+  int D;   // tiles of weight loads in flight per wave
+  int KS;  // k-ranges (workgroups sharing a panel block; partials reduced in order)
+  int KW;  // waves splitting a workgroup's k-range (LDS reduction, one group per wave)
+  int PB;  // panels per workgroup block
 };
 
 // kernel launchers (q4mi_gemm.hip); return hipError_t as int
-int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* stream);
 GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N);
+size_t gemm_workspace(int fmt, int M, int64_t K, int64_t N);
+int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* stream);
 int launch_dequant(int fmt, const uint8_t* w, int64_t panel_bytes, int64_t N, int64_t K, float g,
                    float* out, void* stream);
+
+// Router split of D over workgroups: each holds `route_rows` rows of W_r (and
+// the matching x columns) in LDS; the last of the ceil(D / rows) <= 32
+// workgroups sums their partial logits.
+constexpr int kRouteMaxBlocks = 32;
+Q4_HD inline int route_rows(int T, int D, int E) {
+  int rows = 24576 / (E + T);  // (E + T) floats of LDS per row, 96 KiB in all
+  const int need = (D + kRouteMaxBlocks - 1) / kRouteMaxBlocks;
+  rows = rows < need ? need : rows;
+  return rows < D ? rows : D;
+}
+Q4_HD inline size_t route_lds_bytes(int T, int D, int E) {
+  const size_t rows = static_cast<size_t>(route_rows(T, D, E));
+  const size_t stage = rows * E * 4 + static_cast<size_t>(T) * rows * 4;
+  const size_t fin = static_cast<size_t>(T) * E * 4;
+  return stage > fin ? stage : fin;
+}
 
 struct RouteArgs {
   const uint16_t* x;    // f16 [T][D]

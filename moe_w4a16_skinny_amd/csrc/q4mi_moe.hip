@@ -34,83 +34,96 @@ using namespace dev;
 // ------------------------------------------------------------------ router
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteChunk = 64;   // rows of W_r staged per pass
-constexpr int kRouteTG = 8;       // tokens per thread item
-
+constexpr int kRouteTG = 8;         // tokens per thread item
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
+  extern __shared__ float rsm[];  // [rows][E] of W_r, then [T][rows] of x
   const int T = r.T, D = r.D, E = r.E;
   const int tid = threadIdx.x;
-  const int rows = (D + r.nblk - 1) / r.nblk;
+  const int rows = route_rows(T, D, E);
   const int d0 = blockIdx.x * rows;
-  const int d1 = min(D, d0 + rows);
+  const int cn = min(D, d0 + rows) - d0;
+  float* wrs = rsm;
+  float* xs = rsm + static_cast<size_t>(rows) * E;
   const int ntg = (T + kRouteTG - 1) / kRouteTG;
   const int nitems = E * ntg;
 
-  __shared__ float xs[64][kRouteChunk];  // [token][row in chunk]
-  float acc[2][kRouteTG];                // 2 items per thread: host limits roundup(T, 8) * E to 4096
+  // stage the block: loads issued 8 at a time per thread, coalesced along E and D
+  {
+    const int nw = cn * E;
+    for (int q0 = tid; q0 < nw; q0 += kRouteThreads * 8) {
+      float v[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u * kRouteThreads;
+        v[u] = q < nw ? r.wr[static_cast<size_t>(d0) * E + q] : 0.f;
+      }
 #pragma unroll
-    for (int t = 0; t < kRouteTG; ++t) acc[i][t] = 0.f;
-
-  for (int c0 = d0; c0 < d1; c0 += kRouteChunk) {
-    const int cn = min(kRouteChunk, d1 - c0);
-    __syncthreads();
-    for (int q = tid; q < T * kRouteChunk; q += kRouteThreads) {
-      const int t = q / kRouteChunk, dd = q % kRouteChunk;
-      xs[t][dd] = dd < cn ? (float)reinterpret_cast<const _Float16*>(r.x)[static_cast<size_t>(t) * D + c0 + dd] : 0.f;
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u * kRouteThreads;
+        if (q < nw) wrs[q] = v[u];
+      }
     }
-    __syncthreads();
+    const int nx = T * cn;
+    for (int q0 = tid; q0 < nx; q0 += kRouteThreads * 8) {
+      float v[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int item = tid + i * kRouteThreads;
-      if (item < nitems) {
-        const int e = item % E, tg = item / E;
-        for (int dd = 0; dd < cn; ++dd) {
-          const float w = r.wr[static_cast<size_t>(c0 + dd) * E + e];
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u * kRouteThreads;
+        const int t = q / max(cn, 1), dd = q - t * cn;
+        v[u] = q < nx ? (float)reinterpret_cast<const _Float16*>(r.x)[static_cast<size_t>(t) * D + d0 + dd] : 0.f;
+      }
 #pragma unroll
-          for (int t = 0; t < kRouteTG; ++t) {
-            const int tt = tg * kRouteTG + t;
-            if (tt < T) acc[i][t] = fmaf(xs[tt][dd], w, acc[i][t]);
-          }
-        }
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u * kRouteThreads;
+        if (q < nx) xs[q] = v[u];
       }
     }
   }
-  // partial logits of this row block
+  __syncthreads();
+  for (int item = tid; item < nitems; item += kRouteThreads) {
+    const int e = item % E, tg = item / E;
+    float acc[kRouteTG];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int item = tid + i * kRouteThreads;
-    if (item < nitems) {
-      const int e = item % E, tg = item / E;
+    for (int t = 0; t < kRouteTG; ++t) acc[t] = 0.f;
+    for (int dd = 0; dd < cn; ++dd) {
+      const float w = wrs[dd * E + e];
 #pragma unroll
       for (int t = 0; t < kRouteTG; ++t) {
         const int tt = tg * kRouteTG + t;
-        if (tt < T) r.partial[(static_cast<size_t>(blockIdx.x) * T + tt) * E + e] = acc[i][t];
+        if (tt < T) acc[t] = fmaf(xs[tt * cn + dd], w, acc[t]);
       }
     }
+#pragma unroll
+    for (int t = 0; t < kRouteTG; ++t) {
+      const int tt = tg * kRouteTG + t;
+      if (tt < T) r.partial[(static_cast<size_t>(blockIdx.x) * T + tt) * E + e] = acc[t];
+    }
   }
-  __threadfence();
-  __syncthreads();
+  __syncthreads();  // every wave's partial stores have reached L2
   __shared__ int s_last;
-  if (tid == 0) s_last = atomicAdd(r.counter, 1u) == gridDim.x - 1;
+  if (tid == 0) s_last = arrive(r.counter) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
-  // last workgroup: fixed-order sum of the partials, softmax, top-k
-  __shared__ float lg[4096];
+  // last workgroup: every block's partial of an item is loaded at once, then
+  // summed in block order; then softmax and top-k per token
+  float* lg = rsm;  // reuse: [T][E]
+  const int nb = gridDim.x;
   for (int q = tid; q < T * E; q += kRouteThreads) {
+    float v[kRouteMaxBlocks];
+#pragma unroll
+    for (int b = 0; b < kRouteMaxBlocks; ++b)
+      v[b] = b < nb ? load_coherent(r.partial + static_cast<size_t>(b) * T * E + q) : 0.f;
     float s = 0.f;
-    for (int b = 0; b < static_cast<int>(gridDim.x); ++b)
-      s += __builtin_nontemporal_load(r.partial + static_cast<size_t>(b) * T * E + q);
+#pragma unroll
+    for (int b = 0; b < kRouteMaxBlocks; ++b) s += v[b];
     lg[q] = s;
     if (r.logits) r.logits[q] = s;
   }
   __syncthreads();
   const int lane = tid & 63, wv = tid >> 6;
   for (int t = wv; t < T; t += kRouteThreads / 64) {
-    const float* l = lg + t * E;
+    const float* l = lg + static_cast<size_t>(t) * E;
     float v[4];
     bool taken[4];
     float mx = -INFINITY;
@@ -191,14 +204,21 @@ __device__ void group_expert(const int32_t* idx, int T, int k, int E, int e, int
     return;
   }
   int cnt = 0, below = 0;
-  const int n = T * k;
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    const int j = j0 + lane;
-    const int v = j < n ? idx[j] : -1;
-    const bool valid = v >= 0 && v < E;
-    const unsigned long long eq = __ballot(valid && v == e);
-    const unsigned long long lt = __ballot(valid && v < e);
-    if (valid && v == e) {
+  const int n = T * k;  // <= 16 * 64: at most 16 indices per lane, all loaded at once
+  int v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int j = u * 64 + lane;
+    v[u] = j < n ? idx[j] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    if (u * 64 >= n) break;
+    const int j = u * 64 + lane;
+    const bool valid = v[u] >= 0 && v[u] < E;
+    const unsigned long long eq = __ballot(valid && v[u] == e);
+    const unsigned long long lt = __ballot(valid && v[u] < e);
+    if (valid && v[u] == e) {
       const int rk = cnt + __popcll(eq & ((1ull << lane) - 1ull));
       if (rk < 16) {
         s_tok[rk] = j / k;
@@ -221,8 +241,11 @@ __device__ __forceinline__ float gelu_tanh(float u) {
 
 // ------------------------------------------------------------------ gate/up
 
-template <int KW, int PW, int DP>
-__global__ __launch_bounds__(64 * KW * PW) void moe_gate_up_kernel(MoeArgs m) {
+// Grid (panel-pair blocks, experts).  A workgroup owns PPB consecutive panel
+// pairs of its expert; wave w streams pairs w, w + W, ... (gate panel j and
+// up panel j together, P = 2) over all of K = D with D tiles in flight.
+template <int W, int DP>
+__global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int PPB) {
   const int e = blockIdx.y;
   __shared__ int s_tok[16], s_slot[16], s_meta[2];
   if (threadIdx.x < 64) group_expert(m.idx, m.T, m.k, m.E, e, s_tok, s_slot, s_meta);
@@ -232,63 +255,51 @@ __global__ __launch_bounds__(64 * KW * PW) void moe_gate_up_kernel(MoeArgs m) {
   const int base = s_meta[1];
 
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kw = wid % KW, pw = wid / KW;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = lane >> 4, c = lane & 15;
-  const int npp = m.F / 16;                       // panel pairs
-  const int jp = blockIdx.x * PW + pw;            // this wave's panel pair
-  const int jc = jp < npp ? jp : npp - 1;         // clamped for loads
-  const uint8_t* pbase[2] = {
-      m.gate + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jc) * m.gate_panel_bytes,
-      m.up + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jc) * m.gate_panel_bytes};
+  const int npp = m.F / 16;                        // panel pairs of the expert
+  const int j0 = blockIdx.x * PPB;
+  const int jend = min(npp, j0 + PPB);
+  const int ngb = jend - j0;
+  const int ng = ngb > w ? (ngb - w + W - 1) / W : 0;
+  const uint8_t* gate_e = m.gate + static_cast<size_t>(e) * m.gate_stride;
+  const uint8_t* up_e = m.up + static_cast<size_t>(e) * m.gate_stride;
   const bool arow_ok = c < me;
   const uint16_t* arow = m.x + static_cast<size_t>(arow_ok ? s_tok[c] : 0) * m.D;
-
-  const KSplit ks = ksplit(m.D);
-  const int per = (ks.nmain + KW - 1) / KW;
-  const int t0 = kw * per;
-  const int nt = max(0, min(ks.nmain, t0 + per) - t0);
-  f32x4 acc[2][2];
-  acc[0][0] = acc[0][1] = acc[1][0] = acc[1][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  wave_accumulate<kNvfp4, 2, DP>(acc, pbase, arow, arow_ok, m.D, t0, nt, kw == KW - 1 ? ks.tail : 0, ks.nmain);
-  f32x4 rg = acc[0][0] + acc[0][1], ru = acc[1][0] + acc[1][1];
-  if constexpr (KW > 1) {
-    __shared__ float red[KW][PW][2][4][64];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      red[kw][pw][0][r][lane] = rg[r];
-      red[kw][pw][1][r][lane] = ru[r];
-    }
-    __syncthreads();
-    if (kw != 0) return;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float sg = 0.f, su = 0.f;
-#pragma unroll
-      for (int j = 0; j < KW; ++j) {
-        sg += red[j][pw][0][r][lane];
-        su += red[j][pw][1][r][lane];
-      }
-      rg[r] = sg;
-      ru[r] = su;
-    }
-  }
-  if (jp >= npp) return;
+  const int nfull = static_cast<int>(full_tiles(m.D));
+  const bool half = has_half_tile(m.D);
   const float gg = m.g_gate[e], gu = m.g_up[e];
+
+  auto gbase = [&](int gi, int p) -> const uint8_t* {
+    int jp = j0 + w + gi * W;
+    jp = jp < npp ? jp : npp - 1;
+    return (p == 0 ? gate_e : up_e) + static_cast<size_t>(jp) * m.gate_panel_bytes;
+  };
+  auto pre = [] {};
+  auto epi = [&](int gi, f32x4 (&acc)[2][2]) {
+    const int jp = j0 + w + gi * W;
+    if (jp >= jend) return;
+    const f32x4 rg = acc[0][0] + acc[0][1], ru = acc[1][0] + acc[1][1];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * o + r;
-    if (row < me) {
-      const float h = gelu_tanh(gg * rg[r]) * (gu * ru[r]);
-      reinterpret_cast<_Float16*>(m.h)[static_cast<size_t>(base + row) * m.F + jp * 16 + c] = (_Float16)h;
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * o + r;
+      if (row < me) {
+        const float h = gelu_tanh(gg * rg[r]) * (gu * ru[r]);
+        reinterpret_cast<_Float16*>(m.h)[static_cast<size_t>(base + row) * m.F + jp * 16 + c] = (_Float16)h;
+      }
     }
-  }
+  };
+  stream_groups<kNvfp4, 2, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, nullptr, arow, arow_ok,
+                                      m.D, gbase, pre, epi);
 }
 
 // ------------------------------------------------------------------ down
 
-template <int P, int PW, int DP>
-__global__ __launch_bounds__(64 * PW) void moe_down_kernel(MoeArgs m) {
+// Grid (panel blocks, experts): PB panels of W_down (N = D) per workgroup,
+// groups of P panels per wave, K = F; the activation rows are the expert's
+// contiguous h rows.  o[pair][n] = w_pair * g_down * acc.
+template <int P, int W, int DP>
+__global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int PB) {
   const int e = blockIdx.y;
   __shared__ int s_tok[16], s_slot[16], s_meta[2];
   if (threadIdx.x < 64) group_expert(m.idx, m.T, m.k, m.E, e, s_tok, s_slot, s_meta);
@@ -298,24 +309,18 @@ __global__ __launch_bounds__(64 * PW) void moe_down_kernel(MoeArgs m) {
   const int base = s_meta[1];
 
   const int lane = threadIdx.x & 63;
-  const int pw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = lane >> 4, c = lane & 15;
   const int npan = m.D / 16;
-  const int panel0 = (blockIdx.x * PW + pw) * P;
-  const uint8_t* pbase[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int pi = min(panel0 + p, npan - 1);
-    pbase[p] = m.down + static_cast<size_t>(e) * m.down_stride + static_cast<size_t>(pi) * m.down_panel_bytes;
-  }
+  const int p0 = blockIdx.x * PB;
+  const int pend = min(npan, p0 + PB);
+  const int ngb = (pend - p0 + P - 1) / P;
+  const int ng = ngb > w ? (ngb - w + W - 1) / W : 0;
+  const uint8_t* down_e = m.down + static_cast<size_t>(e) * m.down_stride;
   const bool arow_ok = c < me;
   const uint16_t* arow = m.h + static_cast<size_t>(base + (arow_ok ? c : 0)) * m.F;
-  const KSplit ks = ksplit(m.F);
-  f32x4 acc[P][2];
-#pragma unroll
-  for (int p = 0; p < P; ++p) acc[p][0] = acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  wave_accumulate<kNvfp4, P, DP>(acc, pbase, arow, arow_ok, m.F, 0, ks.nmain, ks.tail, ks.nmain);
-
+  const int nfull = static_cast<int>(full_tiles(m.F));
+  const bool half = has_half_tile(m.F);
   const float gd = m.g_down[e];
   float wrow[4];
 #pragma unroll
@@ -324,33 +329,50 @@ __global__ __launch_bounds__(64 * PW) void moe_down_kernel(MoeArgs m) {
     wrow[r] = 0.f;
     if (row < me) wrow[r] = s_slot[row] < 0 ? 1.0f : m.tw[s_tok[row] * m.k + s_slot[row]];
   }
+
+  auto gbase = [&](int gi, int p) -> const uint8_t* {
+    int pi = p0 + (w + gi * W) * P + p;
+    pi = pi < npan ? pi : npan - 1;
+    return down_e + static_cast<size_t>(pi) * m.down_panel_bytes;
+  };
+  auto pre = [] {};
+  auto epi = [&](int gi, f32x4 (&acc)[P][2]) {
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int pi = panel0 + p;
-    if (pi >= npan) continue;
-    const f32x4 v = acc[p][0] + acc[p][1];
+    for (int p = 0; p < P; ++p) {
+      const int pi = p0 + (w + gi * W) * P + p;
+      if (pi >= pend) continue;
+      const f32x4 v = acc[p][0] + acc[p][1];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * o + r;
-      if (row < me) m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wrow[r] * (gd * v[r]);
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * o + r;
+        if (row < me) m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wrow[r] * (gd * v[r]);
+      }
     }
-  }
+  };
+  stream_groups<kNvfp4, P, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, nullptr, arow, arow_ok,
+                                      m.F, gbase, pre, epi);
 }
 
 // ------------------------------------------------------------------ combine
 
+// y[t][n] = sum_{s<k} o[pos(t, s)][n] (+ o[T k + t][n] for the shared expert),
+// slots in order.  pos(t, s) = (valid pairs routed to lower experts) + (rank of
+// the pair among its expert's pairs), the row gate_up/down used for it.
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
   const int t = blockIdx.x;
   const int n = blockIdx.y * 256 + threadIdx.x;
-  extern __shared__ int s_pos[];  // [k]
+  __shared__ int s_idx[16 * 64];
+  __shared__ int s_pos[64];
   const int nall = m.T * m.k;
+  for (int j = threadIdx.x; j < nall; j += 256) s_idx[j] = m.idx[j];
+  __syncthreads();
   for (int s = threadIdx.x; s < m.k; s += 256) {
-    const int e = m.idx[t * m.k + s];
+    const int e = s_idx[t * m.k + s];
     int pos = -1;
     if (e >= 0 && e < m.E) {
       int below = 0, rank = 0;
       for (int j = 0; j < nall; ++j) {
-        const int v = m.idx[j];
+        const int v = s_idx[j];
         if (v >= 0 && v < m.E) {
           below += v < e;
           rank += (v == e) && (j < t * m.k + s);
@@ -363,9 +385,16 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
   __syncthreads();
   if (n >= m.D) return;
   float acc = 0.f;
-  for (int s = 0; s < m.k; ++s) {
-    const int pos = s_pos[s];
-    if (pos >= 0) acc += m.o[static_cast<size_t>(pos) * m.D + n];
+  for (int s0 = 0; s0 < m.k; s0 += 16) {  // 16 slots' rows in flight, summed in slot order
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int s = s0 + u;
+      const int pos = s < m.k ? s_pos[s] : -1;
+      v[u] = pos >= 0 ? m.o[static_cast<size_t>(pos) * m.D + n] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += v[u];
   }
   if (m.has_shared) acc += m.o[static_cast<size_t>(nall + t) * m.D + n];
   if (m.out_dtype == Q4_F32)
@@ -378,23 +407,36 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
 
 int launch_route(const RouteArgs& r, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(route_kernel, dim3(r.nblk), dim3(kRouteThreads), 0, s, r);
+  const size_t need = route_lds_bytes(r.T, r.D, r.E);
+  static size_t lds_allowed = 48 * 1024;
+  if (need > lds_allowed) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(need));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return static_cast<int>(e);
+    }
+    lds_allowed = need;
+  }
+  hipLaunchKernelGGL(route_kernel, dim3(r.nblk), dim3(kRouteThreads), need, s, r);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_moe(const MoeArgs& m, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nexp = m.E + m.has_shared;
-  constexpr int GU_KW = 2, GU_PW = 2, DN_P = 2, DN_PW = 4;
+  constexpr int GU_W = 4, DN_P = 2, DN_W = 4;
   const int npp = m.F / 16;
-  hipLaunchKernelGGL((moe_gate_up_kernel<GU_KW, GU_PW, 4>), dim3((npp + GU_PW - 1) / GU_PW, nexp),
-                     dim3(64 * GU_KW * GU_PW), 0, s, m);
+  const int ppb = 2 * GU_W;  // panel pairs per gate/up workgroup: 2 per wave
+  hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4>), dim3((npp + ppb - 1) / ppb, nexp), dim3(64 * GU_W), 0, s, m,
+                     ppb);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
   const int npan = m.D / 16;
-  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_PW, 4>), dim3((npan + DN_P * DN_PW - 1) / (DN_P * DN_PW), nexp),
-                     dim3(64 * DN_PW), 0, s, m);
+  const int pb = 2 * DN_P * DN_W;  // panels per down workgroup: 2 groups per wave
+  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3((npan + pb - 1) / pb, nexp), dim3(64 * DN_W), 0, s, m,
+                     pb);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(m.T, (m.D + 255) / 256), dim3(256), m.k * sizeof(int), s, m);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(m.T, (m.D + 255) / 256), dim3(256), 0, s, m);
   return static_cast<int>(hipGetLastError());
 }
 

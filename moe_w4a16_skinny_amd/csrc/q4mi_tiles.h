@@ -70,12 +70,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
 
-template <int FMT, int P>
-struct Stage {
-  u32x4 a[4];
-  u32x4 c[P];
-  typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type s[P];
-};
 
 // fp32 -> output element
 __device__ __forceinline__ float store_out(void* out, int dtype, size_t off, float v) {
@@ -91,6 +85,20 @@ __device__ __forceinline__ float store_out(void* out, int dtype, size_t off, flo
     static_cast<__bf16*>(out)[off] = h;
     return (float)h;
   }
+}
+
+// Cross-workgroup handoff without cache-wide invalidation: the producer's
+// stores reach the coherence point through one agent-scope release fence
+// (issued by one thread after a workgroup barrier has drained every wave's
+// stores to L2), then an arrival counter is bumped; the consumer reads the
+// published data with agent-scope loads, which bypass stale L2 lines, so no
+// acquire fence (L2 invalidation) is needed.
+__device__ __forceinline__ unsigned arrive(unsigned* counter) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ordered 64-bit key: larger value first, then lower index; 0 = "no value"
@@ -115,124 +123,172 @@ __device__ __forceinline__ unsigned long long max_key_16(unsigned long long k) {
 }
 
 
-// Accumulate one wave's share of y = a . W^T over packed tiles [t0, t0 + nt)
-// of P panels (base pointers pbase), then optionally the tail tile `tt`
-// (tail 1: half tile, 2: full tile crossing K), whose activation loads are
-// bounded by K.  The lane's activation row is `arow` (nullptr-safe: rows the
-// lane does not own pass arow_ok = false and read zeros).  D tiles of loads
-// stay in flight ahead of the math.
-template <int FMT, int P, int D>
-__device__ __forceinline__ void wave_accumulate(f32x4 (&acc)[P][2], const uint8_t* const (&pbase)[P],
-                                                const uint16_t* arow, bool arow_ok, int K, int t0, int nt,
-                                                int tail, int tt) {
-  const int lane = threadIdx.x & 63;
-  const int o = lane >> 4;
-  const int c = lane & 15;
-
-  auto load = [&](Stage<FMT, P>& st, int t) {
-    const int kb = t * kTileK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      st.a[i] = arow_ok ? *reinterpret_cast<const u32x4*>(arow + kb + 32 * i + 8 * o) : u32x4{0u, 0u, 0u, 0u};
+// One MFMA tile step: P panels of codes/scales in `c`/`s`, activation
+// operands a[0..3] (the four 32-k steps of the tile).
+template <int FMT, int P>
+__device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4], const u32x4 (&c)[P],
+                                          const typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type (&s)[P]) {
+  if constexpr (FMT == kNvfp4) {
+    f16x2 sv[P][2];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const uint8_t* tb = pbase[p] + static_cast<size_t>(t) * kTileBytes;
-      st.c[p] = ld_nt16(tb + lane * 16);
-      if constexpr (FMT == kNvfp4)
-        st.s[p] = ld_nt4(tb + kTileCodeBytes + (c * 2 + (lane >> 5)) * 4);
-      else
-        st.s[p] = ld_nt8(tb + kTileCodeBytes + c * 8);
+      sv[p][0] = e4m3_pair(s[p], false);
+      sv[p][1] = e4m3_pair(s[p], true);
     }
-  };
-
-  auto compute = [&](const Stage<FMT, P>& st) {
-    if constexpr (FMT == kNvfp4) {
-      f16x2 sv[P][2];
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        sv[p][0] = e4m3_pair(st.s[p], false);
-        sv[p][1] = e4m3_pair(st.s[p], true);
-      }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int p = 0; p < P; ++p)
+        acc[p][i & 1] = mfma_f16(a[i], nvfp4_operand(c[p][i], sv[p][i >> 1][i & 1]), acc[p][i & 1]);
+  } else {
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 as0 = mfma_bf16(a[0], ones, z);
+    as0 = mfma_bf16(a[1], ones, as0);
+    f32x4 as1 = mfma_bf16(a[2], ones, z);
+    as1 = mfma_bf16(a[3], ones, as1);
 #pragma unroll
-        for (int p = 0; p < P; ++p)
-          acc[p][i & 1] = mfma_f16(st.a[i], nvfp4_operand(st.c[p][i], sv[p][i >> 1][i & 1]), acc[p][i & 1]);
-    } else {
-      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 as0 = mfma_bf16(st.a[0], ones, z);
-      as0 = mfma_bf16(st.a[1], ones, as0);
-      f32x4 as1 = mfma_bf16(st.a[2], ones, z);
-      as1 = mfma_bf16(st.a[3], ones, as1);
+    for (int p = 0; p < P; ++p) {
+      f32x4 q0 = mfma_bf16(a[0], affine_operand(c[p][0]), z);
+      q0 = mfma_bf16(a[1], affine_operand(c[p][1]), q0);
+      f32x4 q1 = mfma_bf16(a[2], affine_operand(c[p][2]), z);
+      q1 = mfma_bf16(a[3], affine_operand(c[p][3]), q1);
+      const float s0 = bf16_lo(s[p].x), b0 = bf16_hi(s[p].x);
+      const float s1 = bf16_lo(s[p].y), b1 = bf16_hi(s[p].y);
+      const float c0 = fmaf(-128.0f, s0, b0), c1 = fmaf(-128.0f, s1, b1);
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        f32x4 q0 = mfma_bf16(st.a[0], affine_operand(st.c[p][0]), z);
-        q0 = mfma_bf16(st.a[1], affine_operand(st.c[p][1]), q0);
-        f32x4 q1 = mfma_bf16(st.a[2], affine_operand(st.c[p][2]), z);
-        q1 = mfma_bf16(st.a[3], affine_operand(st.c[p][3]), q1);
-        const float s0 = bf16_lo(st.s[p].x), b0 = bf16_hi(st.s[p].x);
-        const float s1 = bf16_lo(st.s[p].y), b1 = bf16_hi(st.s[p].y);
-        const float c0 = fmaf(-128.0f, s0, b0), c1 = fmaf(-128.0f, s1, b1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = acc[p][0][r];
-          v = fmaf(s0, q0[r], v);
-          v = fmaf(c0, as0[r], v);
-          v = fmaf(s1, q1[r], v);
-          v = fmaf(c1, as1[r], v);
-          acc[p][0][r] = v;
-        }
-      }
-    }
-  };
-
-  {
-    Stage<FMT, P> st[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (d < nt) load(st[d], t0 + d);
-    for (int base = 0; base < nt; base += D) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const int t = base + d;
-        if (t < nt) {
-          compute(st[d]);
-          if (t + D < nt) load(st[d], t0 + t + D);
-        }
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[p][0][r];
+        v = fmaf(s0, q0[r], v);
+        v = fmaf(c0, as0[r], v);
+        v = fmaf(s1, q1[r], v);
+        v = fmaf(c1, as1[r], v);
+        acc[p][0][r] = v;
       }
     }
   }
+}
 
-  if (tail != 0) {
-    const int kb = tt * kTileK;
-    const int steps = tail == 1 ? 2 : 4;
-    Stage<FMT, P> st;
+// Where a wave's activation operands come from.
+//  * ALDS: the workgroup staged the k-range in LDS as [tile][step i][octet o]
+//    [row c] 16-byte blocks (rows >= M and k >= K zero), so that lane l of
+//    step i of local tile t reads block (t * 4 + i) * 64 + l: one
+//    conflict-free ds_read_b128 per step.
+//  * global: lane reads a[row][k0 .. k0 + 8) from its row pointer, zeros for
+//    rows it does not own or k0 >= K (the only bound check of the loop).
+template <int FMT, int P, bool ALDS>
+struct StreamStage {
+  u32x4 c[P];
+  typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type s[P];
+  u32x4 a[ALDS ? 1 : 4];
+};
+
+// Stage the activation k-range [kt0, kt0 + nt) tiles of rows 0..M-1 into LDS
+// in the ALDS layout (whole workgroup; caller synchronizes).  a is [M][K].
+__device__ __forceinline__ void stage_a_lds(u32x4* alds, const uint16_t* a, int M, int K, int kt0, int nt) {
+  const int nblk = nt * 16;  // 16-byte blocks per row in the range
+  for (int q = threadIdx.x; q < 16 * nblk; q += blockDim.x) {
+    const int c = q / nblk, b = q - c * nblk;         // row, block along k (8 k each)
+    const int t = b >> 4, i = (b >> 2) & 3, o = b & 3;
+    const int k0 = (kt0 + t) * kTileK + 32 * i + 8 * o;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < M && k0 < K) v = *reinterpret_cast<const u32x4*>(a + static_cast<size_t>(c) * K + k0);
+    alds[(t * 4 + i) * 64 + o * 16 + c] = v;
+  }
+}
+
+// Stream ng groups of P panels over the tiles [kt0, kt0 + KRg) of each group
+// (global packed tile indices; tile `half_t` is the 576-byte half tile, -1 if
+// none), keeping D tiles of weight loads in flight across group boundaries.
+// gbase(g, p): packed base of panel p of the wave's g-th group.  After the
+// last tile of group g, epi(g, acc) consumes the accumulators, which restart
+// at zero.  pre() runs once after the first loads are issued (the workgroup
+// stages its activations there, so that the LDS fill overlaps the first HBM
+// round trip; every wave must reach it).  All arguments except the
+// lane-dependent A row are wave-uniform.
+template <int FMT, int P, int D, bool ALDS, class GBase, class Pre, class Epi>
+__device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, const u32x4* alds,
+                                              const uint16_t* arow, bool arow_ok, int K, GBase gbase, Pre pre,
+                                              Epi epi) {
+  const int lane = threadIdx.x & 63;
+  const int o = lane >> 4;
+  const int c = lane & 15;
+  const int F = ng * KRg;
+  using St = StreamStage<FMT, P, ALDS>;
+
+  auto load = [&](St& st, int g, int t) {
+    const int tg = kt0 + t;
+    const bool half = tg == half_t;
+    if constexpr (!ALDS) {
+      const int kb = tg * kTileK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k0 = kb + 32 * i + 8 * o;
-      st.a[i] = (arow_ok && i < steps && k0 < K) ? *reinterpret_cast<const u32x4*>(arow + k0)
-                                                : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 4; ++i) {
+        const int k0 = kb + 32 * i + 8 * o;
+        st.a[i] = (arow_ok && k0 < K) ? *reinterpret_cast<const u32x4*>(arow + k0) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const uint8_t* tb = pbase[p] + static_cast<size_t>(tt) * kTileBytes;
-      if (steps == 2) {
-        const u32x2 cc = ld_nt8(tb + lane * 8);
-        st.c[p] = u32x4{cc.x, cc.y, 0u, 0u};
-        if constexpr (FMT == kNvfp4)
-          st.s[p] = ld_nt2(tb + kHalfCodeBytes + (c * 2 + (lane >> 5)) * 2);
-        else
-          st.s[p] = u32x2{ld_nt4(tb + kHalfCodeBytes + c * 4), 0u};  // 2nd group: s = b = 0 adds 0
-      } else {
+      const uint8_t* tb = gbase(g, p) + static_cast<size_t>(tg) * kTileBytes;
+      if (!half) {
         st.c[p] = ld_nt16(tb + lane * 16);
         if constexpr (FMT == kNvfp4)
           st.s[p] = ld_nt4(tb + kTileCodeBytes + (c * 2 + (lane >> 5)) * 4);
         else
           st.s[p] = ld_nt8(tb + kTileCodeBytes + c * 8);
+      } else {
+        const u32x2 cc = ld_nt8(tb + lane * 8);
+        st.c[p] = u32x4{cc.x, cc.y, 0u, 0u};
+        if constexpr (FMT == kNvfp4)
+          st.s[p] = ld_nt2(tb + kHalfCodeBytes + (c * 2 + (lane >> 5)) * 2);
+        else
+          st.s[p] = u32x2{ld_nt4(tb + kHalfCodeBytes + c * 4), 0u};  // 2nd group s = b = 0 adds 0
       }
     }
-    compute(st);  // zero operands make the missing steps contribute exactly 0
+  };
+
+  f32x4 acc[P][2];
+#pragma unroll
+  for (int p = 0; p < P; ++p) acc[p][0] = acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  St st[D];
+  // load cursor (group, tile) and compute cursor
+  int lg = 0, lt = 0;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (d < F) {
+      load(st[d], lg, lt);
+      if (++lt == KRg) { lt = 0; ++lg; }
+    }
+  }
+  pre();
+  int cg = 0, ct = 0;
+  for (int f0 = 0; f0 < F; f0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (f0 + d < F) {
+        u32x4 a[4];
+        if constexpr (ALDS) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = alds[(ct * 4 + i) * 64 + lane];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = st[d].a[i];
+        }
+        tile_math<FMT, P>(acc, a, st[d].c, st[d].s);
+        if (f0 + d + D < F) {
+          load(st[d], lg, lt);
+          if (++lt == KRg) { lt = 0; ++lg; }
+        }
+        if (++ct == KRg) {
+          epi(cg, acc);
+#pragma unroll
+          for (int p = 0; p < P; ++p) acc[p][0] = acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ct = 0;
+          ++cg;
+        }
+      }
+    }
   }
 }
 

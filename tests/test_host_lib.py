@@ -123,12 +123,17 @@ def test_gemm_refusals_without_gpu():
         (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, 9, None, None, 0, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
         (lambda: lib.qgemm_nvfp4(mis, 1.0, p, 1, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_ALIGNMENT, "w_packed"),
         (lambda: lib.qgemm_nvfp4(p, 1.0, mis, 1, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_ALIGNMENT, "a is"),
-        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, q4.Q4_F32, p, None, 0, None), q4.Q4_ERR_WORKSPACE, "ws"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, q4.Q4_F32, p, None, 0, None), q4.Q4_ERR_WORKSPACE, "ws is NULL"),
         (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, q4.Q4_F32, p, p, 8, None), q4.Q4_ERR_WORKSPACE, "ws_bytes"),
-        (lambda: lib.qgemm_affine4(p, p, 1, 96, 16, p, q4.Q4_F32, None), q4.Q4_ERR_UNSUPPORTED, "K=96"),
-        (lambda: lib.qgemm_affine4(p, p, 1, 128, 16, p, q4.Q4_F16, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
+        (lambda: lib.qgemm_affine4(p, p, 1, 96, 16, p, q4.Q4_F32, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "K=96"),
+        (lambda: lib.qgemm_affine4(p, p, 1, 128, 16, p, q4.Q4_F16, None, 0, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
+        (lambda: lib.qgemm_affine4(p, p, 16, 5120, 15360, p, q4.Q4_F32, None, 0, None), q4.Q4_ERR_WORKSPACE, "ws is NULL"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 16, 4096, 8192, p, q4.Q4_F16, p, p, 64, None), q4.Q4_ERR_WORKSPACE, "ws_bytes"),
         (lambda: lib.q4_dequant_nvfp4(p, 1.0, 15, 64, p, None), q4.Q4_ERR_UNSUPPORTED, "N=15"),
     ]
+    # these shapes must need a workspace, or the refusal cases above would launch
+    assert lib.qgemm_affine4_workspace_bytes(16, 5120, 15360) > 0
+    assert lib.qgemm_nvfp4_workspace_bytes(16, 4096, 8192, 1) > 64
     for call, code, needle in cases:
         assert call() == code, needle
         assert needle in _err(code), (needle, _err(code))
@@ -157,6 +162,7 @@ def test_router_and_moe_refusals_without_gpu():
     mcases = [
         (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 17, 8, p, q4.Q4_F32, p, need, None), q4.Q4_ERR_UNSUPPORTED, "T=17"),
         (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 16, 129, p, q4.Q4_F32, p, need, None), q4.Q4_ERR_UNSUPPORTED, "k=129"),
+        (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 16, 65, p, q4.Q4_F32, p, need, None), q4.Q4_ERR_UNSUPPORTED, "k=65"),
         (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 16, 8, p, q4.Q4_BF16, p, need, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
         (lambda: lib.moe_grouped_qgemm(C.byref(d), p, p, p, 16, 8, p, q4.Q4_F32, p, need - 1, None), q4.Q4_ERR_WORKSPACE, "ws_bytes"),
         (lambda: lib.moe_grouped_qgemm(None, p, p, p, 16, 8, p, q4.Q4_F32, p, need, None), q4.Q4_ERR_INVALID_ARG, "w is NULL"),
