@@ -48,6 +48,7 @@ struct KP2 {
   int half_t;      // packed index of the half tile, -1 if none
   int KS, KR;      // k-splits and tiles per split
   int KW;          // waves splitting a workgroup's k-range (one group per wave if > 1)
+  int NGW;         // result slots (panel groups) per wave in LDS
   int PB;          // panels per workgroup block
   int nblocks;     // panel blocks
   float* partial;  // [KS][M][N] fp32 (KS > 1)
@@ -58,10 +59,10 @@ constexpr int kMaxKS = 8;  // partial sums summed per output by the last workgro
 
 template <int FMT, int P, int W, int D>
 __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
+  // dynamic LDS: [KR tiles of activations][W waves x NGW groups x P panels of results]
   extern __shared__ u32x4 alds[];
   __shared__ unsigned long long sbest[16];
   __shared__ int s_last;
-  __shared__ float red[W][P][4][64];  // intra-workgroup k-split partials (KW > 1)
   const GemmArgs& g = kp.g;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -81,11 +82,35 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
   const int pend = min(kp.npanels, p0 + kp.PB);
   const int ngb = (pend - p0 + P - 1) / P;                 // panel groups in the block
   const int ng = ngb > pw ? (ngb - pw + PWv - 1) / PWv : 0; // this wave's: pw, pw + PWv, ...
+  const int NGW = kp.NGW;                                  // result slots per wave
+  f32x4* const rbase = reinterpret_cast<f32x4*>(alds + static_cast<size_t>(kp.KR) * 4 * 64);  // results
+  f32x4* wout = rbase + static_cast<size_t>(w) * NGW * P * 64;
   const int M = g.M;
   const float gs = g.gscale;
 
   if (threadIdx.x < 16) sbest[threadIdx.x] = 0ull;
   unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+
+  auto gbase = [&](int gi, int p) -> const uint8_t* {
+    int panel = p0 + (pw + gi * PWv) * P + p;
+    panel = panel < kp.npanels ? panel : kp.npanels - 1;   // in-bounds load, store skipped
+    return g.w + static_cast<size_t>(panel) * static_cast<size_t>(g.panel_bytes);
+  };
+  StageRegs stg;
+  auto pre_issue = [&]() { stage_issue(stg, g.a, M, g.K, kt0, KRg); };
+  auto pre = [&]() {
+    stage_finish(stg, alds, g.a, M, g.K, kt0, KRg);
+    __syncthreads();
+  };
+  auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash<P>(wout, gi, acc); };
+  auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
+  stream_groups<FMT, P, D, true>(ng, wtn, kt0 + wt0, kp.half_t, alds + static_cast<size_t>(wt0) * 4 * 64, nullptr,
+                                 false, g.K, gbase, pre_issue, pre, epi, epi_add);
+  if (wtn == 0) {  // a k-split wave without tiles still owns zero partials
+    for (int gi = 0; gi < ng; ++gi)
+#pragma unroll
+      for (int p = 0; p < P; ++p) wout[(gi * P + p) * 64 + lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // final value of output (m, n) -> stored, argmax key kept
   auto finish = [&](int r, int m, int n, float v) {
@@ -93,66 +118,25 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
     const unsigned long long key = argmax_key(y, n);
     best[r] = key > best[r] ? key : best[r];
   };
-  auto gbase = [&](int gi, int p) -> const uint8_t* {
-    int panel = p0 + (pw + gi * PWv) * P + p;
-    panel = panel < kp.npanels ? panel : kp.npanels - 1;   // in-bounds load, store skipped
-    return g.w + static_cast<size_t>(panel) * static_cast<size_t>(g.panel_bytes);
-  };
-  auto pre = [&]() {
-    stage_a_lds(alds, g.a, M, g.K, kt0, KRg);
-    __syncthreads();
-  };
-  f32x4 keep[P];  // KW > 1: this wave's single group, reduced after the stream
-#pragma unroll
-  for (int p = 0; p < P; ++p) keep[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto epi = [&](int gi, f32x4 (&acc)[P][2]) {
-    if (KW > 1) {
-#pragma unroll
-      for (int p = 0; p < P; ++p) keep[p] = acc[p][0] + acc[p][1];
-      return;
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int panel = p0 + (pw + gi * PWv) * P + p;
-      if (panel >= pend) continue;
-      const int n = panel * 16 + c;
-      const f32x4 v = acc[p][0] + acc[p][1];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * o + r;
-        if (m >= M) continue;
-        if (KS == 1)
-          finish(r, m, n, v[r]);
-        else
-          kp.partial[(static_cast<size_t>(ks) * M + m) * g.N + n] = v[r];
-      }
-    }
-  };
-  stream_groups<FMT, P, D, true>(ng, wtn, kt0 + wt0, kp.half_t, alds + static_cast<size_t>(wt0) * 4 * 64, nullptr,
-                                 false, g.K, gbase, pre, epi);
-
-  if (KW > 1) {  // one group per wave: sum the KW k-slices in order
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[w][p][r][lane] = keep[p][r];
-    __syncthreads();
-    if (kw == 0 && ng > 0) {
+  // group gi of wave column pw: results of k-split waves kw' = 0..KW-1 summed in order
+  if (KW > 1) __syncthreads();
+  if (kw == 0) {
+    for (int gi = 0; gi < ng; ++gi) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        const int panel = p0 + pw * P + p;
+        const int panel = p0 + (pw + gi * PWv) * P + p;
         if (panel >= pend) continue;
+        f32x4 v = wout[(gi * P + p) * 64 + lane];
+        for (int j = 1; j < KW; ++j) v += rbase[static_cast<size_t>(pw * KW + j) * NGW * P * 64 + (gi * P + p) * 64 + lane];
         const int n = panel * 16 + c;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = 4 * o + r;
           if (m >= M) continue;
-          float v = 0.f;
-          for (int j = 0; j < KW; ++j) v += red[pw * KW + j][p][r][lane];
           if (KS == 1)
-            finish(r, m, n, v);
+            finish(r, m, n, v[r]);
           else
-            kp.partial[(static_cast<size_t>(ks) * M + m) * g.N + n] = v;
+            kp.partial[(static_cast<size_t>(ks) * M + m) * g.N + n] = v[r];
         }
       }
     }
@@ -266,7 +250,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(const uint8_t* __restrict__
 
 template <int FMT, int P, int W, int D>
 int launch_cfg(const KP2& kp, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(kp.KR) * 4 * 64 * sizeof(u32x4);
+  const size_t lds = (static_cast<size_t>(kp.KR) * 4 * 64 + static_cast<size_t>(W) * kp.NGW * P * 64) * sizeof(u32x4);
   static size_t lds_allowed = 48 * 1024;  // per instantiation: raise the dynamic LDS limit on demand
   if (lds > lds_allowed) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm2_kernel<FMT, P, W, D>),
@@ -358,6 +342,11 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
   kp.KW = cfg.KW;
   kp.PB = cfg.PB;
   kp.nblocks = (kp.npanels + cfg.PB - 1) / cfg.PB;
+  {
+    const int pwv = cfg.W / (cfg.KW > 0 ? cfg.KW : 1);
+    const int ngb = (cfg.PB + cfg.P - 1) / cfg.P;
+    kp.NGW = (ngb + pwv - 1) / pwv;
+  }
   if (kp.KS > kMaxKS) return static_cast<int>(hipErrorInvalidConfiguration);
   if (kp.KW < 1 || cfg.W % kp.KW != 0 || (kp.KW > 1 && kp.PB > cfg.P * (cfg.W / kp.KW)))
     return static_cast<int>(hipErrorInvalidConfiguration);
@@ -366,7 +355,7 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
     kp.bcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsBlockCounters);
     kp.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
   }
-  if (kp.KR * 4096 + static_cast<int>(sizeof(float)) * cfg.W * cfg.P * 256 > 156 * 1024)
+  if ((static_cast<size_t>(kp.KR) * 256 + static_cast<size_t>(cfg.W) * kp.NGW * cfg.P * 64) * 16 > 158 * 1024)
     return static_cast<int>(hipErrorInvalidConfiguration);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return fmt == kNvfp4 ? launch_fmt<kNvfp4>(kp, cfg, s) : launch_fmt<kAffine>(kp, cfg, s);

@@ -275,11 +275,18 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int PPB)
     jp = jp < npp ? jp : npp - 1;
     return (p == 0 ? gate_e : up_e) + static_cast<size_t>(jp) * m.gate_panel_bytes;
   };
+  extern __shared__ f32x4 gu_out[];  // [W][NGW][2 panels][64 lanes]
+  const int NGW = (PPB + W - 1) / W;
+  f32x4* wout = gu_out + static_cast<size_t>(w) * NGW * 2 * 64;
   auto pre = [] {};
-  auto epi = [&](int gi, f32x4 (&acc)[2][2]) {
+  auto epi = [&](int gi, f32x4 (&acc)[2][2]) { stash<2>(wout, gi, acc); };
+  auto epi_add = [&](int gi, f32x4 (&acc)[2][2]) { stash_add<2>(wout, gi, acc); };
+  stream_groups<kNvfp4, 2, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, nullptr, arow, arow_ok,
+                                      m.D, gbase, pre, pre, epi, epi_add);
+  for (int gi = 0; gi < ng; ++gi) {
     const int jp = j0 + w + gi * W;
-    if (jp >= jend) return;
-    const f32x4 rg = acc[0][0] + acc[0][1], ru = acc[1][0] + acc[1][1];
+    if (jp >= jend) continue;
+    const f32x4 rg = wout[(gi * 2 + 0) * 64 + lane], ru = wout[(gi * 2 + 1) * 64 + lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * o + r;
@@ -288,9 +295,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int PPB)
         reinterpret_cast<_Float16*>(m.h)[static_cast<size_t>(base + row) * m.F + jp * 16 + c] = (_Float16)h;
       }
     }
-  };
-  stream_groups<kNvfp4, 2, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, nullptr, arow, arow_ok,
-                                      m.D, gbase, pre, epi);
+  }
 }
 
 // ------------------------------------------------------------------ down
@@ -335,22 +340,27 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int PB) {
     pi = pi < npan ? pi : npan - 1;
     return down_e + static_cast<size_t>(pi) * m.down_panel_bytes;
   };
+  extern __shared__ f32x4 dn_out[];  // [W][NGW][P][64]
+  const int NGW = ((PB + P - 1) / P + W - 1) / W;
+  f32x4* wout = dn_out + static_cast<size_t>(w) * NGW * P * 64;
   auto pre = [] {};
-  auto epi = [&](int gi, f32x4 (&acc)[P][2]) {
+  auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash<P>(wout, gi, acc); };
+  auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
+  stream_groups<kNvfp4, P, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, nullptr, arow, arow_ok,
+                                      m.F, gbase, pre, pre, epi, epi_add);
+  for (int gi = 0; gi < ng; ++gi) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int pi = p0 + (w + gi * W) * P + p;
       if (pi >= pend) continue;
-      const f32x4 v = acc[p][0] + acc[p][1];
+      const f32x4 v = wout[(gi * P + p) * 64 + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * o + r;
         if (row < me) m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wrow[r] * (gd * v[r]);
       }
     }
-  };
-  stream_groups<kNvfp4, P, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, nullptr, arow, arow_ok,
-                                      m.F, gbase, pre, epi);
+  }
 }
 
 // ------------------------------------------------------------------ combine
@@ -428,13 +438,15 @@ int launch_moe(const MoeArgs& m, void* stream) {
   constexpr int GU_W = 4, DN_P = 2, DN_W = 4;
   const int npp = m.F / 16;
   const int ppb = 2 * GU_W;  // panel pairs per gate/up workgroup: 2 per wave
-  hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4>), dim3((npp + ppb - 1) / ppb, nexp), dim3(64 * GU_W), 0, s, m,
-                     ppb);
+  const size_t gu_lds = static_cast<size_t>(GU_W) * ((ppb + GU_W - 1) / GU_W) * 2 * 64 * 16;
+  hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4>), dim3((npp + ppb - 1) / ppb, nexp), dim3(64 * GU_W), gu_lds, s,
+                     m, ppb);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
   const int npan = m.D / 16;
   const int pb = 2 * DN_P * DN_W;  // panels per down workgroup: 2 groups per wave
-  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3((npan + pb - 1) / pb, nexp), dim3(64 * DN_W), 0, s, m,
-                     pb);
+  const size_t dn_lds = static_cast<size_t>(DN_W) * (((pb + DN_P - 1) / DN_P + DN_W - 1) / DN_W) * DN_P * 64 * 16;
+  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3((npan + pb - 1) / pb, nexp), dim3(64 * DN_W), dn_lds, s,
+                     m, pb);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
   hipLaunchKernelGGL(moe_combine_kernel, dim3(m.T, (m.D + 255) / 256), dim3(256), 0, s, m);
   return static_cast<int>(hipGetLastError());

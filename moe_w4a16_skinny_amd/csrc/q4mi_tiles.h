@@ -123,6 +123,19 @@ __device__ __forceinline__ unsigned long long max_key_16(unsigned long long k) {
 }
 
 
+// Park a finished group's accumulators in LDS: lane l writes its P f32x4
+// (rows 4 (l >> 4) + r of column l & 15 of each panel) to
+// wout[((g * P + p) * 64 + l)].  The streaming loop must issue no vector-
+// memory instruction other than its loads (the compiler's wait counting
+// across a loop with stores in it degenerates to waiting for everything), so
+// the epilogues write results to global memory only after the stream.
+template <int P>
+__device__ __forceinline__ void stash(f32x4* wout, int g, const f32x4 (&acc)[P][2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int p = 0; p < P; ++p) wout[(g * P + p) * 64 + lane] = acc[p][0] + acc[p][1];
+}
+
 // One MFMA tile step: P panels of codes/scales in `c`/`s`, activation
 // operands a[0..3] (the four 32-k steps of the tile).
 template <int FMT, int P>
@@ -185,40 +198,89 @@ struct StreamStage {
 
 // Stage the activation k-range [kt0, kt0 + nt) tiles of rows 0..M-1 into LDS
 // in the ALDS layout (whole workgroup; caller synchronizes).  a is [M][K].
-__device__ __forceinline__ void stage_a_lds(u32x4* alds, const uint16_t* a, int M, int K, int kt0, int nt) {
-  const int nblk = nt * 16;  // 16-byte blocks per row in the range
-  for (int q = threadIdx.x; q < 16 * nblk; q += blockDim.x) {
-    const int c = q / nblk, b = q - c * nblk;         // row, block along k (8 k each)
-    const int t = b >> 4, i = (b >> 2) & 3, o = b & 3;
-    const int k0 = (kt0 + t) * kTileK + 32 * i + 8 * o;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < M && k0 < K) v = *reinterpret_cast<const u32x4*>(a + static_cast<size_t>(c) * K + k0);
-    alds[(t * 4 + i) * 64 + o * 16 + c] = v;
+// In two halves so that the loads can be in flight together with the first
+// weight tiles: stage_issue loads this thread's first kStageB blocks into
+// registers, stage_finish writes them (and stages any remaining blocks).
+constexpr int kStageB = 16;
+struct StageRegs {
+  u32x4 v[kStageB];
+};
+// Thread q fills LDS block q (consecutive threads write consecutive 16-byte
+// blocks: no bank conflicts); block q = ((t * 4 + i) * 4 + o) * 16 + c holds
+// a[c][(kt0 + t) * 128 + 32 i + 8 o + 0..7].
+__device__ __forceinline__ void stage_block(int q, int nblk, int* dst, int* c_out, int* k0_out, int kt0) {
+  (void)nblk;
+  const int c = q & 15, o = (q >> 4) & 3, i = (q >> 6) & 3, t = q >> 8;
+  *c_out = c;
+  *k0_out = (kt0 + t) * kTileK + 32 * i + 8 * o;
+  *dst = q;
+}
+__device__ __forceinline__ void stage_issue(StageRegs& r, const uint16_t* a, int M, int K, int kt0, int nt) {
+  const int nblk = nt * 16, total = 16 * nblk;
+#pragma unroll
+  for (int u = 0; u < kStageB; ++u) {
+    const int q = threadIdx.x + u * blockDim.x;
+    int dst, c, k0;
+    stage_block(q, nblk, &dst, &c, &k0, kt0);
+    r.v[u] = (q < total && c < M && k0 < K) ? *reinterpret_cast<const u32x4*>(a + static_cast<size_t>(c) * K + k0)
+                                           : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+__device__ __forceinline__ void stage_finish(const StageRegs& r, u32x4* alds, const uint16_t* a, int M, int K,
+                                             int kt0, int nt) {
+  const int nblk = nt * 16, total = 16 * nblk;
+#pragma unroll
+  for (int u = 0; u < kStageB; ++u) {
+    const int q = threadIdx.x + u * blockDim.x;
+    int dst, c, k0;
+    stage_block(q, nblk, &dst, &c, &k0, kt0);
+    if (q < total) alds[dst] = r.v[u];
+  }
+  // blocks beyond the first kStageB per thread (large k-ranges, few threads)
+  for (int q0 = threadIdx.x + kStageB * blockDim.x; q0 < total; q0 += kStageB * blockDim.x) {
+    StageRegs t;
+#pragma unroll
+    for (int u = 0; u < kStageB; ++u) {
+      const int q = q0 + u * blockDim.x;
+      int dst, c, k0;
+      stage_block(q, nblk, &dst, &c, &k0, kt0);
+      t.v[u] = (q < total && c < M && k0 < K) ? *reinterpret_cast<const u32x4*>(a + static_cast<size_t>(c) * K + k0)
+                                             : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kStageB; ++u) {
+      const int q = q0 + u * blockDim.x;
+      int dst, c, k0;
+      stage_block(q, nblk, &dst, &c, &k0, kt0);
+      if (q < total) alds[dst] = t.v[u];
+    }
   }
 }
 
 // Stream ng groups of P panels over the tiles [kt0, kt0 + KRg) of each group
-// (global packed tile indices; tile `half_t` is the 576-byte half tile, -1 if
-// none), keeping D tiles of weight loads in flight across group boundaries.
-// gbase(g, p): packed base of panel p of the wave's g-th group.  After the
-// last tile of group g, epi(g, acc) consumes the accumulators, which restart
-// at zero.  pre() runs once after the first loads are issued (the workgroup
-// stages its activations there, so that the LDS fill overlaps the first HBM
-// round trip; every wave must reach it).  All arguments except the
-// lane-dependent A row are wave-uniform.
-template <int FMT, int P, int D, bool ALDS, class GBase, class Pre, class Epi>
+// (global packed tile indices; if half_t falls in that range it must be the
+// range's last tile, the 576-byte half tile), keeping D tiles of weight loads
+// in flight across group boundaries.  gbase(g, p): packed base of panel p of
+// the wave's g-th group.  After the last tile of group g, epi(g, acc) consumes
+// the accumulators (it must not touch global memory: see stash), which
+// restart at zero; the half tile of every group is added afterwards through
+// epi_add(g, acc).  pre_issue() runs before the first weight loads and pre()
+// after them (the workgroup stages its activations across the two, so both
+// travel in the same round trip; every wave must reach pre()).  All
+// arguments except the lane-dependent A row are wave-uniform.
+template <int FMT, int P, int D, bool ALDS, class GBase, class PreIssue, class Pre, class Epi, class EpiAdd>
 __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, const u32x4* alds,
-                                              const uint16_t* arow, bool arow_ok, int K, GBase gbase, Pre pre,
-                                              Epi epi) {
+                                              const uint16_t* arow, bool arow_ok, int K, GBase gbase,
+                                              PreIssue pre_issue, Pre pre, Epi epi, EpiAdd epi_add) {
   const int lane = threadIdx.x & 63;
   const int o = lane >> 4;
   const int c = lane & 15;
-  const int F = ng * KRg;
+  const bool has_half = half_t >= kt0 && half_t < kt0 + KRg;
+  const int KRf = has_half ? KRg - 1 : KRg;  // full tiles streamed per group
+  const int F = ng * KRf;
   using St = StreamStage<FMT, P, ALDS>;
 
-  auto load = [&](St& st, int g, int t) {
-    const int tg = kt0 + t;
-    const bool half = tg == half_t;
+  auto load_a = [&](St& st, int tg) {
     if constexpr (!ALDS) {
       const int kb = tg * kTileK;
 #pragma unroll
@@ -227,23 +289,31 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
         st.a[i] = (arow_ok && k0 < K) ? *reinterpret_cast<const u32x4*>(arow + k0) : u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+  auto load = [&](St& st, int g, int t) {
+    const int tg = kt0 + t;
+    load_a(st, tg);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint8_t* tb = gbase(g, p) + static_cast<size_t>(tg) * kTileBytes;
-      if (!half) {
-        st.c[p] = ld_nt16(tb + lane * 16);
-        if constexpr (FMT == kNvfp4)
-          st.s[p] = ld_nt4(tb + kTileCodeBytes + (c * 2 + (lane >> 5)) * 4);
-        else
-          st.s[p] = ld_nt8(tb + kTileCodeBytes + c * 8);
-      } else {
-        const u32x2 cc = ld_nt8(tb + lane * 8);
-        st.c[p] = u32x4{cc.x, cc.y, 0u, 0u};
-        if constexpr (FMT == kNvfp4)
-          st.s[p] = ld_nt2(tb + kHalfCodeBytes + (c * 2 + (lane >> 5)) * 2);
-        else
-          st.s[p] = u32x2{ld_nt4(tb + kHalfCodeBytes + c * 4), 0u};  // 2nd group s = b = 0 adds 0
-      }
+      st.c[p] = ld_nt16(tb + lane * 16);
+      if constexpr (FMT == kNvfp4)
+        st.s[p] = ld_nt4(tb + kTileCodeBytes + (c * 2 + (lane >> 5)) * 4);
+      else
+        st.s[p] = ld_nt8(tb + kTileCodeBytes + c * 8);
+    }
+  };
+  auto load_half = [&](St& st, int g) {
+    load_a(st, half_t);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint8_t* tb = gbase(g, p) + static_cast<size_t>(half_t) * kTileBytes;
+      const u32x2 cc = ld_nt8(tb + lane * 8);
+      st.c[p] = u32x4{cc.x, cc.y, 0u, 0u};
+      if constexpr (FMT == kNvfp4)
+        st.s[p] = ld_nt2(tb + kHalfCodeBytes + (c * 2 + (lane >> 5)) * 2);
+      else
+        st.s[p] = u32x2{ld_nt4(tb + kHalfCodeBytes + c * 4), 0u};  // 2nd group s = b = 0 adds 0
     }
   };
 
@@ -252,44 +322,105 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   for (int p = 0; p < P; ++p) acc[p][0] = acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   St st[D];
-  // load cursor (group, tile) and compute cursor
-  int lg = 0, lt = 0;
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (d < F) {
-      load(st[d], lg, lt);
-      if (++lt == KRg) { lt = 0; ++lg; }
+  int lg = 0, lt = 0;  // load cursor (group, tile)
+  int cg = 0, ct = 0;  // compute cursor
+  auto load_next = [&](St& x) {
+    load(x, lg, lt);
+    if (++lt == KRf) {
+      lt = 0;
+      ++lg;
     }
+  };
+  auto tile_a = [&](const St& x, int t, u32x4 (&a)[4]) {
+    if constexpr (ALDS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = alds[(t * 4 + i) * 64 + lane];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = x.a[i];
+    }
+  };
+  auto compute_next = [&](const St& x) {
+    u32x4 a[4];
+    tile_a(x, ct, a);
+    tile_math<FMT, P>(acc, a, x.c, x.s);
+    if (++ct == KRf) {
+      epi(cg, acc);
+#pragma unroll
+      for (int p = 0; p < P; ++p) acc[p][0] = acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ct = 0;
+      ++cg;
+    }
+  };
+
+  // The steady loop issues exactly D loads per D tiles of math with no
+  // condition around any load, so the compiler's wait before each tile only
+  // covers that tile's loads (D - 1 tiles stay in flight).  The drain computes
+  // the last tiles with the remaining loads issued under conditions.
+  pre_issue();
+  if (F >= D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_next(st[d]);
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < F) load_next(st[d]);
   }
   pre();
-  int cg = 0, ct = 0;
-  for (int f0 = 0; f0 < F; f0 += D) {
+  // Drain the prologue once: its first tile is needed next anyway, and
+  // entering the loop with nothing pending lets the compiler's wait before
+  // each tile of the steady loop count only the D - 1 younger tiles.
+  __builtin_amdgcn_s_waitcnt(0);
+  int f = 0;
+  for (; f + 2 * D <= F; f += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (f0 + d < F) {
-        u32x4 a[4];
-        if constexpr (ALDS) {
+      compute_next(st[d]);
+      load_next(st[d]);
+    }
+  }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = alds[(ct * 4 + i) * 64 + lane];
-        } else {
+  for (int d = 0; d < D; ++d) {
+    if (f + d < F) {
+      compute_next(st[d]);
+      if (f + d + D < F) load_next(st[d]);
+    }
+  }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = st[d].a[i];
-        }
-        tile_math<FMT, P>(acc, a, st[d].c, st[d].s);
-        if (f0 + d + D < F) {
-          load(st[d], lg, lt);
-          if (++lt == KRg) { lt = 0; ++lg; }
-        }
-        if (++ct == KRg) {
-          epi(cg, acc);
+  for (int d = 0; d < D; ++d)
+    if (f + D + d < F) compute_next(st[d]);
+  if (KRf == 0) {  // a range of only the half tile: every group still owns a result
+    for (int gg = 0; gg < ng; ++gg) epi(gg, acc);
+  }
+
+  // half tiles: loads of up to D groups in flight, then their math
+  if (has_half) {
+    for (int g0 = 0; g0 < ng; g0 += D) {
 #pragma unroll
-          for (int p = 0; p < P; ++p) acc[p][0] = acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-          ct = 0;
-          ++cg;
+      for (int d = 0; d < D; ++d)
+        if (g0 + d < ng) load_half(st[d], g0 + d);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (g0 + d < ng) {
+          f32x4 hacc[P][2];
+#pragma unroll
+          for (int p = 0; p < P; ++p) hacc[p][0] = hacc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          u32x4 a[4];
+          tile_a(st[d], KRg - 1, a);
+          tile_math<FMT, P>(hacc, a, st[d].c, st[d].s);
+          epi_add(g0 + d, hacc);
         }
       }
     }
   }
+}
+
+// Add a half tile's accumulators to a stashed group result.
+template <int P>
+__device__ __forceinline__ void stash_add(f32x4* wout, int g, const f32x4 (&acc)[P][2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int p = 0; p < P; ++p) wout[(g * P + p) * 64 + lane] += acc[p][0] + acc[p][1];
 }
 
 // Split of a K range into the checked-free tiles and an optional tail tile.
