@@ -79,7 +79,10 @@ const char* q4_last_error(void);
  * contiguous loads.  Here the order is that of the gfx950 16x16x32 MFMA B
  * operand: per 16 output rows, 128-k tiles of 1152 bytes (1 KiB of codes
  * where each lane's 16 bytes are one 16-byte load, then the tile's scales),
- * and one 576-byte half tile when K % 128 == 64.
+ * and one 576-byte half tile when K % 128 == 64.  A matrix whose panels end
+ * in a half tile is followed by a 576-byte zero guard (part of the packed
+ * size), so that a full-tile load issued at the last half tile stays inside
+ * the buffer.
  * ------------------------------------------------------------------------- */
 
 /* Bytes of the packed NVFP4 matrix [N][K]; 0 if N % 16 != 0, K % 16 != 0 or

@@ -48,26 +48,73 @@ struct KP2 {
   int half_t;      // packed index of the half tile, -1 if none
   int KS, KR;      // k-splits and tiles per split
   int KW;          // waves splitting a workgroup's k-range (one group per wave if > 1)
-  int NGW;         // result slots (panel groups) per wave in LDS
   int PB;          // panels per workgroup block
   int nblocks;     // panel blocks
+  int res_off;     // byte offset of the result area in dynamic LDS
+  int rs;          // result row stride in floats (PB * 16 + 4)
+  unsigned nc4_magic;  // ceil(2^32 / (PB * 4)): row of an epilogue item without a division
   float* partial;  // [KS][M][N] fp32 (KS > 1)
   unsigned* bcnt;  // [nblocks] arrival counters (KS > 1), left at zero
 };
 
 constexpr int kMaxKS = 8;  // partial sums summed per output by the last workgroup
+constexpr size_t kGemmLdsMax = 160 * 1024 - 512;  // dynamic LDS per workgroup (static LDS is < 512 B)
+
+// LDS bytes of one workgroup: staged activations (+ zero row), then KW row-major
+// result blocks [M][PB * 16 + 4]
+__host__ __device__ inline size_t gemm_res_offset(int M, int KR) {
+  return (static_cast<size_t>(stage_bytes(M, KR)) + 15) / 16 * 16;
+}
+__host__ __device__ inline size_t gemm_lds_bytes(int M, int KR, int KW, int PB) {
+  return gemm_res_offset(M, KR) + static_cast<size_t>(KW) * M * (PB * 16 + 4) * 4;
+}
+
+// output element group (m, n .. n + 3) -> stored values (rounded to the output type)
+__device__ __forceinline__ f32x4 store_out4(void* out, int dtype, size_t off, f32x4 v) {
+  if (dtype == Q4_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = v;
+    return v;
+  } else if (dtype == Q4_F16) {
+    typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 h = {(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+    *reinterpret_cast<f16x4*>(static_cast<f16*>(out) + off) = h;
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  } else {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + off) = h;
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  }
+}
+
+__device__ __forceinline__ unsigned long long max_key_64(unsigned long long k) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned lo = __shfl_xor(static_cast<unsigned>(k), off);
+    const unsigned hi = __shfl_xor(static_cast<unsigned>(k >> 32), off);
+    const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+// 16 bytes written by other workgroups (possibly on other XCDs): agent-scope loads
+__device__ __forceinline__ f32x4 load_coherent4(const float* p) {
+  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+  const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float(static_cast<unsigned>(lo)), __uint_as_float(static_cast<unsigned>(lo >> 32)),
+               __uint_as_float(static_cast<unsigned>(hi)), __uint_as_float(static_cast<unsigned>(hi >> 32))};
+}
 
 template <int FMT, int P, int W, int D>
 __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
-  // dynamic LDS: [KR tiles of activations][W waves x NGW groups x P panels of results]
-  extern __shared__ u32x4 alds[];
+  // dynamic LDS: staged activations (+ zero row), then KW row-major result blocks [M][rs]
+  extern __shared__ u32x4 lds[];
   __shared__ unsigned long long sbest[16];
   __shared__ int s_last;
   const GemmArgs& g = kp.g;
-  const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int o = lane >> 4;
-  const int c = lane & 15;
   const int KS = kp.KS, KW = kp.KW;
   const int PWv = W / KW;                                  // wave columns (panel groups in parallel)
   const int kw = w % KW, pw = w / KW;
@@ -82,88 +129,112 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
   const int pend = min(kp.npanels, p0 + kp.PB);
   const int ngb = (pend - p0 + P - 1) / P;                 // panel groups in the block
   const int ng = ngb > pw ? (ngb - pw + PWv - 1) / PWv : 0; // this wave's: pw, pw + PWv, ...
-  const int NGW = kp.NGW;                                  // result slots per wave
-  f32x4* const rbase = reinterpret_cast<f32x4*>(alds + static_cast<size_t>(kp.KR) * 4 * 64);  // results
-  f32x4* wout = rbase + static_cast<size_t>(w) * NGW * P * 64;
-  const int M = g.M;
+  const int M = g.M, rs = kp.rs;
+  float* const res = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kp.res_off);
+  float* const wres = res + static_cast<size_t>(kw) * M * rs;  // this wave's k-slice block
   const float gs = g.gscale;
 
   if (threadIdx.x < 16) sbest[threadIdx.x] = 0ull;
-  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
 
   auto gbase = [&](int gi, int p) -> const uint8_t* {
     int panel = p0 + (pw + gi * PWv) * P + p;
-    panel = panel < kp.npanels ? panel : kp.npanels - 1;   // in-bounds load, store skipped
+    panel = panel < kp.npanels ? panel : kp.npanels - 1;   // in-bounds load, result dropped
     return g.w + static_cast<size_t>(panel) * static_cast<size_t>(g.panel_bytes);
   };
-  StageRegs stg;
-  auto pre_issue = [&]() { stage_issue(stg, g.a, M, g.K, kt0, KRg); };
-  auto pre = [&]() {
-    stage_finish(stg, alds, g.a, M, g.K, kt0, KRg);
-    __syncthreads();
-  };
-  auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash<P>(wout, gi, acc); };
-  auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
-  stream_groups<FMT, P, D, true>(ng, wtn, kt0 + wt0, kp.half_t, alds + static_cast<size_t>(wt0) * 4 * 64, nullptr,
-                                 false, g.K, gbase, pre_issue, pre, epi, epi_add);
+  const StageGeom sg = stage_geom(g.a, M, g.K, kt0, KRg);
+  auto pre_issue = [&]() { stage_issue(sg, lds); };
+  auto pre = [&]() { stage_wait<D * P * 2>(); };  // D tiles of P panels: codes + scales
+  auto col_of = [&](int gi) { return (pw + gi * PWv) * P * 16; };  // block-local first column
+  auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash_rows<P, false>(wres, rs, col_of(gi), M, acc); };
+  auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_rows<P, true>(wres, rs, col_of(gi), M, acc); };
+  const ALds al = alds_view(reinterpret_cast<const char*>(lds), KRg, M, wt0);
+  stream_groups<FMT, P, D, true>(ng, wtn, kt0 + wt0, kp.half_t, al, nullptr, false, g.K, gbase, pre_issue, pre, epi,
+                                 epi_add);
   if (wtn == 0) {  // a k-split wave without tiles still owns zero partials
-    for (int gi = 0; gi < ng; ++gi)
+    f32x4 z[P][2];
 #pragma unroll
-      for (int p = 0; p < P; ++p) wout[(gi * P + p) * 64 + lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < P; ++p) z[p][0] = z[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < ng; ++gi) stash_rows<P, false>(wres, rs, col_of(gi), M, z);
   }
+  __syncthreads();
 
-  // final value of output (m, n) -> stored, argmax key kept
-  auto finish = [&](int r, int m, int n, float v) {
-    const float y = store_out(g.out, g.out_dtype, static_cast<size_t>(m) * g.N + n, gs * v);
-    const unsigned long long key = argmax_key(y, n);
-    best[r] = key > best[r] ? key : best[r];
+  // Epilogue over the block's outputs, row-major in 4-column groups: every
+  // thread sums the KW k-slices of its group, then stores 4 outputs (or 4
+  // partials) in one vector store, so a wave writes 64 consecutive groups.
+  const int nc4 = (pend - p0) * 4;  // 4-column groups per row
+  // row of item q: q / nc4 by a multiply and a correction (the magic is for
+  // PB * 4: exact up to one step, except in a last block with fewer panels,
+  // whose few items correct by more steps)
+  auto item_row = [&](int q) {
+    int m = static_cast<int>(__umulhi(static_cast<unsigned>(q), kp.nc4_magic));
+    while (m * nc4 > q) --m;
+    while ((m + 1) * nc4 <= q) ++m;
+    return m;
   };
-  // group gi of wave column pw: results of k-split waves kw' = 0..KW-1 summed in order
-  if (KW > 1) __syncthreads();
-  if (kw == 0) {
-    for (int gi = 0; gi < ng; ++gi) {
+  const int items = M * nc4;
+  const bool wave_rows = (nc4 & 63) == 0;  // each wave-wide batch of items lies in one row
+  for (int q0 = 0; q0 < items; q0 += 64 * W) {
+    const int q = q0 + static_cast<int>(threadIdx.x);
+    unsigned long long key = 0ull;
+    int m = 0;
+    if (q < items) {
+      m = item_row(q);
+      const int c4 = q - m * nc4;
+      const float* rp = res + m * rs + c4 * 4;
+      f32x4 v = *reinterpret_cast<const f32x4*>(rp);
+      for (int j = 1; j < KW; ++j) v += *reinterpret_cast<const f32x4*>(rp + static_cast<size_t>(j) * M * rs);
+      const int n = p0 * 16 + c4 * 4;
+      const size_t off = static_cast<size_t>(m) * g.N + n;
+      if (KS == 1) {
+        const f32x4 y = store_out4(g.out, g.out_dtype, off, gs * v);
+        if (g.argmax) {
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int panel = p0 + (pw + gi * PWv) * P + p;
-        if (panel >= pend) continue;
-        f32x4 v = wout[(gi * P + p) * 64 + lane];
-        for (int j = 1; j < KW; ++j) v += rbase[static_cast<size_t>(pw * KW + j) * NGW * P * 64 + (gi * P + p) * 64 + lane];
-        const int n = panel * 16 + c;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 4 * o + r;
-          if (m >= M) continue;
-          if (KS == 1)
-            finish(r, m, n, v[r]);
-          else
-            kp.partial[(static_cast<size_t>(ks) * M + m) * g.N + n] = v[r];
+          for (int j = 0; j < 4; ++j) {
+            const unsigned long long kj = argmax_key(y[j], n + j);
+            key = kj > key ? kj : key;
+          }
         }
+      } else {
+        *reinterpret_cast<f32x4*>(kp.partial + static_cast<size_t>(ks) * M * g.N + off) = v;
+      }
+    }
+    if (KS == 1 && g.argmax) {
+      if (wave_rows) {  // uniform row per wave: one LDS atomic per wave
+        key = max_key_64(key);
+        if ((threadIdx.x & 63) == 0 && key != 0ull) atomicMax(&sbest[m], key);
+      } else if (key != 0ull) {
+        atomicMax(&sbest[m], key);
       }
     }
   }
 
   bool final_wg = true;  // does this workgroup hold final values of its block?
   if (KS > 1) {
-    __syncthreads();  // every wave's partial stores have reached L2
+    __syncthreads();  // every wave's partial stores have completed
     if (threadIdx.x == 0) s_last = arrive(kp.bcnt + pb) == static_cast<unsigned>(KS - 1);
     __syncthreads();
     final_wg = s_last != 0;
     if (final_wg) {
-      const int ncols = (pend - p0) * 16;
-      // all KS partials of an item are loaded together, then summed in ks order
-      for (int q = threadIdx.x; q < M * ncols; q += 64 * W) {
-        const int m = q / ncols;
-        const int n = p0 * 16 + (q - m * ncols);
-        float v[kMaxKS];
+      // all KS partials of a 4-column group are loaded together, then summed in ks order
+      for (int q = threadIdx.x; q < items; q += 64 * W) {
+        const int m = item_row(q);
+        const int n = p0 * 16 + (q - m * nc4) * 4;
+        const size_t off = static_cast<size_t>(m) * g.N + n;
+        f32x4 v[kMaxKS];
 #pragma unroll
         for (int j = 0; j < kMaxKS; ++j)
-          v[j] = j < KS ? load_coherent(kp.partial + (static_cast<size_t>(j) * M + m) * g.N + n) : 0.f;
-        float sacc = 0.f;
+          v[j] = j < KS ? load_coherent4(kp.partial + static_cast<size_t>(j) * M * g.N + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 sacc = v[0];
 #pragma unroll
-        for (int j = 0; j < kMaxKS; ++j) sacc += v[j];
-        const float y = store_out(g.out, g.out_dtype, static_cast<size_t>(m) * g.N + n, gs * sacc);
+        for (int j = 1; j < kMaxKS; ++j) sacc += v[j];
+        const f32x4 y = store_out4(g.out, g.out_dtype, off, gs * sacc);
         if (g.argmax) {
-          const unsigned long long key = argmax_key(y, n);
+          unsigned long long key = 0ull;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const unsigned long long kj = argmax_key(y[j], n + j);
+            key = kj > key ? kj : key;
+          }
           if (key) atomicMax(&sbest[m], key);
         }
       }
@@ -172,13 +243,6 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
   }
 
   if (g.argmax && final_wg) {
-    if (KS == 1) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const unsigned long long k = max_key_16(best[r]);
-        if (c == 0 && k != 0ull) atomicMax(&sbest[4 * o + r], k);
-      }
-    }
     __syncthreads();
     if (threadIdx.x < 16 && static_cast<int>(threadIdx.x) < M && sbest[threadIdx.x] != 0ull)
       atomicMax(g.keys + threadIdx.x, sbest[threadIdx.x]);
@@ -250,7 +314,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(const uint8_t* __restrict__
 
 template <int FMT, int P, int W, int D>
 int launch_cfg(const KP2& kp, hipStream_t s) {
-  const size_t lds = (static_cast<size_t>(kp.KR) * 4 * 64 + static_cast<size_t>(W) * kp.NGW * P * 64) * sizeof(u32x4);
+  const size_t lds = gemm_lds_bytes(kp.g.M, kp.KR, kp.KW, kp.PB);
   static size_t lds_allowed = 48 * 1024;  // per instantiation: raise the dynamic LDS limit on demand
   if (lds > lds_allowed) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm2_kernel<FMT, P, W, D>),
@@ -285,7 +349,6 @@ int launch_fmt(const KP2& kp, const GemmCfg& cfg, hipStream_t s) {
 
 GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
   (void)fmt;
-  (void)M;
   const int npanels = static_cast<int>(N / 16);
   const int ntiles = static_cast<int>(full_tiles(K) + (has_half_tile(K) ? 1 : 0));
   GemmCfg c{};
@@ -293,25 +356,28 @@ GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
     if (std::sscanf(e, "%d,%d,%d,%d,%d,%d", &c.P, &c.W, &c.D, &c.KS, &c.KW, &c.PB) == 6) {
       c.KS = c.KS < 1 ? 1 : (c.KS > ntiles ? ntiles : (c.KS > kMaxKS ? kMaxKS : c.KS));
       c.KW = (c.KW >= 1 && c.W % c.KW == 0) ? c.KW : 1;
-      if (c.KW > 1 && c.PB > c.P * (c.W / c.KW)) c.PB = c.P * (c.W / c.KW);  // one group per wave
       return c;
     }
   }
+  constexpr size_t kBudget = kGemmLdsMax;
+  auto fits = [&](const GemmCfg& x) {
+    const int KR = (ntiles + x.KS - 1) / x.KS;
+    return gemm_lds_bytes(M, KR, x.KW, x.PB) <= kBudget;
+  };
   c.P = 2;
   c.W = 8;
   c.D = 4;
   c.KW = 1;
   c.KS = 1;
-  // LDS holds a workgroup's k-range of activations, 4 KiB per tile: at most 32 tiles (128 KiB)
-  while ((ntiles + c.KS - 1) / c.KS > 32) c.KS *= 2;
   if (npanels >= 4096) {
     // large N: one k-range, persistent blocks over 256 workgroups
-    while ((ntiles + c.KS - 1) / c.KS > 24) c.KS *= 2;
     c.PB = ((npanels + 255) / 256 + c.P * c.W - 1) / (c.P * c.W) * (c.P * c.W);
+    while (!fits(c) && c.KS < kMaxKS) c.KS *= 2;
   } else {
     // small N: 8 waves split each workgroup's k-range over one group of 2 panels
     c.KW = 8;
     c.PB = 2;
+    while (!fits(c) && c.KS < kMaxKS) c.KS *= 2;
     while (c.KS * ((npanels + 1) / 2) < 256 && (ntiles + 2 * c.KS - 1) / (2 * c.KS) >= 8) c.KS *= 2;
   }
   if (c.KS > kMaxKS) c.KS = kMaxKS;
@@ -320,11 +386,17 @@ GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
   return c;
 }
 
+// k-split actually launched: cfg.KS, less any k-range that would be empty
+static int launch_ks(const GemmCfg& c, int ntiles) {
+  const int KS = c.KS < 1 ? 1 : c.KS;
+  const int KR = (ntiles + KS - 1) / KS;
+  return (ntiles + KR - 1) / KR;
+}
+
 size_t gemm_workspace(int fmt, int M, int64_t K, int64_t N) {
   const GemmCfg c = choose_gemm_cfg(fmt, M, K, N);
   const int ntiles = static_cast<int>(full_tiles(K) + (has_half_tile(K) ? 1 : 0));
-  const int KR = (ntiles + c.KS - 1) / c.KS;
-  const int KS = (ntiles + KR - 1) / KR;
+  const int KS = launch_ks(c, ntiles);
   size_t bytes = kWsCounterBytes;
   if (KS > 1) bytes += static_cast<size_t>(KS) * M * N * 4;
   return bytes;
@@ -336,26 +408,23 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
   kp.npanels = g.N / 16;
   kp.ntiles = g.nfull + g.half;
   kp.half_t = g.half ? g.nfull : -1;
-  kp.KS = cfg.KS;
-  kp.KR = (kp.ntiles + cfg.KS - 1) / cfg.KS;
-  kp.KS = (kp.ntiles + kp.KR - 1) / kp.KR;  // no empty k-range
+  kp.KS = launch_ks(cfg, kp.ntiles);
+  kp.KR = (kp.ntiles + kp.KS - 1) / kp.KS;
   kp.KW = cfg.KW;
-  kp.PB = cfg.PB;
-  kp.nblocks = (kp.npanels + cfg.PB - 1) / cfg.PB;
-  {
-    const int pwv = cfg.W / (cfg.KW > 0 ? cfg.KW : 1);
-    const int ngb = (cfg.PB + cfg.P - 1) / cfg.P;
-    kp.NGW = (ngb + pwv - 1) / pwv;
-  }
+  if (cfg.P < 1 || cfg.PB < 1) return static_cast<int>(hipErrorInvalidConfiguration);
+  kp.PB = (cfg.PB + cfg.P - 1) / cfg.P * cfg.P;  // whole groups: every stashed column has a slot
+  kp.nblocks = (kp.npanels + kp.PB - 1) / kp.PB;
+  kp.rs = kp.PB * 16 + 4;
+  kp.nc4_magic = static_cast<unsigned>(((1ull << 32) + kp.PB * 4 - 1) / (kp.PB * 4));
+  kp.res_off = static_cast<int>(gemm_res_offset(g.M, kp.KR));
   if (kp.KS > kMaxKS) return static_cast<int>(hipErrorInvalidConfiguration);
-  if (kp.KW < 1 || cfg.W % kp.KW != 0 || (kp.KW > 1 && kp.PB > cfg.P * (cfg.W / kp.KW)))
-    return static_cast<int>(hipErrorInvalidConfiguration);
+  if (kp.KW < 1 || cfg.W % kp.KW != 0 || kp.PB < 1) return static_cast<int>(hipErrorInvalidConfiguration);
   if (kp.KS > 1) {
     if (kp.nblocks > kMaxSplitBlocks) return static_cast<int>(hipErrorInvalidConfiguration);
     kp.bcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsBlockCounters);
     kp.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
   }
-  if ((static_cast<size_t>(kp.KR) * 256 + static_cast<size_t>(cfg.W) * kp.NGW * cfg.P * 64) * 16 > 158 * 1024)
+  if (gemm_lds_bytes(g.M, kp.KR, kp.KW, kp.PB) > kGemmLdsMax)
     return static_cast<int>(hipErrorInvalidConfiguration);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return fmt == kNvfp4 ? launch_fmt<kNvfp4>(kp, cfg, s) : launch_fmt<kAffine>(kp, cfg, s);

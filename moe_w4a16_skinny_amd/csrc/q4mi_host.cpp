@@ -140,7 +140,7 @@ const char* q4_last_error(void) { return g_last_error.c_str(); }
 
 size_t q4_nvfp4_packed_bytes(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % 16 || K % 16) return 0;
-  return size_t(N / 16) * size_t(panel_bytes(K));
+  return size_t(packed_matrix_bytes(N, K));
 }
 
 int q4_nvfp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, void* packed,
@@ -152,6 +152,7 @@ int q4_nvfp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int6
   if (packed_bytes < q4_nvfp4_packed_bytes(N, K))
     return fail(Q4_ERR_INVALID_ARG, "%s: packed_bytes=%zu < %zu", __func__, packed_bytes, q4_nvfp4_packed_bytes(N, K));
   uint8_t* out = static_cast<uint8_t*>(packed);
+  std::memset(out + N / 16 * panel_bytes(K), 0, size_t(packed_tail(K)));
   nvfp4_walk(N, K,
              [&](int64_t off, int64_t n, int64_t kk) { out[off] = code_byte(codes, K, n, kk); },
              [&](int64_t off, int64_t n, int64_t grp) { out[off] = scale_byte(scales, K, n, grp); });
@@ -176,7 +177,7 @@ int q4_nvfp4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes, ui
 
 size_t q4_affine4_packed_bytes(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % 16 || K % 64) return 0;
-  return size_t(N / 16) * size_t(panel_bytes(K));
+  return size_t(packed_matrix_bytes(N, K));
 }
 
 int q4_affine4_repack(const uint8_t* codes, const uint16_t* scale_bf16, const uint16_t* bias_bf16,
@@ -189,6 +190,7 @@ int q4_affine4_repack(const uint8_t* codes, const uint16_t* scale_bf16, const ui
   if (packed_bytes < q4_affine4_packed_bytes(N, K))
     return fail(Q4_ERR_INVALID_ARG, "%s: packed_bytes=%zu < %zu", __func__, packed_bytes, q4_affine4_packed_bytes(N, K));
   uint8_t* out = static_cast<uint8_t*>(packed);
+  std::memset(out + N / 16 * panel_bytes(K), 0, size_t(packed_tail(K)));
   const int64_t G = K / 64;
   affine_walk(
       N, K,

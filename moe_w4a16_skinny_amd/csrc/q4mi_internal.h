@@ -34,6 +34,11 @@ Q4_HD inline bool has_half_tile(int64_t K) { return padded_k(K) % kTileK != 0; }
 Q4_HD inline int64_t panel_bytes(int64_t K) {
   return full_tiles(K) * kTileBytes + (has_half_tile(K) ? kHalfBytes : 0);
 }
+// Zero guard behind the last panel when panels end in a half tile: a kernel
+// may issue a full-tile load at a half tile (and never use its second half),
+// which then stays inside the buffer.
+Q4_HD inline int64_t packed_tail(int64_t K) { return has_half_tile(K) ? kTileBytes - kHalfBytes : 0; }
+Q4_HD inline int64_t packed_matrix_bytes(int64_t N, int64_t K) { return N / 16 * panel_bytes(K) + packed_tail(K); }
 
 enum Fmt { kNvfp4 = 0, kAffine = 1 };
 

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int PPB)
   auto pre = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[2][2]) { stash<2>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[2][2]) { stash_add<2>(wout, gi, acc); };
-  stream_groups<kNvfp4, 2, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, nullptr, arow, arow_ok,
+  stream_groups<kNvfp4, 2, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, arow, arow_ok,
                                       m.D, gbase, pre, pre, epi, epi_add);
   for (int gi = 0; gi < ng; ++gi) {
     const int jp = j0 + w + gi * W;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int PB) {
   auto pre = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash<P>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
-  stream_groups<kNvfp4, P, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, nullptr, arow, arow_ok,
+  stream_groups<kNvfp4, P, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, arow, arow_ok,
                                       m.F, gbase, pre, pre, epi, epi_add);
   for (int gi = 0; gi < ng; ++gi) {
 #pragma unroll

@@ -183,10 +183,8 @@ __device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4
 }
 
 // Where a wave's activation operands come from.
-//  * ALDS: the workgroup staged the k-range in LDS as [tile][step i][octet o]
-//    [row c] 16-byte blocks (rows >= M and k >= K zero), so that lane l of
-//    step i of local tile t reads block (t * 4 + i) * 64 + l: one
-//    conflict-free ds_read_b128 per step.
+//  * ALDS: the workgroup staged its k-range of the activations in LDS (see
+//    stage_a); ALds gives each lane its read address.
 //  * global: lane reads a[row][k0 .. k0 + 8) from its row pointer, zeros for
 //    rows it does not own or k0 >= K (the only bound check of the loop).
 template <int FMT, int P, bool ALDS>
@@ -196,82 +194,117 @@ struct StreamStage {
   u32x4 a[ALDS ? 1 : 4];
 };
 
-// Stage the activation k-range [kt0, kt0 + nt) tiles of rows 0..M-1 into LDS
-// in the ALDS layout (whole workgroup; caller synchronizes).  a is [M][K].
-// In two halves so that the loads can be in flight together with the first
-// weight tiles: stage_issue loads this thread's first kStageB blocks into
-// registers, stage_finish writes them (and stages any remaining blocks).
-constexpr int kStageB = 16;
-struct StageRegs {
-  u32x4 v[kStageB];
+// Staged activations in LDS, row-major: row c (< M) of a workgroup's
+// k-range of nt tiles is nt * 256 contiguous bytes at c * RS, with
+// RS = nt * 256 + 16, so that the 16 rows of one 32-k step sit in 16
+// different 16-byte bank groups (conflict-free ds_read_b128: lane (c, o)
+// reads row c, k-octet o).  Lanes of rows c >= M read a zero row placed
+// after the M rows.  For local tile t and step i, lane (c, o) reads
+// base + t * 256 + i * 64 with base = c * RS + o * 16.
+struct ALds {
+  const char* base;  // this lane's address of step 0 of the wave's local tile 0
 };
-// Thread q fills LDS block q (consecutive threads write consecutive 16-byte
-// blocks: no bank conflicts); block q = ((t * 4 + i) * 4 + o) * 16 + c holds
-// a[c][(kt0 + t) * 128 + 32 i + 8 o + 0..7].
-__device__ __forceinline__ void stage_block(int q, int nblk, int* dst, int* c_out, int* k0_out, int kt0) {
-  (void)nblk;
-  const int c = q & 15, o = (q >> 4) & 3, i = (q >> 6) & 3, t = q >> 8;
-  *c_out = c;
-  *k0_out = (kt0 + t) * kTileK + 32 * i + 8 * o;
-  *dst = q;
+__host__ __device__ inline int stage_row_stride(int nt) { return nt * 256 + 16; }
+__host__ __device__ inline int stage_bytes(int M, int nt) {
+  return M * stage_row_stride(nt) + (M < 16 ? nt * 256 : 0);
 }
-__device__ __forceinline__ void stage_issue(StageRegs& r, const uint16_t* a, int M, int K, int kt0, int nt) {
-  const int nblk = nt * 16, total = 16 * nblk;
-#pragma unroll
-  for (int u = 0; u < kStageB; ++u) {
-    const int q = threadIdx.x + u * blockDim.x;
-    int dst, c, k0;
-    stage_block(q, nblk, &dst, &c, &k0, kt0);
-    r.v[u] = (q < total && c < M && k0 < K) ? *reinterpret_cast<const u32x4*>(a + static_cast<size_t>(c) * K + k0)
-                                           : u32x4{0u, 0u, 0u, 0u};
+__device__ __forceinline__ ALds alds_view(const char* stage, int nt_staged, int M, int t0) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, o = lane >> 4;
+  const int rs = stage_row_stride(nt_staged);
+  ALds v;
+  v.base = stage + (c < M ? c * rs : M * rs) + o * 16 + t0 * 256;
+  return v;
+}
+
+// Staging of tiles [kt0, kt0 + nt) of rows 0..M-1 of a [M][K] into LDS
+// (whole workgroup).  One direct-to-LDS load moves 64 consecutive 16-byte
+// k-chunks of one row (1 KiB contiguous in both memories; lane l lands at
+// the load's LDS base + 16 l); lanes past the range or at k >= K load
+// nothing and the bytes they cover are never read as data (k >= K is
+// written as zeros first).  Rows are dealt to the waves; each row's loads
+// start at a workgroup-dependent block so that the CUs of an XCD do not all
+// read the same lines at the same time.  stage_issue only
+// issues the loads, so that they travel together with the first weight
+// tiles; stage_wait (after those weight loads) waits for exactly the staging
+// loads and synchronizes the workgroup.
+struct StageGeom {
+  const uint16_t* a;
+  int M, K, kt0, nt, rs;
+  int bpr;     // 1 KiB load blocks per row
+};
+__device__ __forceinline__ StageGeom stage_geom(const uint16_t* a, int M, int K, int kt0, int nt) {
+  StageGeom g;
+  g.a = a;
+  g.M = M;
+  g.K = K;
+  g.kt0 = kt0;
+  g.nt = nt;
+  g.rs = stage_row_stride(nt);
+  g.bpr = (nt * 16 + 63) / 64;
+  return g;
+}
+__device__ __forceinline__ void stage_issue(const StageGeom& g, u32x4* lds) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  char* const lb = reinterpret_cast<char*>(lds);
+  const int kbase = g.kt0 * kTileK;
+  const int nch = g.nt * 16;                                // 16-byte chunks per row
+  const int kch = min(nch, max(0, (g.K - kbase + 7) / 8));  // chunks holding k < K
+  // chunks at k >= K (the k-padding of the last tile) -> zeros; rows handled by waves
+  if (kch < nch)
+    for (int c = w; c < g.M; c += nw)
+      for (int ch = kch + lane; ch < nch; ch += 64)
+        *reinterpret_cast<u32x4*>(lb + c * g.rs + ch * 16) = u32x4{0u, 0u, 0u, 0u};
+  if (g.M < 16)  // the zero row
+    for (int ch = threadIdx.x; ch < nch; ch += blockDim.x)
+      *reinterpret_cast<u32x4*>(lb + g.M * g.rs + ch * 16) = u32x4{0u, 0u, 0u, 0u};
+  // rows are dealt to waves; within a row the 1 KiB blocks start at a
+  // workgroup-dependent block (no integer division in the loop)
+  int b0 = static_cast<int>(blockIdx.x) * 7;
+  b0 -= (b0 / g.bpr) * g.bpr;
+  for (int c = w; c < g.M; c += nw) {
+    const uint16_t* row = g.a + static_cast<size_t>(c) * g.K + kbase;
+    char* const lrow = lb + c * g.rs;
+    int b = b0;
+    for (int j = 0; j < g.bpr; ++j) {
+      const int ch = b * 64 + lane;
+      if (ch < kch) __builtin_amdgcn_global_load_lds(row + ch * 8, lrow + b * 1024, 16, 0, 0);
+      if (++b == g.bpr) b = 0;
+    }
   }
 }
-__device__ __forceinline__ void stage_finish(const StageRegs& r, u32x4* alds, const uint16_t* a, int M, int K,
-                                             int kt0, int nt) {
-  const int nblk = nt * 16, total = 16 * nblk;
-#pragma unroll
-  for (int u = 0; u < kStageB; ++u) {
-    const int q = threadIdx.x + u * blockDim.x;
-    int dst, c, k0;
-    stage_block(q, nblk, &dst, &c, &k0, kt0);
-    if (q < total) alds[dst] = r.v[u];
-  }
-  // blocks beyond the first kStageB per thread (large k-ranges, few threads)
-  for (int q0 = threadIdx.x + kStageB * blockDim.x; q0 < total; q0 += kStageB * blockDim.x) {
-    StageRegs t;
-#pragma unroll
-    for (int u = 0; u < kStageB; ++u) {
-      const int q = q0 + u * blockDim.x;
-      int dst, c, k0;
-      stage_block(q, nblk, &dst, &c, &k0, kt0);
-      t.v[u] = (q < total && c < M && k0 < K) ? *reinterpret_cast<const u32x4*>(a + static_cast<size_t>(c) * K + k0)
-                                             : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kStageB; ++u) {
-      const int q = q0 + u * blockDim.x;
-      int dst, c, k0;
-      stage_block(q, nblk, &dst, &c, &k0, kt0);
-      if (q < total) alds[dst] = t.v[u];
-    }
-  }
+// NLATER = vector-memory instructions this wave issued after stage_issue.
+// A plain barrier, not __syncthreads: the latter's fence would wait for every
+// outstanding load (the weight tiles too), since direct-to-LDS loads count as
+// vector-memory operations.
+template <int NLATER>
+__device__ __forceinline__ void stage_wait() {
+  static_assert(NLATER >= 0 && NLATER < 64, "vmcnt range");
+  // s_waitcnt vmcnt(NLATER) (bits 3:0 and 15:14) lgkmcnt(0), expcnt left at its maximum
+  __builtin_amdgcn_s_waitcnt((NLATER & 15) | ((NLATER >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
 }
 
 // Stream ng groups of P panels over the tiles [kt0, kt0 + KRg) of each group
 // (global packed tile indices; if half_t falls in that range it must be the
 // range's last tile, the 576-byte half tile), keeping D tiles of weight loads
 // in flight across group boundaries.  gbase(g, p): packed base of panel p of
-// the wave's g-th group.  After the last tile of group g, epi(g, acc) consumes
-// the accumulators (it must not touch global memory: see stash), which
-// restart at zero; the half tile of every group is added afterwards through
-// epi_add(g, acc).  pre_issue() runs before the first weight loads and pre()
-// after them (the workgroup stages its activations across the two, so both
-// travel in the same round trip; every wave must reach pre()).  All
-// arguments except the lane-dependent A row are wave-uniform.
+// the wave's g-th group; it must return an in-bounds panel for any g >= 0
+// (the prologue loads D tiles even when the wave has fewer).  After the last
+// tile of group g, epi(g, acc) consumes the accumulators (it must not touch
+// global memory: stores inside the loop would make the compiler's wait
+// counting degenerate), which restart at zero; the half tile of every group
+// is added afterwards through epi_add(g, acc).  pre_issue() runs before the
+// first weight loads and pre() after them (the workgroup stages its
+// activations across the two, so both travel in the same round trip; every
+// wave must reach pre()).  All arguments except the lane-dependent A source
+// are wave-uniform.
 template <int FMT, int P, int D, bool ALDS, class GBase, class PreIssue, class Pre, class Epi, class EpiAdd>
-__device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, const u32x4* alds,
-                                              const uint16_t* arow, bool arow_ok, int K, GBase gbase,
-                                              PreIssue pre_issue, Pre pre, Epi epi, EpiAdd epi_add) {
+__device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, ALds al, const uint16_t* arow,
+                                              bool arow_ok, int K, GBase gbase, PreIssue pre_issue, Pre pre, Epi epi,
+                                              EpiAdd epi_add) {
   const int lane = threadIdx.x & 63;
   const int o = lane >> 4;
   const int c = lane & 15;
@@ -324,17 +357,19 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   St st[D];
   int lg = 0, lt = 0;  // load cursor (group, tile)
   int cg = 0, ct = 0;  // compute cursor
+  // (>=: a range of only the half tile, KRf == 0, keeps t = 0, the half tile)
   auto load_next = [&](St& x) {
     load(x, lg, lt);
-    if (++lt == KRf) {
+    if (++lt >= KRf) {
       lt = 0;
       ++lg;
     }
   };
   auto tile_a = [&](const St& x, int t, u32x4 (&a)[4]) {
     if constexpr (ALDS) {
+      const char* pa = al.base + t * 256;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = alds[(t * 4 + i) * 64 + lane];
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(pa + i * 64);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = x.a[i];
@@ -353,30 +388,28 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
     }
   };
 
-  // The steady loop issues exactly D loads per D tiles of math with no
-  // condition around any load, so the compiler's wait before each tile only
-  // covers that tile's loads (D - 1 tiles stay in flight).  The drain computes
-  // the last tiles with the remaining loads issued under conditions.
+  // Prologue: D tiles are loaded whatever F is (tiles past the wave's work
+  // read in-bounds panels, or the half tile plus the zero guard behind the
+  // last panel, and are never computed), so the code from here to
+  // the steady loop is straight-line and every wait the compiler places in it
+  // counts exactly the younger loads.  The steady loop issues exactly D loads
+  // per D tiles of math with no condition around any load, so the wait before
+  // each tile covers only that tile's loads; the drain computes the last
+  // tiles with the remaining loads issued under conditions.
   pre_issue();
-  if (F >= D) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_next(st[d]);
-  } else {
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (d < F) load_next(st[d]);
+  for (int d = 0; d < D; ++d) {
+    load_next(st[d]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the steady loop's load order (see the waits below)
   }
   pre();
-  // Drain the prologue once: its first tile is needed next anyway, and
-  // entering the loop with nothing pending lets the compiler's wait before
-  // each tile of the steady loop count only the D - 1 younger tiles.
-  __builtin_amdgcn_s_waitcnt(0);
   int f = 0;
   for (; f + 2 * D <= F; f += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       compute_next(st[d]);
       load_next(st[d]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
@@ -410,6 +443,27 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
           tile_math<FMT, P>(hacc, a, st[d].c, st[d].s);
           epi_add(g0 + d, hacc);
         }
+      }
+    }
+  }
+}
+
+// Park a finished group's P panels in a row-major LDS result block
+// res[m][col] (row stride rs floats; col0 = first column of the group):
+// lane l holds rows 4 (l >> 4) + r of column l & 15.  Rows >= M are dropped.
+template <int P, bool ADD>
+__device__ __forceinline__ void stash_rows(float* res, int rs, int col0, int M, const f32x4 (&acc)[P][2]) {
+  const int lane = threadIdx.x & 63;
+  const int o = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const f32x4 v = acc[p][0] + acc[p][1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * o + r;
+      if (m < M) {
+        float* q = res + m * rs + col0 + p * 16 + c;
+        *q = ADD ? *q + v[r] : v[r];
       }
     }
   }

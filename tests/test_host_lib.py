@@ -38,9 +38,10 @@ def test_nvfp4_repack_round_trip(N, K):
     scales = rng.integers(0, 256, (N, K // 16), dtype=np.uint8)
     packed = q4.q4_nvfp4_repack(codes, scales)
     Kp = (K + 63) // 64 * 64
-    assert packed.size == q4.q4_nvfp4_packed_bytes(N, K) == (N // 16) * ((Kp // 128) * 1152 + (Kp % 128 // 64) * 576)
-    if K % 64 == 0:  # no padding: exactly the algorithmic bytes
-        assert packed.size == N * K // 2 + N * K // 16
+    assert packed.size == q4.q4_nvfp4_packed_bytes(N, K) == (N // 16) * ((Kp // 128) * 1152 + (Kp % 128 // 64) * 576) + (Kp % 128 // 64) * 576
+    if K % 64 == 0:  # no padding: exactly the algorithmic bytes, plus the zero guard after a half tile
+        assert packed.size == N * K // 2 + N * K // 16 + (K % 128 // 64) * 576
+        assert not packed[packed.size - (K % 128 // 64) * 576:].any()
     c2, s2 = q4.q4_nvfp4_unpack(packed, N, K)
     assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
     # every byte of the canonical input lands in a distinct packed byte
@@ -51,7 +52,7 @@ def test_nvfp4_repack_round_trip(N, K):
 def test_affine_repack_round_trip(N, K):
     codes, s, b = synth.affine_weights(N + K, N, K)
     packed = q4.q4_affine4_repack(codes, s, b)
-    assert packed.size == q4.q4_affine4_packed_bytes(N, K) == N * K // 2 + N * (K // 64) * 4
+    assert packed.size == q4.q4_affine4_packed_bytes(N, K) == N * K // 2 + N * (K // 64) * 4 + (K % 128 // 64) * 576
     c2, s2, b2 = q4.q4_affine4_unpack(packed, N, K)
     assert np.array_equal(codes, c2) and np.array_equal(s, s2) and np.array_equal(b, b2)
 
