@@ -69,21 +69,25 @@ __host__ __device__ inline size_t gemm_lds_bytes(int M, int KR, int KW, int PB) 
   return gemm_res_offset(M, KR) + static_cast<size_t>(KW) * M * (PB * 16 + 4) * 4;
 }
 
-// output element group (m, n .. n + 3) -> stored values (rounded to the output type)
+// output element group (m, n .. n + 3) -> stored values (rounded to the output
+// type).  Streaming stores: the outputs are not re-read by this kernel.
 __device__ __forceinline__ f32x4 store_out4(void* out, int dtype, size_t off, f32x4 v) {
   if (dtype == Q4_F32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + off));
     return v;
   } else if (dtype == Q4_F16) {
-    typedef f16 f16x4 __attribute__((ext_vector_type(4)));
-    const f16x4 h = {(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
-    *reinterpret_cast<f16x4*>(static_cast<f16*>(out) + off) = h;
-    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    const f16x2 h0 = {(f16)v[0], (f16)v[1]}, h1 = {(f16)v[2], (f16)v[3]};
+    const u32x2 w = {__builtin_bit_cast(unsigned, h0), __builtin_bit_cast(unsigned, h1)};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(static_cast<f16*>(out) + off));
+    return f32x4{(float)h0[0], (float)h0[1], (float)h1[0], (float)h1[1]};
   } else {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + off) = h;
-    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1], b2 = (__bf16)v[2], b3 = (__bf16)v[3];
+    const u32x2 w = {static_cast<unsigned>(__builtin_bit_cast(unsigned short, b0)) |
+                         (static_cast<unsigned>(__builtin_bit_cast(unsigned short, b1)) << 16),
+                     static_cast<unsigned>(__builtin_bit_cast(unsigned short, b2)) |
+                         (static_cast<unsigned>(__builtin_bit_cast(unsigned short, b3)) << 16)};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(static_cast<__bf16*>(out) + off));
+    return f32x4{(float)b0, (float)b1, (float)b2, (float)b3};
   }
 }
 
@@ -96,15 +100,6 @@ __device__ __forceinline__ unsigned long long max_key_64(unsigned long long k) {
     k = o > k ? o : k;
   }
   return k;
-}
-
-// 16 bytes written by other workgroups (possibly on other XCDs): agent-scope loads
-__device__ __forceinline__ f32x4 load_coherent4(const float* p) {
-  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
-  const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return f32x4{__uint_as_float(static_cast<unsigned>(lo)), __uint_as_float(static_cast<unsigned>(lo >> 32)),
-               __uint_as_float(static_cast<unsigned>(hi)), __uint_as_float(static_cast<unsigned>(hi >> 32))};
 }
 
 template <int FMT, int P, int W, int D>
@@ -195,7 +190,7 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
           }
         }
       } else {
-        *reinterpret_cast<f32x4*>(kp.partial + static_cast<size_t>(ks) * M * g.N + off) = v;
+        store_coherent4(kp.partial + static_cast<size_t>(ks) * M * g.N + off, v);
       }
     }
     if (KS == 1 && g.argmax) {
@@ -210,8 +205,9 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
 
   bool final_wg = true;  // does this workgroup hold final values of its block?
   if (KS > 1) {
-    __syncthreads();  // every wave's partial stores have completed
-    if (threadIdx.x == 0) s_last = arrive(kp.bcnt + pb) == static_cast<unsigned>(KS - 1);
+    wait_stores();  // this wave's partials are at the coherence point
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = count_arrival(kp.bcnt + pb) == static_cast<unsigned>(KS - 1);
     __syncthreads();
     final_wg = s_last != 0;
     if (final_wg) {
@@ -246,9 +242,10 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
     __syncthreads();
     if (threadIdx.x < 16 && static_cast<int>(threadIdx.x) < M && sbest[threadIdx.x] != 0ull)
       atomicMax(g.keys + threadIdx.x, sbest[threadIdx.x]);
+    wait_stores();  // the key atomics have been performed
     __syncthreads();
     if (threadIdx.x == 0) {
-      const unsigned prev = arrive(g.counter);
+      const unsigned prev = count_arrival(g.counter);
       if (prev == static_cast<unsigned>(kp.nblocks - 1)) {
         // keys are read with atomics, which act at the coherence point
         for (int m = 0; m < M; ++m) {
@@ -359,27 +356,35 @@ GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
       return c;
     }
   }
-  constexpr size_t kBudget = kGemmLdsMax;
-  auto fits = [&](const GemmCfg& x) {
-    const int KR = (ntiles + x.KS - 1) / x.KS;
-    return gemm_lds_bytes(M, KR, x.KW, x.PB) <= kBudget;
-  };
+  // About one workgroup per CU: blocks * KS ~ 256.  KS (k-ranges reduced
+  // across workgroups) only as far as needed for the staged activations to
+  // fit in LDS; inside a workgroup, KW waves split the k-range when a block
+  // has fewer panel groups than waves.
   c.P = 2;
   c.W = 8;
-  c.D = 4;
-  c.KW = 1;
-  c.KS = 1;
-  if (npanels >= 4096) {
-    // large N: one k-range, persistent blocks over 256 workgroups
-    c.PB = ((npanels + 255) / 256 + c.P * c.W - 1) / (c.P * c.W) * (c.P * c.W);
-    while (!fits(c) && c.KS < kMaxKS) c.KS *= 2;
-  } else {
-    // small N: 8 waves split each workgroup's k-range over one group of 2 panels
-    c.KW = 8;
-    c.PB = 2;
-    while (!fits(c) && c.KS < kMaxKS) c.KS *= 2;
-    while (c.KS * ((npanels + 1) / 2) < 256 && (ntiles + 2 * c.KS - 1) / (2 * c.KS) >= 8) c.KS *= 2;
-  }
+  c.D = npanels >= 4096 ? 8 : 4;  // long streams: more bytes in flight per wave
+  auto shape = [&](int KS) {
+    GemmCfg x = c;
+    x.KS = KS;
+    int PB = static_cast<int>((static_cast<int64_t>(npanels) * KS + 255) / 256);
+    PB = (PB + x.P - 1) / x.P * x.P;
+    if (PB >= x.P * x.W) {
+      x.KW = 1;
+      x.PB = PB;
+    } else {
+      x.KW = x.W;
+      while (x.KW > 1 && x.P * (x.W / x.KW) < PB) x.KW /= 2;
+      x.PB = x.P * (x.W / x.KW);
+    }
+    return x;
+  };
+  auto fits = [&](const GemmCfg& x) {
+    const int KR = (ntiles + x.KS - 1) / x.KS;
+    return gemm_lds_bytes(M, KR, x.KW, x.PB) <= kGemmLdsMax;
+  };
+  int KS = 1;
+  c = shape(KS);
+  while (!fits(c) && KS < kMaxKS && KS < ntiles) c = shape(++KS);
   if (c.KS > kMaxKS) c.KS = kMaxKS;
   if (c.KS > ntiles) c.KS = ntiles;
   if (c.KS > 1 && (npanels + c.PB - 1) / c.PB > kMaxSplitBlocks) c.KS = 1;

@@ -96,12 +96,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
 #pragma unroll
     for (int t = 0; t < kRouteTG; ++t) {
       const int tt = tg * kRouteTG + t;
-      if (tt < T) r.partial[(static_cast<size_t>(blockIdx.x) * T + tt) * E + e] = acc[t];
+      if (tt < T) store_coherent(r.partial + (static_cast<size_t>(blockIdx.x) * T + tt) * E + e, acc[t]);
     }
   }
-  __syncthreads();  // every wave's partial stores have reached L2
+  wait_stores();  // this wave's partials are at the coherence point
+  __syncthreads();
   __shared__ int s_last;
-  if (tid == 0) s_last = arrive(r.counter) == gridDim.x - 1;
+  if (tid == 0) s_last = count_arrival(r.counter) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
 

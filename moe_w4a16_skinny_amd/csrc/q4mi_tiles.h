@@ -87,18 +87,38 @@ __device__ __forceinline__ float store_out(void* out, int dtype, size_t off, flo
   }
 }
 
-// Cross-workgroup handoff without cache-wide invalidation: the producer's
-// stores reach the coherence point through one agent-scope release fence
-// (issued by one thread after a workgroup barrier has drained every wave's
-// stores to L2), then an arrival counter is bumped; the consumer reads the
-// published data with agent-scope loads, which bypass stale L2 lines, so no
-// acquire fence (L2 invalidation) is needed.
-__device__ __forceinline__ unsigned arrive(unsigned* counter) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// Cross-workgroup handoff without any cache-wide write-back or invalidation.
+// Data meant for another workgroup (possibly on another XCD, whose L2 is not
+// coherent with this one) is written with agent-scope atomic stores, which
+// write through to the device coherence point; every wave waits for its own
+// stores to complete (wait_stores) before the workgroup barrier, after which
+// one thread bumps an arrival counter with an agent-scope atomic.  The
+// workgroup that sees the final count reads the data with agent-scope loads,
+// which fetch from the coherence point instead of a possibly stale L2 line.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent4(float* p, f32x4 v) {
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+  const unsigned long long lo = (static_cast<unsigned long long>(__float_as_uint(v[1])) << 32) | __float_as_uint(v[0]);
+  const unsigned long long hi = (static_cast<unsigned long long>(__float_as_uint(v[3])) << 32) | __float_as_uint(v[2]);
+  __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// this wave's stores and atomics have completed (stores count in vmcnt here)
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned count_arrival(unsigned* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_coherent4(const float* p) {
+  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+  const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float(static_cast<unsigned>(lo)), __uint_as_float(static_cast<unsigned>(lo >> 32)),
+               __uint_as_float(static_cast<unsigned>(hi)), __uint_as_float(static_cast<unsigned>(hi >> 32))};
 }
 
 // ordered 64-bit key: larger value first, then lower index; 0 = "no value"
