@@ -173,8 +173,8 @@ size_t moe_route_workspace_bytes(int T, int D, int E);
  *   topk_idx device int32 [T][k];  topk_w device fp32 [T][k]
  *   ws       device workspace (zero-filled before first use, left zero-filled)
  * Errors: INVALID_ARG, UNSUPPORTED (T outside 1..64, E outside 1..256,
- * roundup(T, 8) * E > 4096, k > E or k > 16, D % 8), ALIGNMENT, WORKSPACE,
- * HIP. */
+ * k > E or k > 16, D % 8, D beyond about 1400 * min(16, 1024 / E) * 16),
+ * ALIGNMENT, WORKSPACE, HIP. */
 int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k,
                    int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
                    size_t ws_bytes, void* stream);

@@ -85,21 +85,31 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
 int launch_dequant(int fmt, const uint8_t* w, int64_t panel_bytes, int64_t N, int64_t K, float g,
                    float* out, void* stream);
 
-// Router split of D over workgroups: each holds `route_rows` rows of W_r (and
-// the matching x columns) in LDS; the last of the ceil(D / rows) <= 32
-// workgroups sums their partial logits.
-constexpr int kRouteMaxBlocks = 32;
-Q4_HD inline int route_rows(int T, int D, int E) {
-  int rows = 24576 / (E + T);  // (E + T) floats of LDS per row, 96 KiB in all
-  const int need = (D + kRouteMaxBlocks - 1) / kRouteMaxBlocks;
-  rows = rows < need ? need : rows;
-  return rows < D ? rows : D;
+// Router split of D over at most kRouteMaxBlocks workgroups of
+// kRouteThreads threads (8 waves).  A wave computes 16 experts x 16 tokens
+// with fp32 MFMAs over a slice of the workgroup's rows (8 / column blocks
+// slices when E < 128, summed in LDS in slice order); the last workgroup to
+// finish adds the blocks' partial logits in block order.
+constexpr int kRouteThreads = 512;
+constexpr int kRouteMaxBlocks = 16;
+Q4_HD inline int route_slices(int E) {
+  const int cb = (E + 15) / 16;
+  return cb >= 8 ? 1 : 8 / cb;
 }
-Q4_HD inline size_t route_lds_bytes(int T, int D, int E) {
-  const size_t rows = static_cast<size_t>(route_rows(T, D, E));
-  const size_t stage = rows * E * 4 + static_cast<size_t>(T) * rows * 4;
-  const size_t fin = static_cast<size_t>(T) * E * 4;
-  return stage > fin ? stage : fin;
+Q4_HD inline int route_rows(int D, int E) {  // rows per workgroup: a multiple of 16 per slice
+  const int unit = 16 * route_slices(E);
+  int nb = (D + 4 * unit - 1) / (4 * unit);  // at least 64 rows per slice
+  nb = nb < 1 ? 1 : (nb > kRouteMaxBlocks ? kRouteMaxBlocks : nb);
+  const int per = (D + nb - 1) / nb;
+  return (per + unit - 1) / unit * unit;
+}
+Q4_HD inline int route_blocks(int D, int E) { return (D + route_rows(D, E) - 1) / route_rows(D, E); }
+// staged x (rows x 16 tokens, fp32) + slice sums / logits (64 KiB holds both
+// slices * 16 * E <= 4096 and T * E <= 16384 floats)
+// (the staged-x area, at least 16 KiB, later holds 8 waves x 256 keys)
+Q4_HD inline size_t route_lds_bytes(int D, int E) {
+  const size_t xs = static_cast<size_t>(route_rows(D, E)) * 64;
+  return (xs < 16384 ? 16384 : xs) + 65536;
 }
 
 struct RouteArgs {
@@ -112,6 +122,7 @@ struct RouteArgs {
   float* partial;       // workspace [nblk][T][E]
   unsigned* counter;    // workspace counter
   int nblk;             // workgroups splitting D
+  int rows;             // rows of D per workgroup
 };
 int launch_route(const RouteArgs& r, void* stream);
 

@@ -33,71 +33,133 @@ using namespace dev;
 
 // ------------------------------------------------------------------ router
 
-constexpr int kRouteThreads = 256;
-constexpr int kRouteTG = 8;         // tokens per thread item
+// Ordered key of (logit, expert), kRouteKeyBits wide: larger logit first,
+// then lower expert index (9 bits, E <= 256); distinct and non-zero for every
+// expert (a NaN logit ranks below -inf); 0 marks "no expert".
+constexpr int kRouteKeyBits = 41;
+__device__ __forceinline__ unsigned long long route_key(float v, int e) {
+  unsigned ord = 0u;
+  if (v == v) {
+    if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
+    const unsigned b = __float_as_uint(v);
+    ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  }
+  return (static_cast<unsigned long long>(ord) << 9) | (511u - static_cast<unsigned>(e)) + 0ull;
+}
+// logit of a key (inverse of the order map; NaN keys never reach this)
+__device__ __forceinline__ float route_key_value(unsigned long long key) {
+  const unsigned ord = static_cast<unsigned>(key >> 9);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+// Wave-wide reductions with DPP: row_shr 1, 2, 4, 8 leave each row's total in
+// its lane 15, row_bcast 15 and 31 fold the rows into lane 63, which is then
+// read into a scalar register (a fixed combination order).  Lanes shifted in
+// from outside a row read 0, the identity of both reductions used here.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u32(unsigned x) {
+  return static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_key(unsigned long long k) {
+  const unsigned lo = dpp_u32<CTRL>(static_cast<unsigned>(k));
+  const unsigned hi = dpp_u32<CTRL>(static_cast<unsigned>(k >> 32));
+  const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
+  return o > k ? o : k;
+}
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+  k = dpp_max_key<0x111>(k);  // row_shr:1
+  k = dpp_max_key<0x112>(k);  // row_shr:2
+  k = dpp_max_key<0x114>(k);  // row_shr:4
+  k = dpp_max_key<0x118>(k);  // row_shr:8
+  k = dpp_max_key<0x142>(k);  // row_bcast:15
+  k = dpp_max_key<0x143>(k);  // row_bcast:31
+  const unsigned lo = __builtin_amdgcn_readlane(static_cast<unsigned>(k), 63);
+  const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(k >> 32), 63);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __uint_as_float(dpp_u32<CTRL>(__float_as_uint(x)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = dpp_add<0x111>(x);
+  x = dpp_add<0x112>(x);
+  x = dpp_add<0x114>(x);
+  x = dpp_add<0x118>(x);
+  x = dpp_add<0x142>(x);
+  x = dpp_add<0x143>(x);
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 63));
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
-  extern __shared__ float rsm[];  // [rows][E] of W_r, then [T][rows] of x
+  extern __shared__ float rsm[];  // [rows][16] staged x (fp32), then [slices][16][E] sums / [T][E] logits
   const int T = r.T, D = r.D, E = r.E;
   const int tid = threadIdx.x;
-  const int rows = route_rows(T, D, E);
-  const int d0 = blockIdx.x * rows;
-  const int cn = min(D, d0 + rows) - d0;
-  float* wrs = rsm;
-  float* xs = rsm + static_cast<size_t>(rows) * E;
-  const int ntg = (T + kRouteTG - 1) / kRouteTG;
-  const int nitems = E * ntg;
+  const int R = r.rows;  // a multiple of 16 * (row slices)
+  const int d0 = blockIdx.x * R;
+  float* xs = rsm;
+  float* red = rsm + (R * 16 > 4096 ? R * 16 : 4096);  // after the staged-x area (>= 16 KiB)
+  const _Float16* x = reinterpret_cast<const _Float16*>(r.x);
 
-  // stage the block: loads issued 8 at a time per thread, coalesced along E and D
-  {
-    const int nw = cn * E;
-    for (int q0 = tid; q0 < nw; q0 += kRouteThreads * 8) {
+  // Tokens in groups of 16: stage x (zeros past T and past D) as [row][16],
+  // then v_mfma_f32_16x16x4_f32 jobs of 16 experts x a slice of the rows:
+  // lane (c, q) = (lane & 15, lane >> 4) supplies A = x[token c][row 4i + q]
+  // and B = W_r[row 4i + q][expert e0 + c]; its accumulator holds expert
+  // e0 + c of tokens 4q + r.  Slices are summed in LDS in slice order.
+  const int lane = tid & 63, wv = tid >> 6;
+  const int c = lane & 15, kq = lane >> 4;
+  const int cb = (E + 15) / 16;              // 16-expert column blocks
+  const int ns = cb >= 8 ? 1 : 8 / cb;       // row slices per column block
+  const int rps = R / ns;                    // rows per slice (a multiple of 16)
+  for (int t0 = 0; t0 < T; t0 += 16) {
+    const int tn = min(16, T - t0);
+    for (int q0 = 0; q0 < R * 16; q0 += 8 * kRouteThreads) {
       float v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int q = q0 + u * kRouteThreads;
-        v[u] = q < nw ? r.wr[static_cast<size_t>(d0) * E + q] : 0.f;
+        const int q = q0 + u * kRouteThreads + tid;
+        const int dd = q >> 4, t = q & 15;
+        const bool ok = q < R * 16 && t < tn && d0 + dd < D;
+        const float xv = static_cast<float>(x[ok ? static_cast<size_t>(t0 + t) * D + d0 + dd : 0]);
+        v[u] = ok ? xv : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int q = q0 + u * kRouteThreads;
-        if (q < nw) wrs[q] = v[u];
+        const int q = q0 + u * kRouteThreads + tid;
+        if (q < R * 16) xs[q] = v[u];
       }
     }
-    const int nx = T * cn;
-    for (int q0 = tid; q0 < nx; q0 += kRouteThreads * 8) {
-      float v[8];
+    __syncthreads();
+    for (int job = wv; job < cb * ns; job += kRouteThreads / 64) {
+      const int cbk = job % cb, sl = job / cb;
+      const int e0 = cbk * 16;
+      const float* wcol = r.wr + min(e0 + c, E - 1);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i0 = sl * rps; i0 < (sl + 1) * rps; i0 += 16) {
+        float av[4], bv[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = q0 + u * kRouteThreads;
-        const int t = q / max(cn, 1), dd = q - t * cn;
-        v[u] = q < nx ? (float)reinterpret_cast<const _Float16*>(r.x)[static_cast<size_t>(t) * D + d0 + dd] : 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const int dd = i0 + 4 * j + kq;
+          av[j] = xs[dd * 16 + c];
+          bv[j] = wcol[static_cast<size_t>(min(d0 + dd, D - 1)) * E];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc, 0, 0, 0);
       }
+      if (e0 + c < E) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = q0 + u * kRouteThreads;
-        if (q < nx) xs[q] = v[u];
-      }
-    }
-  }
-  __syncthreads();
-  for (int item = tid; item < nitems; item += kRouteThreads) {
-    const int e = item % E, tg = item / E;
-    float acc[kRouteTG];
-#pragma unroll
-    for (int t = 0; t < kRouteTG; ++t) acc[t] = 0.f;
-    for (int dd = 0; dd < cn; ++dd) {
-      const float w = wrs[dd * E + e];
-#pragma unroll
-      for (int t = 0; t < kRouteTG; ++t) {
-        const int tt = tg * kRouteTG + t;
-        if (tt < T) acc[t] = fmaf(xs[tt * cn + dd], w, acc[t]);
+        for (int rr = 0; rr < 4; ++rr) red[(sl * 16 + 4 * kq + rr) * E + e0 + c] = acc[rr];
       }
     }
-#pragma unroll
-    for (int t = 0; t < kRouteTG; ++t) {
-      const int tt = tg * kRouteTG + t;
-      if (tt < T) store_coherent(r.partial + (static_cast<size_t>(blockIdx.x) * T + tt) * E + e, acc[t]);
+    __syncthreads();
+    for (int q = tid; q < tn * E; q += kRouteThreads) {
+      const int t = q / E, ee = q - t * E;
+      float sum = 0.f;
+      for (int j = 0; j < ns; ++j) sum += red[(j * 16 + t) * E + ee];
+      store_coherent(r.partial + (static_cast<size_t>(blockIdx.x) * T + t0 + t) * E + ee, sum);
     }
+    __syncthreads();  // xs and red are reused
   }
   wait_stores();  // this wave's partials are at the coherence point
   __syncthreads();
@@ -106,77 +168,75 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
   __syncthreads();
   if (!s_last) return;
 
-  // last workgroup: every block's partial of an item is loaded at once, then
-  // summed in block order; then softmax and top-k per token
-  float* lg = rsm;  // reuse: [T][E]
+  // last workgroup: the blocks' partials of 4 items per thread are loaded at
+  // once, then summed in block order
+  float* lg = red;  // reuse: [T][E]
   const int nb = gridDim.x;
-  for (int q = tid; q < T * E; q += kRouteThreads) {
-    float v[kRouteMaxBlocks];
+  for (int q0 = 0; q0 < T * E; q0 += 4 * kRouteThreads) {
+    float v[4][kRouteMaxBlocks];
 #pragma unroll
-    for (int b = 0; b < kRouteMaxBlocks; ++b)
-      v[b] = b < nb ? load_coherent(r.partial + static_cast<size_t>(b) * T * E + q) : 0.f;
-    float s = 0.f;
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * kRouteThreads + tid;
 #pragma unroll
-    for (int b = 0; b < kRouteMaxBlocks; ++b) s += v[b];
-    lg[q] = s;
-    if (r.logits) r.logits[q] = s;
+      for (int b = 0; b < kRouteMaxBlocks; ++b)
+        v[u][b] = (b < nb && q < T * E) ? load_coherent(r.partial + static_cast<size_t>(b) * T * E + q) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * kRouteThreads + tid;
+      float sum = 0.f;
+#pragma unroll
+      for (int b = 0; b < kRouteMaxBlocks; ++b) sum += v[u][b];
+      if (q < T * E) {
+        lg[q] = sum;
+        if (r.logits) r.logits[q] = sum;
+      }
+    }
   }
   __syncthreads();
-  const int lane = tid & 63, wv = tid >> 6;
+
+  // Per token (one wave; lane l holds experts l + 64 j): k rounds of a
+  // wave-wide maximum of the not-yet-chosen keys (keys are distinct, so each
+  // round picks exactly one expert, in decreasing order, ties to the lower
+  // index); softmax over all E with the first choice as the maximum.
   for (int t = wv; t < T; t += kRouteThreads / 64) {
     const float* l = lg + static_cast<size_t>(t) * E;
     float v[4];
-    bool taken[4];
-    float mx = -INFINITY;
+    unsigned long long key[4];
+    int slot[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      v[j] = e < E ? l[e] : -INFINITY;
-      taken[j] = e >= E;
-      mx = fmaxf(mx, v[j]);
+      const int ee = lane + 64 * j;
+      v[j] = ee < E ? l[ee] : -INFINITY;
+      key[j] = ee < E ? route_key(v[j], ee) : 0ull;
+      slot[j] = -1;
     }
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    float se = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) se += (lane + 64 * j < E) ? expf(v[j] - mx) : 0.f;
-    for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
-    float wsel[16];
-    int isel[16];
-    float wsum = 0.f;
+    unsigned long long first = 0ull;
     for (int s = 0; s < r.k; ++s) {
-      // best (largest value, then lowest index) among the not-yet-chosen
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
+      unsigned long long mine = 0ull;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        if (!taken[j] && (v[j] > bv || (v[j] == bv && e < bi))) {
-          bv = v[j];
-          bi = e;
-        }
-      }
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
+      for (int j = 0; j < 4; ++j) mine = (slot[j] < 0 && key[j] > mine) ? key[j] : mine;
+      const unsigned long long best = wave_max_key(mine);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (lane + 64 * j == bi) taken[j] = true;
-      const float p = expf(bv - mx) / se;
-      if (s < 16) {
-        wsel[s] = p;
-        isel[s] = bi;
-      }
-      wsum += p;
+      for (int j = 0; j < 4; ++j) slot[j] = key[j] == best ? s : slot[j];
+      if (s == 0) first = best;
     }
-    if (lane == 0) {
-      for (int s = 0; s < r.k && s < 16; ++s) {
-        r.idx[t * r.k + s] = isel[s];
-        r.w[t * r.k + s] = r.renormalize ? wsel[s] / wsum : wsel[s];
+    const float mx = route_key_value(first);
+    float se = 0.f, ws = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = lane + 64 * j < E ? expf(v[j] - mx) : 0.f;
+      se += p;
+      ws += slot[j] >= 0 ? p : 0.f;
+    }
+    se = wave_sum(se);
+    ws = wave_sum(ws);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (slot[j] >= 0) {
+        const float p = expf(v[j] - mx) / se;
+        r.idx[t * r.k + slot[j]] = lane + 64 * j;
+        r.w[t * r.k + slot[j]] = r.renormalize ? p / (ws / se) : p;
       }
     }
   }
@@ -418,7 +478,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
 
 int launch_route(const RouteArgs& r, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t need = route_lds_bytes(r.T, r.D, r.E);
+  const size_t need = route_lds_bytes(r.D, r.E);
   static size_t lds_allowed = 48 * 1024;
   if (need > lds_allowed) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel),

@@ -333,13 +333,26 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   const int F = ng * KRf;
   using St = StreamStage<FMT, P, ALDS>;
 
+  // Global activations: a full tile lies entirely below K (callers of this
+  // mode have K % 64 == 0), so its loads are unconditional (exact waits); a
+  // lane's row pointer is always a valid row, and rows the lane does not own
+  // only feed output rows that are never stored.  The half tile's k >= K
+  // half is read at k 0 and zeroed.
   auto load_a = [&](St& st, int tg) {
     if constexpr (!ALDS) {
       const int kb = tg * kTileK;
 #pragma unroll
+      for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(arow + kb + 32 * i + 8 * o);
+    }
+  };
+  auto load_a_half = [&](St& st) {
+    if constexpr (!ALDS) {
+      const int kb = half_t * kTileK;
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k0 = kb + 32 * i + 8 * o;
-        st.a[i] = (arow_ok && k0 < K) ? *reinterpret_cast<const u32x4*>(arow + k0) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 v = *reinterpret_cast<const u32x4*>(arow + (k0 < K ? k0 : 0));
+        st.a[i] = (arow_ok && k0 < K) ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -357,7 +370,7 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
     }
   };
   auto load_half = [&](St& st, int g) {
-    load_a(st, half_t);
+    load_a_half(st);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint8_t* tb = gbase(g, p) + static_cast<size_t>(half_t) * kTileBytes;
