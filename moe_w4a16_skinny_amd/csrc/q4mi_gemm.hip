@@ -131,10 +131,14 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
 
   if (threadIdx.x < 16) sbest[threadIdx.x] = 0ull;
 
-  auto gbase = [&](int gi, int p) -> const uint8_t* {
-    int panel = p0 + (pw + gi * PWv) * P + p;
-    panel = panel < kp.npanels ? panel : kp.npanels - 1;   // in-bounds load, result dropped
-    return g.w + static_cast<size_t>(panel) * static_cast<size_t>(g.panel_bytes);
+  auto group = [&](int gi, GroupPtrs<P>& gp) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      int panel = p0 + (pw + gi * PWv) * P + p;
+      panel = panel < kp.npanels ? panel : kp.npanels - 1;  // in-bounds load, result dropped
+      gp.panel[p] = g.w + static_cast<size_t>(panel) * static_cast<size_t>(g.panel_bytes);
+    }
+    gp.arow = nullptr;
   };
   const StageGeom sg = stage_geom(g.a, M, g.K, kt0, KRg);
   auto pre_issue = [&]() { stage_issue(sg, lds); };
@@ -143,8 +147,7 @@ __global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
   auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash_rows<P, false>(wres, rs, col_of(gi), M, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_rows<P, true>(wres, rs, col_of(gi), M, acc); };
   const ALds al = alds_view(reinterpret_cast<const char*>(lds), KRg, M, wt0);
-  stream_groups<FMT, P, D, true>(ng, wtn, kt0 + wt0, kp.half_t, al, nullptr, false, g.K, gbase, pre_issue, pre, epi,
-                                 epi_add);
+  stream_groups<FMT, P, D, true>(ng, wtn, kt0 + wt0, kp.half_t, al, g.K, group, pre_issue, pre, epi, epi_add);
   if (wtn == 0) {  // a k-split wave without tiles still owns zero partials
     f32x4 z[P][2];
 #pragma unroll

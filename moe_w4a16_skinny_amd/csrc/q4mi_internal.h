@@ -143,6 +143,7 @@ struct MoeArgs {
   int out_dtype;
   uint16_t* h;             // workspace f16 [npairs][F]
   float* o;                // workspace fp32 [npairs][D]
+  int32_t* rowof;          // workspace [T * k]: pair -> scratch row (-1: none)
 };
 int launch_moe(const MoeArgs& m, void* stream);
 

@@ -245,54 +245,144 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
 
 // ------------------------------------------------------------------ grouping
 
-// (token, slot) pairs routed to expert e, in token-major order, plus the
-// number of valid pairs routed to lower experts (the expert's first row in
-// the expert-sorted scratch).  Run by wave 0; results in LDS.  Indices
-// outside 0..E-1 are dropped; pairs past the 16th of one expert (possible
-// only when a token names the same expert twice) are dropped too.
-__device__ void group_expert(const int32_t* idx, int T, int k, int E, int e, int* s_tok, int* s_slot,
-                             int* s_meta) {
-  const int lane = threadIdx.x & 63;
-  if (e >= E) {  // the shared expert: every token, after all routed pairs
-    if (lane < T) {
-      s_tok[lane] = lane;
-      s_slot[lane] = -1;
-    }
-    if (lane == 0) {
-      s_meta[0] = T;
-      s_meta[1] = T * k;
-    }
-    return;
+// The expert-sorted scratch: routed (token, slot) pairs with a valid expert
+// index, by expert, then token-major (t k + s) order inside an expert; then,
+// with a shared expert, one row per token at T k + t.  At most 16 rows of an
+// expert are computed (more only when a token names one expert twice); the
+// rest are dropped, here and in the combine.  Every GEMM workgroup builds
+// the table in LDS from topk_idx on its own (a few microseconds, no launch
+// and no handoff between workgroups).
+constexpr int kMoeMaxE = 1024;
+constexpr int kMoeMaxPairs = 16 * 64;
+struct MoeGroups {
+  int cnt[kMoeMaxE + 1];       // valid pairs per expert (shared expert: T)
+  int base[kMoeMaxE + 1];      // first scratch row of each expert
+  unsigned tmask[kMoeMaxE];    // tokens (bit t) routed to each expert
+  int act[kMoeMaxE + 1];       // experts with pairs, increasing
+  int nact;
+  int dup;                     // some token names one expert twice
+  int idx[kMoeMaxPairs];
+  int rowof[kMoeMaxPairs];     // pair t k + s -> scratch row (-1: invalid index or dropped)
+  short tok[kMoeMaxPairs + 16];   // scratch row -> token
+  short slot[kMoeMaxPairs + 16];  // scratch row -> slot (-1: shared expert)
+};
+
+__device__ void build_groups(const MoeArgs& m, MoeGroups& G) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int E = m.E, k = m.k, n = m.T * k;
+  for (int e = tid; e <= E; e += nt) {
+    G.cnt[e] = 0;
+    if (e < E) G.tmask[e] = 0u;
   }
-  int cnt = 0, below = 0;
-  const int n = T * k;  // <= 16 * 64: at most 16 indices per lane, all loaded at once
-  int v[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int j = u * 64 + lane;
-    v[u] = j < n ? idx[j] : -1;
+  if (tid == 0) G.dup = 0;
+  for (int q = tid; q < n; q += nt) {
+    const int e = m.idx[q];
+    G.idx[q] = (e >= 0 && e < E) ? e : -1;
   }
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    if (u * 64 >= n) break;
-    const int j = u * 64 + lane;
-    const bool valid = v[u] >= 0 && v[u] < E;
-    const unsigned long long eq = __ballot(valid && v[u] == e);
-    const unsigned long long lt = __ballot(valid && v[u] < e);
-    if (valid && v[u] == e) {
-      const int rk = cnt + __popcll(eq & ((1ull << lane) - 1ull));
-      if (rk < 16) {
-        s_tok[rk] = j / k;
-        s_slot[rk] = j % k;
+  __syncthreads();
+  for (int q = tid; q < n; q += nt) {
+    const int e = G.idx[q];
+    if (e < 0) continue;
+    const int t = q / k, s0 = t * k;
+    atomicAdd(&G.cnt[e], 1);
+    atomicOr(&G.tmask[e], 1u << t);
+    for (int j = s0; j < q; ++j)
+      if (G.idx[j] == e) G.dup = 1;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    // exclusive scans of the counts (row bases) and of the active flags, lane l
+    // owning experts [l per, (l + 1) per)
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int sc = 0, sa = 0;
+    for (int j = 0; j < per; ++j) {
+      const int e = e0 + j;
+      if (e < E) {
+        sc += G.cnt[e];
+        sa += G.cnt[e] > 0 ? 1 : 0;
       }
     }
-    cnt += __popcll(eq);
-    below += __popcll(lt);
+    int xc = sc, xa = sa;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int yc = __shfl_up(xc, off), ya = __shfl_up(xa, off);
+      if (lane >= off) {
+        xc += yc;
+        xa += ya;
+      }
+    }
+    xc -= sc;
+    xa -= sa;
+    for (int j = 0; j < per; ++j) {
+      const int e = e0 + j;
+      if (e < E) {
+        G.base[e] = xc;
+        xc += G.cnt[e];
+        if (G.cnt[e] > 0) G.act[xa++] = e;
+      }
+    }
+    if (lane == 63) {
+      int na = xa;
+      if (m.has_shared) {
+        G.cnt[E] = m.T;
+        G.base[E] = n;
+        G.act[na++] = E;
+      }
+      G.nact = na;
+    }
   }
-  if (lane == 0) {
-    s_meta[0] = min(cnt, 16);
-    s_meta[1] = below;
+  __syncthreads();
+  // Row of pair (t, s) = base[e] + rank, the rank counting the expert's
+  // pairs of lower tokens (token-major order): the popcount of its token
+  // mask below bit t.  Tokens that name one expert twice break that count;
+  // then wave 0 ranks the pairs 64 at a time instead (earlier lanes with the
+  // same expert, broadcast through scalar registers, plus earlier chunks).
+  if (!G.dup) {
+    for (int q = tid; q < n; q += nt) {
+      const int e = G.idx[q];
+      int row = -1;
+      if (e >= 0) {
+        const int t = q / k;
+        const int rank = __popc(G.tmask[e] & ((1u << t) - 1u));
+        if (rank < 16) {
+          row = G.base[e] + rank;
+          G.tok[row] = static_cast<short>(t);
+          G.slot[row] = static_cast<short>(q - t * k);
+        }
+      }
+      G.rowof[q] = row;
+    }
+  } else if (tid < 64) {
+    const int lane = tid;
+    for (int q0 = 0; q0 < n; q0 += 64) {
+      const int q = q0 + lane;
+      const int e = q < n ? G.idx[q] : -1;
+      int below = 0;
+      for (int l = 0; l < 64; ++l) {
+        const int el = __builtin_amdgcn_readlane(e, l);
+        below += (el == e && l < lane) ? 1 : 0;
+      }
+      int earlier = 0;  // same-expert pairs in earlier chunks
+      for (int j = 0; j < q0; ++j) earlier += (G.idx[j] == e) ? 1 : 0;
+      int row = -1;
+      if (e >= 0) {
+        const int rank = earlier + below;
+        if (rank < 16) {
+          row = G.base[e] + rank;
+          G.tok[row] = static_cast<short>(q / k);
+          G.slot[row] = static_cast<short>(q - (q / k) * k);
+        }
+      }
+      if (q < n) G.rowof[q] = row;
+    }
   }
+  if (m.has_shared)
+    for (int t = tid; t < m.T; t += nt) {
+      G.tok[n + t] = static_cast<short>(t);
+      G.slot[n + t] = -1;
+    }
+  __syncthreads();
 }
 
 __device__ __forceinline__ float gelu_tanh(float u) {
@@ -300,53 +390,61 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   return 0.5f * u * (1.0f + tanhf(z));
 }
 
+// Work items are dealt round-robin over every wave of the grid: wave gw of NW
+// takes items gw, gw + NW, ...; its g-th item is gw + g NW.
+__device__ __forceinline__ int items_of_wave(int nitems, int gw, int NW) {
+  return gw < nitems ? (nitems - gw + NW - 1) / NW : 0;
+}
+
 // ------------------------------------------------------------------ gate/up
 
-// Grid (panel-pair blocks, experts).  A workgroup owns PPB consecutive panel
-// pairs of its expert; wave w streams pairs w, w + W, ... (gate panel j and
-// up panel j together, P = 2) over all of K = D with D tiles in flight.
+// Item (active expert a, panel pair j): gate panel j and up panel j of the
+// expert streamed together over K = D (P = 2), h = gelu_tanh(g_gate acc_g) *
+// (g_up acc_u) for the expert's rows, written as f16 to the scratch row.
 template <int W, int DP>
-__global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int PPB) {
-  const int e = blockIdx.y;
-  __shared__ int s_tok[16], s_slot[16], s_meta[2];
-  if (threadIdx.x < 64) group_expert(m.idx, m.T, m.k, m.E, e, s_tok, s_slot, s_meta);
-  __syncthreads();
-  const int me = s_meta[0];
-  if (me == 0) return;
-  const int base = s_meta[1];
-
+__global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW) {
+  __shared__ MoeGroups G;
+  build_groups(m, G);
+  if (blockIdx.x == 0)  // the pair -> row map, for the combine
+    for (int q = threadIdx.x; q < m.T * m.k; q += blockDim.x) m.rowof[q] = G.rowof[q];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = lane >> 4, c = lane & 15;
-  const int npp = m.F / 16;                        // panel pairs of the expert
-  const int j0 = blockIdx.x * PPB;
-  const int jend = min(npp, j0 + PPB);
-  const int ngb = jend - j0;
-  const int ng = ngb > w ? (ngb - w + W - 1) / W : 0;
-  const uint8_t* gate_e = m.gate + static_cast<size_t>(e) * m.gate_stride;
-  const uint8_t* up_e = m.up + static_cast<size_t>(e) * m.gate_stride;
-  const bool arow_ok = c < me;
-  const uint16_t* arow = m.x + static_cast<size_t>(arow_ok ? s_tok[c] : 0) * m.D;
+  const int npp = m.F / 16;
+  const int nitems = G.nact * npp;
+  const int gw = blockIdx.x * W + w, NW = gridDim.x * W;
+  const int ng = min(items_of_wave(nitems, gw, NW), NGW);
   const int nfull = static_cast<int>(full_tiles(m.D));
   const bool half = has_half_tile(m.D);
-  const float gg = m.g_gate[e], gu = m.g_up[e];
 
-  auto gbase = [&](int gi, int p) -> const uint8_t* {
-    int jp = j0 + w + gi * W;
-    jp = jp < npp ? jp : npp - 1;
-    return (p == 0 ? gate_e : up_e) + static_cast<size_t>(jp) * m.gate_panel_bytes;
+  auto item = [&](int gi, int& e, int& jp) {
+    int it = gw + gi * NW;
+    it = it < nitems ? it : nitems - 1;  // past the wave's items: in-bounds, never computed
+    const int a = it / npp;
+    jp = it - a * npp;
+    e = G.act[a];
+  };
+  auto group = [&](int gi, GroupPtrs<2>& gp) {
+    int e, jp;
+    item(gi, e, jp);
+    gp.panel[0] = m.gate + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jp) * m.gate_panel_bytes;
+    gp.panel[1] = m.up + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jp) * m.gate_panel_bytes;
+    const int me = min(G.cnt[e], 16);
+    gp.arow = m.x + static_cast<size_t>(G.tok[G.base[e] + min(c, me - 1)]) * m.D;
   };
   extern __shared__ f32x4 gu_out[];  // [W][NGW][2 panels][64 lanes]
-  const int NGW = (PPB + W - 1) / W;
   f32x4* wout = gu_out + static_cast<size_t>(w) * NGW * 2 * 64;
   auto pre = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[2][2]) { stash<2>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[2][2]) { stash_add<2>(wout, gi, acc); };
-  stream_groups<kNvfp4, 2, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, arow, arow_ok,
-                                      m.D, gbase, pre, pre, epi, epi_add);
+  if (nitems > 0)
+    stream_groups<kNvfp4, 2, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, m.D, group, pre,
+                                        pre, epi, epi_add);
   for (int gi = 0; gi < ng; ++gi) {
-    const int jp = j0 + w + gi * W;
-    if (jp >= jend) continue;
+    int e, jp;
+    item(gi, e, jp);
+    const int me = min(G.cnt[e], 16), base = G.base[e];
+    const float gg = m.g_gate[e], gu = m.g_up[e];
     const f32x4 rg = wout[(gi * 2 + 0) * 64 + lane], ru = wout[(gi * 2 + 1) * 64 + lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -361,64 +459,68 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int PPB)
 
 // ------------------------------------------------------------------ down
 
-// Grid (panel blocks, experts): PB panels of W_down (N = D) per workgroup,
-// groups of P panels per wave, K = F; the activation rows are the expert's
-// contiguous h rows.  o[pair][n] = w_pair * g_down * acc.
+// Item (active expert a, group q of P panels of W_down, N = D): K = F, the
+// activation rows are the expert's contiguous h rows; o[row][n] = w_pair *
+// g_down * acc in fp32.
 template <int P, int W, int DP>
-__global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int PB) {
-  const int e = blockIdx.y;
-  __shared__ int s_tok[16], s_slot[16], s_meta[2];
-  if (threadIdx.x < 64) group_expert(m.idx, m.T, m.k, m.E, e, s_tok, s_slot, s_meta);
-  __syncthreads();
-  const int me = s_meta[0];
-  if (me == 0) return;
-  const int base = s_meta[1];
-
+__global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
+  __shared__ MoeGroups G;
+  build_groups(m, G);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = lane >> 4, c = lane & 15;
   const int npan = m.D / 16;
-  const int p0 = blockIdx.x * PB;
-  const int pend = min(npan, p0 + PB);
-  const int ngb = (pend - p0 + P - 1) / P;
-  const int ng = ngb > w ? (ngb - w + W - 1) / W : 0;
-  const uint8_t* down_e = m.down + static_cast<size_t>(e) * m.down_stride;
-  const bool arow_ok = c < me;
-  const uint16_t* arow = m.h + static_cast<size_t>(base + (arow_ok ? c : 0)) * m.F;
+  const int ngp = (npan + P - 1) / P;  // panel groups per expert
+  const int nitems = G.nact * ngp;
+  const int gw = blockIdx.x * W + w, NW = gridDim.x * W;
+  const int ng = min(items_of_wave(nitems, gw, NW), NGW);
   const int nfull = static_cast<int>(full_tiles(m.F));
   const bool half = has_half_tile(m.F);
-  const float gd = m.g_down[e];
-  float wrow[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * o + r;
-    wrow[r] = 0.f;
-    if (row < me) wrow[r] = s_slot[row] < 0 ? 1.0f : m.tw[s_tok[row] * m.k + s_slot[row]];
-  }
 
-  auto gbase = [&](int gi, int p) -> const uint8_t* {
-    int pi = p0 + (w + gi * W) * P + p;
-    pi = pi < npan ? pi : npan - 1;
-    return down_e + static_cast<size_t>(pi) * m.down_panel_bytes;
+  auto item = [&](int gi, int& e, int& q) {
+    int it = gw + gi * NW;
+    it = it < nitems ? it : nitems - 1;
+    const int a = it / ngp;
+    q = it - a * ngp;
+    e = G.act[a];
+  };
+  auto group = [&](int gi, GroupPtrs<P>& gp) {
+    int e, q;
+    item(gi, e, q);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int pi = min(q * P + p, npan - 1);
+      gp.panel[p] = m.down + static_cast<size_t>(e) * m.down_stride + static_cast<size_t>(pi) * m.down_panel_bytes;
+    }
+    const int me = min(G.cnt[e], 16);
+    gp.arow = m.h + static_cast<size_t>(G.base[e] + min(c, me - 1)) * m.F;
   };
   extern __shared__ f32x4 dn_out[];  // [W][NGW][P][64]
-  const int NGW = ((PB + P - 1) / P + W - 1) / W;
   f32x4* wout = dn_out + static_cast<size_t>(w) * NGW * P * 64;
   auto pre = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash<P>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
-  stream_groups<kNvfp4, P, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, arow, arow_ok,
-                                      m.F, gbase, pre, pre, epi, epi_add);
+  if (nitems > 0)
+    stream_groups<kNvfp4, P, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, m.F, group, pre,
+                                        pre, epi, epi_add);
   for (int gi = 0; gi < ng; ++gi) {
+    int e, q;
+    item(gi, e, q);
+    const int me = min(G.cnt[e], 16), base = G.base[e];
+    const float gd = m.g_down[e];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int pi = p0 + (w + gi * W) * P + p;
-      if (pi >= pend) continue;
+      const int pi = q * P + p;
+      if (pi >= npan) continue;
       const f32x4 v = wout[(gi * P + p) * 64 + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * o + r;
-        if (row < me) m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wrow[r] * (gd * v[r]);
+        if (row < me) {
+          const int sl = G.slot[base + row];
+          const float wp = sl < 0 ? 1.0f : m.tw[G.tok[base + row] * m.k + sl];
+          m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wp * (gd * v[r]);
+        }
       }
     }
   }
@@ -432,36 +534,15 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int PB) {
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
   const int t = blockIdx.x;
   const int n = blockIdx.y * 256 + threadIdx.x;
-  __shared__ int s_idx[16 * 64];
-  __shared__ int s_pos[64];
-  const int nall = m.T * m.k;
-  for (int j = threadIdx.x; j < nall; j += 256) s_idx[j] = m.idx[j];
-  __syncthreads();
-  for (int s = threadIdx.x; s < m.k; s += 256) {
-    const int e = s_idx[t * m.k + s];
-    int pos = -1;
-    if (e >= 0 && e < m.E) {
-      int below = 0, rank = 0;
-      for (int j = 0; j < nall; ++j) {
-        const int v = s_idx[j];
-        if (v >= 0 && v < m.E) {
-          below += v < e;
-          rank += (v == e) && (j < t * m.k + s);
-        }
-      }
-      pos = rank < 16 ? below + rank : -1;
-    }
-    s_pos[s] = pos;
-  }
-  __syncthreads();
   if (n >= m.D) return;
+  const int nall = m.T * m.k;
   float acc = 0.f;
   for (int s0 = 0; s0 < m.k; s0 += 16) {  // 16 slots' rows in flight, summed in slot order
     float v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int s = s0 + u;
-      const int pos = s < m.k ? s_pos[s] : -1;
+      const int pos = s < m.k ? m.rowof[t * m.k + s] : -1;
       v[u] = pos >= 0 ? m.o[static_cast<size_t>(pos) * m.D + n] : 0.f;
     }
 #pragma unroll
@@ -496,18 +577,35 @@ int launch_route(const RouteArgs& r, void* stream) {
 int launch_moe(const MoeArgs& m, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nexp = m.E + m.has_shared;
-  constexpr int GU_W = 4, DN_P = 2, DN_W = 4;
+  constexpr int GU_W = 4, DN_P = 2, DN_W = 4, kWG = 512;  // two 4-wave workgroups per CU
+  const int NW = kWG * 4;
   const int npp = m.F / 16;
-  const int ppb = 2 * GU_W;  // panel pairs per gate/up workgroup: 2 per wave
-  const size_t gu_lds = static_cast<size_t>(GU_W) * ((ppb + GU_W - 1) / GU_W) * 2 * 64 * 16;
-  hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4>), dim3((npp + ppb - 1) / ppb, nexp), dim3(64 * GU_W), gu_lds, s,
-                     m, ppb);
+  const int gu_ngw = (nexp * npp + NW - 1) / NW;  // items per wave at most
+  const size_t gu_lds = static_cast<size_t>(GU_W) * gu_ngw * 2 * 64 * 16;
+  const int ngp = (m.D / 16 + DN_P - 1) / DN_P;
+  const int dn_ngw = (nexp * ngp + NW - 1) / NW;
+  const size_t dn_lds = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
+  if (gu_lds > 96 * 1024 || dn_lds > 96 * 1024) return static_cast<int>(hipErrorInvalidConfiguration);
+  static size_t gu_allowed = 48 * 1024, dn_allowed = 48 * 1024;
+  if (gu_lds > gu_allowed) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(gu_lds)) != hipSuccess) {
+      (void)hipGetLastError();
+      return static_cast<int>(hipErrorInvalidConfiguration);
+    }
+    gu_allowed = gu_lds;
+  }
+  if (dn_lds > dn_allowed) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dn_lds)) != hipSuccess) {
+      (void)hipGetLastError();
+      return static_cast<int>(hipErrorInvalidConfiguration);
+    }
+    dn_allowed = dn_lds;
+  }
+  hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m, gu_ngw);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
-  const int npan = m.D / 16;
-  const int pb = 2 * DN_P * DN_W;  // panels per down workgroup: 2 groups per wave
-  const size_t dn_lds = static_cast<size_t>(DN_W) * (((pb + DN_P - 1) / DN_P + DN_W - 1) / DN_W) * DN_P * 64 * 16;
-  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3((npan + pb - 1) / pb, nexp), dim3(64 * DN_W), dn_lds, s,
-                     m, pb);
+  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
   hipLaunchKernelGGL(moe_combine_kernel, dim3(m.T, (m.D + 255) / 256), dim3(256), 0, s, m);
   return static_cast<int>(hipGetLastError());

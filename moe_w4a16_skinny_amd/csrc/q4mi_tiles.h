@@ -307,24 +307,34 @@ __device__ __forceinline__ void stage_wait() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Where group g's data lives: the packed base of each of its P panels and,
+// when the activations come from global memory, this lane's activation row
+// (a valid row for every lane; rows a lane does not own only feed output rows
+// that are never stored).
+template <int P>
+struct GroupPtrs {
+  const uint8_t* panel[P];
+  const uint16_t* arow;
+};
+
 // Stream ng groups of P panels over the tiles [kt0, kt0 + KRg) of each group
 // (global packed tile indices; if half_t falls in that range it must be the
 // range's last tile, the 576-byte half tile), keeping D tiles of weight loads
-// in flight across group boundaries.  gbase(g, p): packed base of panel p of
-// the wave's g-th group; it must return an in-bounds panel for any g >= 0
-// (the prologue loads D tiles even when the wave has fewer).  After the last
-// tile of group g, epi(g, acc) consumes the accumulators (it must not touch
-// global memory: stores inside the loop would make the compiler's wait
-// counting degenerate), which restart at zero; the half tile of every group
-// is added afterwards through epi_add(g, acc).  pre_issue() runs before the
-// first weight loads and pre() after them (the workgroup stages its
-// activations across the two, so both travel in the same round trip; every
-// wave must reach pre()).  All arguments except the lane-dependent A source
-// are wave-uniform.
-template <int FMT, int P, int D, bool ALDS, class GBase, class PreIssue, class Pre, class Epi, class EpiAdd>
-__device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, ALds al, const uint16_t* arow,
-                                              bool arow_ok, int K, GBase gbase, PreIssue pre_issue, Pre pre, Epi epi,
-                                              EpiAdd epi_add) {
+// in flight across group boundaries.  group(g, ptrs) fills group g's
+// pointers; it is called when the load cursor enters a group and must give
+// in-bounds pointers for any g >= 0 (the prologue loads D tiles even when the
+// wave has fewer).  After the last tile of group g, epi(g, acc) consumes the
+// accumulators (it must not touch global memory: stores inside the loop
+// would make the compiler's wait counting degenerate), which restart at zero;
+// the half tile of every group is added afterwards through epi_add(g, acc).
+// pre_issue() runs before the first weight loads and pre() after them (the
+// workgroup stages its activations across the two, so both travel in the
+// same round trip; every wave must reach pre()).  K is the activations' row
+// length (global mode: a multiple of 64).  All arguments except the
+// lane-dependent pointers are wave-uniform.
+template <int FMT, int P, int D, bool ALDS, class Group, class PreIssue, class Pre, class Epi, class EpiAdd>
+__device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, ALds al, int K, Group group,
+                                              PreIssue pre_issue, Pre pre, Epi epi, EpiAdd epi_add) {
   const int lane = threadIdx.x & 63;
   const int o = lane >> 4;
   const int c = lane & 15;
@@ -333,35 +343,33 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   const int F = ng * KRf;
   using St = StreamStage<FMT, P, ALDS>;
 
-  // Global activations: a full tile lies entirely below K (callers of this
-  // mode have K % 64 == 0), so its loads are unconditional (exact waits); a
-  // lane's row pointer is always a valid row, and rows the lane does not own
-  // only feed output rows that are never stored.  The half tile's k >= K
-  // half is read at k 0 and zeroed.
-  auto load_a = [&](St& st, int tg) {
+  // Global activations: a full tile lies entirely below K, so its loads are
+  // unconditional (exact waits).  The half tile's k >= K half is read at k 0
+  // and zeroed.
+  auto load_a = [&](St& st, const GroupPtrs<P>& gp, int tg) {
     if constexpr (!ALDS) {
       const int kb = tg * kTileK;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(arow + kb + 32 * i + 8 * o);
+      for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(gp.arow + kb + 32 * i + 8 * o);
     }
   };
-  auto load_a_half = [&](St& st) {
+  auto load_a_half = [&](St& st, const GroupPtrs<P>& gp) {
     if constexpr (!ALDS) {
       const int kb = half_t * kTileK;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k0 = kb + 32 * i + 8 * o;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(arow + (k0 < K ? k0 : 0));
-        st.a[i] = (arow_ok && k0 < K) ? v : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 v = *reinterpret_cast<const u32x4*>(gp.arow + (k0 < K ? k0 : 0));
+        st.a[i] = k0 < K ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto load = [&](St& st, int g, int t) {
+  auto load = [&](St& st, const GroupPtrs<P>& gp, int t) {
     const int tg = kt0 + t;
-    load_a(st, tg);
+    load_a(st, gp, tg);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const uint8_t* tb = gbase(g, p) + static_cast<size_t>(tg) * kTileBytes;
+      const uint8_t* tb = gp.panel[p] + static_cast<size_t>(tg) * kTileBytes;
       st.c[p] = ld_nt16(tb + lane * 16);
       if constexpr (FMT == kNvfp4)
         st.s[p] = ld_nt4(tb + kTileCodeBytes + (c * 2 + (lane >> 5)) * 4);
@@ -369,11 +377,11 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
         st.s[p] = ld_nt8(tb + kTileCodeBytes + c * 8);
     }
   };
-  auto load_half = [&](St& st, int g) {
-    load_a_half(st);
+  auto load_half = [&](St& st, const GroupPtrs<P>& gp) {
+    load_a_half(st, gp);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const uint8_t* tb = gbase(g, p) + static_cast<size_t>(half_t) * kTileBytes;
+      const uint8_t* tb = gp.panel[p] + static_cast<size_t>(half_t) * kTileBytes;
       const u32x2 cc = ld_nt8(tb + lane * 8);
       st.c[p] = u32x4{cc.x, cc.y, 0u, 0u};
       if constexpr (FMT == kNvfp4)
@@ -390,12 +398,15 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   St st[D];
   int lg = 0, lt = 0;  // load cursor (group, tile)
   int cg = 0, ct = 0;  // compute cursor
+  GroupPtrs<P> cur;    // the load cursor's group
+  group(0, cur);
   // (>=: a range of only the half tile, KRf == 0, keeps t = 0, the half tile)
   auto load_next = [&](St& x) {
-    load(x, lg, lt);
+    load(x, cur, lt);
     if (++lt >= KRf) {
       lt = 0;
       ++lg;
+      group(lg, cur);
     }
   };
   auto tile_a = [&](const St& x, int t, u32x4 (&a)[4]) {
@@ -463,8 +474,13 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   if (has_half) {
     for (int g0 = 0; g0 < ng; g0 += D) {
 #pragma unroll
-      for (int d = 0; d < D; ++d)
-        if (g0 + d < ng) load_half(st[d], g0 + d);
+      for (int d = 0; d < D; ++d) {
+        if (g0 + d < ng) {
+          GroupPtrs<P> hp;
+          group(g0 + d, hp);
+          load_half(st[d], hp);
+        }
+      }
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         if (g0 + d < ng) {
