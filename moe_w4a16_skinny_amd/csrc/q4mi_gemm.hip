@@ -41,7 +41,7 @@ namespace q4mi {
 namespace {
 using namespace dev;
 
-struct KP2 {
+struct GemmParams {
   GemmArgs g;
   int npanels;
   int ntiles;      // packed tiles per panel, half tile included
@@ -103,7 +103,7 @@ __device__ __forceinline__ unsigned long long max_key_64(unsigned long long k) {
 }
 
 template <int FMT, int P, int W, int D>
-__global__ __launch_bounds__(64 * W) void qgemm2_kernel(KP2 kp) {
+__global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
   // dynamic LDS: staged activations (+ zero row), then KW row-major result blocks [M][rs]
   extern __shared__ u32x4 lds[];
   __shared__ unsigned long long sbest[16];
@@ -313,11 +313,11 @@ __global__ __launch_bounds__(64) void dequant_kernel(const uint8_t* __restrict__
 
 
 template <int FMT, int P, int W, int D>
-int launch_cfg(const KP2& kp, hipStream_t s) {
+int launch_cfg(const GemmParams& kp, hipStream_t s) {
   const size_t lds = gemm_lds_bytes(kp.g.M, kp.KR, kp.KW, kp.PB);
   static size_t lds_allowed = 48 * 1024;  // per instantiation: raise the dynamic LDS limit on demand
   if (lds > lds_allowed) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm2_kernel<FMT, P, W, D>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_kernel<FMT, P, W, D>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the next call
@@ -325,12 +325,12 @@ int launch_cfg(const KP2& kp, hipStream_t s) {
     }
     lds_allowed = lds;
   }
-  hipLaunchKernelGGL((qgemm2_kernel<FMT, P, W, D>), dim3(kp.nblocks * kp.KS), dim3(64 * W), lds, s, kp);
+  hipLaunchKernelGGL((qgemm_kernel<FMT, P, W, D>), dim3(kp.nblocks * kp.KS), dim3(64 * W), lds, s, kp);
   return static_cast<int>(hipGetLastError());
 }
 
 template <int FMT>
-int launch_fmt(const KP2& kp, const GemmCfg& cfg, hipStream_t s) {
+int launch_fmt(const GemmParams& kp, const GemmCfg& cfg, hipStream_t s) {
 #define Q4_CFG(P_, W_, D_) \
   if (cfg.P == P_ && cfg.W == W_ && cfg.D == D_) return launch_cfg<FMT, P_, W_, D_>(kp, s);
   Q4_CFG(1, 4, 4)
@@ -411,7 +411,7 @@ size_t gemm_workspace(int fmt, int M, int64_t K, int64_t N) {
 }
 
 int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* stream) {
-  KP2 kp{};
+  GemmParams kp{};
   kp.g = g;
   kp.npanels = g.N / 16;
   kp.ntiles = g.nfull + g.half;
