@@ -62,11 +62,11 @@ constexpr size_t kGemmLdsMax = 160 * 1024 - 512;  // dynamic LDS per workgroup (
 
 // LDS bytes of one workgroup: staged activations (+ zero row), then KW row-major
 // result blocks [M][PB * 16 + 4]
-__host__ __device__ inline size_t gemm_res_offset(int M, int KR) {
-  return (static_cast<size_t>(stage_bytes(M, KR)) + 15) / 16 * 16;
+__host__ __device__ inline size_t gemm_res_offset(int M, int KR, bool ring, int W, int D) {
+  return ring ? static_cast<size_t>(W) * D * kRingSlot : (static_cast<size_t>(stage_bytes(M, KR)) + 15) / 16 * 16;
 }
-__host__ __device__ inline size_t gemm_lds_bytes(int M, int KR, int KW, int PB) {
-  return gemm_res_offset(M, KR) + static_cast<size_t>(KW) * M * (PB * 16 + 4) * 4;
+__host__ __device__ inline size_t gemm_lds_bytes(int M, int KR, int KW, int PB, bool ring, int W, int D) {
+  return gemm_res_offset(M, KR, ring, W, D) + static_cast<size_t>(KW) * M * (PB * 16 + 4) * 4;
 }
 
 // output element group (m, n .. n + 3) -> stored values (rounded to the output
@@ -102,9 +102,15 @@ __device__ __forceinline__ unsigned long long max_key_64(unsigned long long k) {
   return k;
 }
 
-template <int FMT, int P, int W, int D>
+// RING: every wave moves its own tiles' activations into an LDS ring
+// together with their weight loads (kARing) instead of the workgroup
+// staging its k-range up front; chosen when each wave streams a single panel
+// group, so that staging would save no re-reads and only hold back the first
+// tile's math until the whole range has landed.
+template <int FMT, int P, int W, int D, bool RING>
 __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
-  // dynamic LDS: staged activations (+ zero row), then KW row-major result blocks [M][rs]
+  // dynamic LDS: staged activations (+ zero row), or with RING the W rings
+  // of D slots; then KW row-major result blocks [M][rs]
   extern __shared__ u32x4 lds[];
   __shared__ unsigned long long sbest[16];
   __shared__ int s_last;
@@ -131,6 +137,14 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
 
   if (threadIdx.x < 16) sbest[threadIdx.x] = 0ull;
 
+  // RING: the row this lane moves for each row group (rows >= M repeat
+  // row M - 1; their outputs are dropped), plus its swizzled chunk
+  const uint16_t* ar[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    ar[j] = RING ? g.a + static_cast<size_t>(min(4 * j + static_cast<int>((threadIdx.x & 63) >> 4), M - 1)) * g.K +
+                       ring_chunk(j)
+                 : nullptr;
   auto group = [&](int gi, GroupPtrs<P>& gp) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -139,15 +153,26 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
       gp.panel[p] = g.w + static_cast<size_t>(panel) * static_cast<size_t>(g.panel_bytes);
     }
     gp.arow = nullptr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gp.ar[j] = ar[j];
   };
   const StageGeom sg = stage_geom(g.a, M, g.K, kt0, KRg);
-  auto pre_issue = [&]() { stage_issue(sg, lds); };
-  auto pre = [&]() { stage_wait<D * P * 2>(); };  // D tiles of P panels: codes + scales
+  auto pre_issue = [&]() {
+    if constexpr (!RING) stage_issue(sg, lds);
+  };
+  auto pre = [&]() {
+    if constexpr (!RING) stage_wait<D * P * 2>();  // D tiles of P panels: codes + scales
+  };
   auto col_of = [&](int gi) { return (pw + gi * PWv) * P * 16; };  // block-local first column
   auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash_rows<P, false>(wres, rs, col_of(gi), M, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_rows<P, true>(wres, rs, col_of(gi), M, acc); };
   const ALds al = alds_view(reinterpret_cast<const char*>(lds), KRg, M, wt0);
-  stream_groups<FMT, P, D, true>(ng, wtn, kt0 + wt0, kp.half_t, al, g.K, group, pre_issue, pre, epi, epi_add);
+  const ARing rg = aring_view(lds_offset(lds) + static_cast<unsigned>(w * D * kRingSlot));
+  // a wave without tiles streams an empty range placed at the last packed
+  // tile, so that its prologue's loads (never computed) stay in the matrix
+  const int wk0 = wtn > 0 ? kt0 + wt0 : kp.ntiles - 1;
+  stream_groups<FMT, P, D, RING ? kARing : kAStaged>(ng, wtn, wk0, kp.half_t, al, rg, g.K, group, pre_issue, pre, epi,
+                                                    epi_add);
   if (wtn == 0) {  // a k-split wave without tiles still owns zero partials
     f32x4 z[P][2];
 #pragma unroll
@@ -312,12 +337,12 @@ __global__ __launch_bounds__(64) void dequant_kernel(const uint8_t* __restrict__
 }
 
 
-template <int FMT, int P, int W, int D>
+template <int FMT, int P, int W, int D, bool RING>
 int launch_cfg(const GemmParams& kp, hipStream_t s) {
-  const size_t lds = gemm_lds_bytes(kp.g.M, kp.KR, kp.KW, kp.PB);
+  const size_t lds = gemm_lds_bytes(kp.g.M, kp.KR, kp.KW, kp.PB, RING, W, D);
   static size_t lds_allowed = 48 * 1024;  // per instantiation: raise the dynamic LDS limit on demand
   if (lds > lds_allowed) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_kernel<FMT, P, W, D>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_kernel<FMT, P, W, D, RING>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the next call
@@ -325,14 +350,15 @@ int launch_cfg(const GemmParams& kp, hipStream_t s) {
     }
     lds_allowed = lds;
   }
-  hipLaunchKernelGGL((qgemm_kernel<FMT, P, W, D>), dim3(kp.nblocks * kp.KS), dim3(64 * W), lds, s, kp);
+  hipLaunchKernelGGL((qgemm_kernel<FMT, P, W, D, RING>), dim3(kp.nblocks * kp.KS), dim3(64 * W), lds, s, kp);
   return static_cast<int>(hipGetLastError());
 }
 
 template <int FMT>
 int launch_fmt(const GemmParams& kp, const GemmCfg& cfg, hipStream_t s) {
 #define Q4_CFG(P_, W_, D_) \
-  if (cfg.P == P_ && cfg.W == W_ && cfg.D == D_) return launch_cfg<FMT, P_, W_, D_>(kp, s);
+  if (cfg.P == P_ && cfg.W == W_ && cfg.D == D_)              \
+    return cfg.RING ? launch_cfg<FMT, P_, W_, D_, true>(kp, s) : launch_cfg<FMT, P_, W_, D_, false>(kp, s);
   Q4_CFG(1, 4, 4)
   Q4_CFG(2, 4, 4)
   Q4_CFG(2, 8, 4)
@@ -352,17 +378,23 @@ GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
   const int npanels = static_cast<int>(N / 16);
   const int ntiles = static_cast<int>(full_tiles(K) + (has_half_tile(K) ? 1 : 0));
   GemmCfg c{};
-  if (const char* e = std::getenv("Q4MI_GEMM_CFG")) {  // "P,W,D,KS,KW,PB" for A/B measurements
-    if (std::sscanf(e, "%d,%d,%d,%d,%d,%d", &c.P, &c.W, &c.D, &c.KS, &c.KW, &c.PB) == 6) {
+  const bool ring_ok = K % 64 == 0;  // full tiles lie below K: unconditional activation loads
+  if (const char* e = std::getenv("Q4MI_GEMM_CFG")) {  // "P,W,D,KS,KW,PB[,RING]" for A/B measurements
+    const int nf = std::sscanf(e, "%d,%d,%d,%d,%d,%d,%d", &c.P, &c.W, &c.D, &c.KS, &c.KW, &c.PB, &c.RING);
+    if (nf >= 6) {
       c.KS = c.KS < 1 ? 1 : (c.KS > ntiles ? ntiles : (c.KS > kMaxKS ? kMaxKS : c.KS));
       c.KW = (c.KW >= 1 && c.W % c.KW == 0) ? c.KW : 1;
+      c.RING = (nf == 7 && c.RING && ring_ok) ? 1 : 0;
       return c;
     }
   }
-  // About one workgroup per CU: blocks * KS ~ 256.  KS (k-ranges reduced
-  // across workgroups) only as far as needed for the staged activations to
-  // fit in LDS; inside a workgroup, KW waves split the k-range when a block
-  // has fewer panel groups than waves.
+  // About one workgroup per CU: blocks * KS ~ 256.  Inside a workgroup, KW
+  // waves split the k-range when a block has fewer panel groups than waves.
+  // If all W waves then split the k-range of a single group, no two waves
+  // share activations and, for M > 8 (the ring always moves 16 rows), each
+  // wave moves its own (RING: no workgroup-wide stage, no k-split);
+  // otherwise KS (k-ranges reduced across workgroups) grows only as far as
+  // needed for the staged activations to fit in LDS.
   c.P = 2;
   c.W = 8;
   c.D = npanels >= 4096 ? 8 : 4;  // long streams: more bytes in flight per wave
@@ -383,10 +415,16 @@ GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
   };
   auto fits = [&](const GemmCfg& x) {
     const int KR = (ntiles + x.KS - 1) / x.KS;
-    return gemm_lds_bytes(M, KR, x.KW, x.PB) <= kGemmLdsMax;
+    return gemm_lds_bytes(M, KR, x.KW, x.PB, false, x.W, x.D) <= kGemmLdsMax;
   };
   int KS = 1;
   c = shape(KS);
+  c.RING = 0;
+  if (ring_ok && M > 8 && c.KW == c.W && c.PB == c.P &&
+      gemm_lds_bytes(M, ntiles, c.KW, c.PB, true, c.W, c.D) <= kGemmLdsMax) {
+    c.RING = 1;
+    return c;
+  }
   while (!fits(c) && KS < kMaxKS && KS < ntiles) c = shape(++KS);
   if (c.KS > kMaxKS) c.KS = kMaxKS;
   if (c.KS > ntiles) c.KS = ntiles;
@@ -424,7 +462,8 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
   kp.nblocks = (kp.npanels + kp.PB - 1) / kp.PB;
   kp.rs = kp.PB * 16 + 4;
   kp.nc4_magic = static_cast<unsigned>(((1ull << 32) + kp.PB * 4 - 1) / (kp.PB * 4));
-  kp.res_off = static_cast<int>(gemm_res_offset(g.M, kp.KR));
+  if (cfg.RING && g.K % 64 != 0) return static_cast<int>(hipErrorInvalidConfiguration);
+  kp.res_off = static_cast<int>(gemm_res_offset(g.M, kp.KR, cfg.RING != 0, cfg.W, cfg.D));
   if (kp.KS > kMaxKS) return static_cast<int>(hipErrorInvalidConfiguration);
   if (kp.KW < 1 || cfg.W % kp.KW != 0 || kp.PB < 1) return static_cast<int>(hipErrorInvalidConfiguration);
   if (kp.KS > 1) {
@@ -432,7 +471,7 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
     kp.bcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsBlockCounters);
     kp.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
   }
-  if (gemm_lds_bytes(g.M, kp.KR, kp.KW, kp.PB) > kGemmLdsMax)
+  if (gemm_lds_bytes(g.M, kp.KR, kp.KW, kp.PB, cfg.RING != 0, cfg.W, cfg.D) > kGemmLdsMax)
     return static_cast<int>(hipErrorInvalidConfiguration);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return fmt == kNvfp4 ? launch_fmt<kNvfp4>(kp, cfg, s) : launch_fmt<kAffine>(kp, cfg, s);

@@ -76,6 +76,7 @@ struct GemmCfg {
   int KS;  // k-ranges (workgroups sharing a panel block; partials reduced in order)
   int KW;  // waves splitting a workgroup's k-range (LDS reduction, one group per wave)
   int PB;  // panels per workgroup block
+  int RING;  // 1: each wave moves its own tiles' activations into an LDS ring (one group per wave, K % 64 == 0)
 };
 
 // kernel launchers (q4mi_gemm.hip); return hipError_t as int

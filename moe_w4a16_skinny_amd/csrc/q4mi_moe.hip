@@ -33,10 +33,9 @@ using namespace dev;
 
 // ------------------------------------------------------------------ router
 
-// Ordered key of (logit, expert), kRouteKeyBits wide: larger logit first,
-// then lower expert index (9 bits, E <= 256); distinct and non-zero for every
-// expert (a NaN logit ranks below -inf); 0 marks "no expert".
-constexpr int kRouteKeyBits = 41;
+// Ordered 41-bit key of (logit, expert): larger logit first, then lower
+// expert index (9 bits, E <= 256); distinct and non-zero for every expert (a
+// NaN logit ranks below -inf); 0 marks "no expert".
 __device__ __forceinline__ unsigned long long route_key(float v, int e) {
   unsigned ord = 0u;
   if (v == v) {
@@ -438,7 +437,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   auto epi = [&](int gi, f32x4 (&acc)[2][2]) { stash<2>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[2][2]) { stash_add<2>(wout, gi, acc); };
   if (nitems > 0)
-    stream_groups<kNvfp4, 2, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, m.D, group, pre,
+    stream_groups<kNvfp4, 2, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.D, group, pre,
                                         pre, epi, epi_add);
   for (int gi = 0; gi < ng; ++gi) {
     int e, jp;
@@ -501,7 +500,7 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash<P>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
   if (nitems > 0)
-    stream_groups<kNvfp4, P, DP, false>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, m.F, group, pre,
+    stream_groups<kNvfp4, P, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.F, group, pre,
                                         pre, epi, epi_add);
   for (int gi = 0; gi < ng; ++gi) {
     int e, q;

@@ -203,16 +203,67 @@ __device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4
 }
 
 // Where a wave's activation operands come from.
-//  * ALDS: the workgroup staged its k-range of the activations in LDS (see
-//    stage_a); ALds gives each lane its read address.
-//  * global: lane reads a[row][k0 .. k0 + 8) from its row pointer, zeros for
-//    rows it does not own or k0 >= K (the only bound check of the loop).
-template <int FMT, int P, bool ALDS>
+//  * kAStaged: the workgroup staged its k-range of the activations in LDS
+//    (stage_issue / stage_wait); ALds gives each lane its read address.
+//  * kARing: the wave itself moves each tile's 16 activation rows into a
+//    ring of D LDS slots with direct-to-LDS loads issued together with that
+//    tile's weight loads (ARing), so the math of a tile waits only for that
+//    tile's own loads.
+//  * kAGlobal: lane (c, o) loads a[row c][k0 .. k0 + 8) straight into
+//    registers from its row pointer.
+enum AMode { kAStaged = 0, kARing = 1, kAGlobal = 2 };
+
+template <int FMT, int P, int AM>
 struct StreamStage {
   u32x4 c[P];
   typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type s[P];
-  u32x4 a[ALDS ? 1 : 4];
+  u32x4 a[AM == kAGlobal ? 4 : 1];
 };
+
+// Ring slots of kARing: slot d holds one tile of 16 rows x 128 k (f16/bf16)
+// as 16 rows of 256 bytes.  The loads that fill it move 4 rows x 256 bytes
+// each (row group j = rows 4j .. 4j + 3; lane l: row 4j + (l >> 4), LDS
+// position l & 15 of that row); the 16-byte chunk q (k = 8q .. 8q + 7) of
+// row r is stored at position q ^ r, so that the 16 rows of one k-step
+// (lane (c, o) reads row c, chunk 4i + o) fall in 16 different bank groups
+// and the global side of every load still covers 4 whole 256-byte row
+// segments.
+constexpr int kRingSlot = 4096;
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<size_t>((const lds_char*)(p)));
+}
+struct ARing {
+  unsigned base;   // LDS offset of this wave's D slots (wave-uniform)
+  unsigned rd[4];  // this lane's read offset of k-step i in slot 0
+};
+__device__ __forceinline__ ARing aring_view(unsigned base) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, o = lane >> 4;
+  ARing r;
+  r.base = base;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.rd[i] = base + 256u * c + 16u * static_cast<unsigned>((4 * i + o) ^ c);
+  return r;
+}
+// Element offset, within a tile, of the chunk that lane l moves for row
+// group j (row 4j + (l >> 4)); add it to that row's base pointer.
+__device__ __forceinline__ int ring_chunk(int j) {
+  const int lane = threadIdx.x & 63;
+  return 8 * ((lane & 15) ^ (4 * j + (lane >> 4)));
+}
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+// One direct-to-LDS load of 16 bytes per lane (lane l lands at lds_off +
+// 16 l), issued as inline assembly so that the compiler does not count it
+// among its outstanding loads: with such loads pending it would otherwise
+// wait for every load before each use of a loaded register.  Its waits for
+// the other loads then count fewer younger loads than are really in
+// flight, which only makes them wait longer; the ring reads are ordered
+// after these loads by a dependency on a load issued after them (loads
+// complete in order).
+__device__ __forceinline__ void dma16_to_lds(const void* src, unsigned lds_off) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_off) : "memory");
+}
 
 // Staged activations in LDS, row-major: row c (< M) of a workgroup's
 // k-range of nt tiles is nt * 256 contiguous bytes at c * RS, with
@@ -308,13 +359,16 @@ __device__ __forceinline__ void stage_wait() {
 }
 
 // Where group g's data lives: the packed base of each of its P panels and,
-// when the activations come from global memory, this lane's activation row
-// (a valid row for every lane; rows a lane does not own only feed output rows
-// that are never stored).
+// for the activations (valid rows for every lane: rows past the real ones
+// only feed output rows that are never stored)
+//  * kAGlobal: arow, this lane's row (c = lane & 15);
+//  * kARing: ar[j], the row this lane moves for row group j plus
+//    ring_chunk(j).
 template <int P>
 struct GroupPtrs {
   const uint8_t* panel[P];
   const uint16_t* arow;
+  const uint16_t* ar[4];
 };
 
 // Stream ng groups of P panels over the tiles [kt0, kt0 + KRg) of each group
@@ -330,31 +384,41 @@ struct GroupPtrs {
 // pre_issue() runs before the first weight loads and pre() after them (the
 // workgroup stages its activations across the two, so both travel in the
 // same round trip; every wave must reach pre()).  K is the activations' row
-// length (global mode: a multiple of 64).  All arguments except the
+// length (kAGlobal and kARing: a multiple of 64).  All arguments except the
 // lane-dependent pointers are wave-uniform.
-template <int FMT, int P, int D, bool ALDS, class Group, class PreIssue, class Pre, class Epi, class EpiAdd>
-__device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, ALds al, int K, Group group,
-                                              PreIssue pre_issue, Pre pre, Epi epi, EpiAdd epi_add) {
+template <int FMT, int P, int D, int AM, class Group, class PreIssue, class Pre, class Epi, class EpiAdd>
+__device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, ALds al, ARing ring, int K,
+                                              Group group, PreIssue pre_issue, Pre pre, Epi epi, EpiAdd epi_add) {
+  constexpr bool ALDS = AM == kAStaged;
   const int lane = threadIdx.x & 63;
   const int o = lane >> 4;
   const int c = lane & 15;
   const bool has_half = half_t >= kt0 && half_t < kt0 + KRg;
   const int KRf = has_half ? KRg - 1 : KRg;  // full tiles streamed per group
   const int F = ng * KRf;
-  using St = StreamStage<FMT, P, ALDS>;
+  using St = StreamStage<FMT, P, AM>;
 
   // Global activations: a full tile lies entirely below K, so its loads are
   // unconditional (exact waits).  The half tile's k >= K half is read at k 0
   // and zeroed.
-  auto load_a = [&](St& st, const GroupPtrs<P>& gp, int tg) {
-    if constexpr (!ALDS) {
+  // kARing: the tile's 4 row-group loads into slot d go first (the asm's
+  // memory clobber keeps the weight loads after them), so that a wait for the
+  // tile's first weight load also covers its activations.
+  auto load_a = [&](St& st, const GroupPtrs<P>& gp, int tg, int d) {
+    if constexpr (AM == kAGlobal) {
       const int kb = tg * kTileK;
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(gp.arow + kb + 32 * i + 8 * o);
+    } else if constexpr (AM == kARing) {
+      const int kb = tg * kTileK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16_to_lds(gp.ar[j] + kb, ring.base + d * kRingSlot + j * 1024);
     }
   };
-  auto load_a_half = [&](St& st, const GroupPtrs<P>& gp) {
-    if constexpr (!ALDS) {
+  // half tile: chunks at k >= K are zeros (the weights there are zero, but
+  // the activations past the row end need not be finite)
+  auto load_a_half = [&](St& st, const GroupPtrs<P>& gp, int d) {
+    if constexpr (AM == kAGlobal) {
       const int kb = half_t * kTileK;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -362,11 +426,21 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
         const u32x4 v = *reinterpret_cast<const u32x4*>(gp.arow + (k0 < K ? k0 : 0));
         st.a[i] = k0 < K ? v : u32x4{0u, 0u, 0u, 0u};
       }
+    } else if constexpr (AM == kARing) {
+      const int kb = half_t * kTileK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned dst = ring.base + d * kRingSlot + j * 1024;
+        if (ring_chunk(j) < kTileK / 2)
+          dma16_to_lds(gp.ar[j] + kb, dst);
+        else
+          *(lds_u32x4*)(static_cast<size_t>(dst + 16u * static_cast<unsigned>(lane))) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
-  auto load = [&](St& st, const GroupPtrs<P>& gp, int t) {
+  auto load = [&](St& st, const GroupPtrs<P>& gp, int t, int d) {
     const int tg = kt0 + t;
-    load_a(st, gp, tg);
+    load_a(st, gp, tg, d);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint8_t* tb = gp.panel[p] + static_cast<size_t>(tg) * kTileBytes;
@@ -377,8 +451,8 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
         st.s[p] = ld_nt8(tb + kTileCodeBytes + c * 8);
     }
   };
-  auto load_half = [&](St& st, const GroupPtrs<P>& gp) {
-    load_a_half(st, gp);
+  auto load_half = [&](St& st, const GroupPtrs<P>& gp, int d) {
+    load_a_half(st, gp, d);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint8_t* tb = gp.panel[p] + static_cast<size_t>(half_t) * kTileBytes;
@@ -401,27 +475,35 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   GroupPtrs<P> cur;    // the load cursor's group
   group(0, cur);
   // (>=: a range of only the half tile, KRf == 0, keeps t = 0, the half tile)
-  auto load_next = [&](St& x) {
-    load(x, cur, lt);
+  auto load_next = [&](St& x, int d) {
+    load(x, cur, lt, d);
     if (++lt >= KRf) {
       lt = 0;
       ++lg;
       group(lg, cur);
     }
   };
-  auto tile_a = [&](const St& x, int t, u32x4 (&a)[4]) {
+  // kARing: the read addresses pass through an empty asm that takes the
+  // tile's first weight word, so the reads wait for that load and hence for
+  // the activation loads issued before it.
+  auto tile_a = [&](const St& x, int t, int d, u32x4 (&a)[4]) {
     if constexpr (ALDS) {
       const char* pa = al.base + t * 256;
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(pa + i * 64);
+    } else if constexpr (AM == kARing) {
+      unsigned off = static_cast<unsigned>(d * kRingSlot);
+      asm volatile("" : "+v"(off) : "v"(x.c[0].x));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const lds_u32x4*)(static_cast<size_t>(ring.rd[i] + off));
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = x.a[i];
     }
   };
-  auto compute_next = [&](const St& x) {
+  auto compute_next = [&](const St& x, int d) {
     u32x4 a[4];
-    tile_a(x, ct, a);
+    tile_a(x, ct, d, a);
     tile_math<FMT, P>(acc, a, x.c, x.s);
     if (++ct == KRf) {
       epi(cg, acc);
@@ -440,32 +522,40 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   // per D tiles of math with no condition around any load, so the wait before
   // each tile covers only that tile's loads; the drain computes the last
   // tiles with the remaining loads issued under conditions.
+  // With kAGlobal or kARing and no full tile (a range of only the half tile,
+  // or none), the prologue is skipped: its full-tile activation loads would
+  // read past the end of rows shorter than a tile.  pre() must then not rely
+  // on the prologue's loads (it does not in these modes).
   pre_issue();
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    load_next(st[d]);
-    __builtin_amdgcn_sched_barrier(0);  // keep the steady loop's load order (see the waits below)
-  }
-  pre();
-  int f = 0;
-  for (; f + 2 * D <= F; f += D) {
+  if (ALDS || KRf > 0) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      compute_next(st[d]);
-      load_next(st[d]);
-      __builtin_amdgcn_sched_barrier(0);
+      load_next(st[d], d);
+      __builtin_amdgcn_sched_barrier(0);  // keep the steady loop's load order (see the waits below)
     }
-  }
+    pre();
+    int f = 0;
+    for (; f + 2 * D <= F; f += D) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (f + d < F) {
-      compute_next(st[d]);
-      if (f + d + D < F) load_next(st[d]);
+      for (int d = 0; d < D; ++d) {
+        compute_next(st[d], d);
+        load_next(st[d], d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  }
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (f + D + d < F) compute_next(st[d]);
+    for (int d = 0; d < D; ++d) {
+      if (f + d < F) {
+        compute_next(st[d], d);
+        if (f + d + D < F) load_next(st[d], d);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (f + D + d < F) compute_next(st[d], d);
+  } else {
+    pre();
+  }
   if (KRf == 0) {  // a range of only the half tile: every group still owns a result
     for (int gg = 0; gg < ng; ++gg) epi(gg, acc);
   }
@@ -478,7 +568,7 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
         if (g0 + d < ng) {
           GroupPtrs<P> hp;
           group(g0 + d, hp);
-          load_half(st[d], hp);
+          load_half(st[d], hp, d);
         }
       }
 #pragma unroll
@@ -488,13 +578,16 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
 #pragma unroll
           for (int p = 0; p < P; ++p) hacc[p][0] = hacc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
           u32x4 a[4];
-          tile_a(st[d], KRg - 1, a);
+          tile_a(st[d], KRg - 1, d, a);
           tile_math<FMT, P>(hacc, a, st[d].c, st[d].s);
           epi_add(g0 + d, hacc);
         }
       }
     }
   }
+  // loads past the wave's work may still be writing the ring: they must land
+  // before the workgroup can end and its LDS be handed to another
+  if constexpr (AM == kARing) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Park a finished group's P panels in a row-major LDS result block

@@ -18,10 +18,14 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 REL = 1e-3
-# "P,W,D,KS,KW,PB": panels per wave group, waves, loads in flight, k-ranges, k-split waves, panels per workgroup
+# "P,W,D,KS,KW,PB[,RING]": panels per wave group, waves, loads in flight, k-ranges, k-split waves,
+# panels per workgroup, activations moved per wave into an LDS ring (1) or staged per workgroup
 CFGS = ["1,4,4,1,1,4", "1,4,4,3,1,8", "2,4,4,1,1,8", "2,4,4,4,1,8", "2,8,4,1,1,16", "2,8,4,2,1,48", "4,4,4,1,1,16",
         "4,8,4,5,1,32", "2,4,8,1,1,8", "2,8,8,7,1,16", "4,4,6,2,1,64", "2,8,4,1,8,2", "2,8,4,2,4,4", "1,4,4,3,2,2",
-        "4,8,4,1,2,16"]
+        "4,8,4,1,2,16",
+        # activations moved by each wave into its own LDS ring
+        "2,8,4,1,8,2,1", "2,8,4,2,4,4,1", "1,4,4,3,2,2,1", "4,8,4,1,2,8,1", "2,4,8,1,1,8,1", "4,4,6,2,1,16,1",
+        "2,4,4,1,1,16,1"]
 
 
 def q4():

@@ -29,7 +29,9 @@ def test_shared_workspace_interleaved_calls():
     aaff = dev(aff.a.view(np.int16)).view(torch.bfloat16)
     ref_aff, bnd_aff = oracle.affine_gemm_ref(aff.codes, aff.scale, aff.bias, aff.a)
 
-    nv = synth.nvfp4_gemm(33, 16, 4096, 1024)
+    # K % 64 != 0: activations staged in LDS, K split over two workgroups per block
+    nv = synth.nvfp4_gemm(33, 16, 5136, 1024)
+    assert q4.raw().qgemm_nvfp4_workspace_bytes(16, 5136, 1024, 1) > 32768
     wnv = dev(q4.q4_nvfp4_repack(nv.codes, nv.scales))
     ref_nv, bnd_nv = oracle.nvfp4_gemm_ref(nv.codes, nv.scales, nv.g, nv.a)
 

@@ -128,12 +128,12 @@ def test_gemm_refusals_without_gpu():
         (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, q4.Q4_F32, p, p, 8, None), q4.Q4_ERR_WORKSPACE, "ws_bytes"),
         (lambda: lib.qgemm_affine4(p, p, 1, 96, 16, p, q4.Q4_F32, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "K=96"),
         (lambda: lib.qgemm_affine4(p, p, 1, 128, 16, p, q4.Q4_F16, None, 0, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
-        (lambda: lib.qgemm_affine4(p, p, 16, 5120, 15360, p, q4.Q4_F32, None, 0, None), q4.Q4_ERR_WORKSPACE, "ws is NULL"),
+        (lambda: lib.qgemm_affine4(p, p, 16, 8192, 131072, p, q4.Q4_F32, None, 0, None), q4.Q4_ERR_WORKSPACE, "ws is NULL"),
         (lambda: lib.qgemm_nvfp4(p, 1.0, p, 16, 4096, 8192, p, q4.Q4_F16, p, p, 64, None), q4.Q4_ERR_WORKSPACE, "ws_bytes"),
         (lambda: lib.q4_dequant_nvfp4(p, 1.0, 15, 64, p, None), q4.Q4_ERR_UNSUPPORTED, "N=15"),
     ]
     # these shapes must need a workspace, or the refusal cases above would launch
-    assert lib.qgemm_affine4_workspace_bytes(16, 5120, 15360) > 0
+    assert lib.qgemm_affine4_workspace_bytes(16, 8192, 131072) > 0
     assert lib.qgemm_nvfp4_workspace_bytes(16, 4096, 8192, 1) > 64
     for call, code, needle in cases:
         assert call() == code, needle
