@@ -171,9 +171,10 @@ size_t moe_route_workspace_bytes(int T, int D, int E);
  *   x        device f16 [T][D];  w_router device fp32 [D][E]
  *   logits   device fp32 [T][E] or NULL
  *   topk_idx device int32 [T][k];  topk_w device fp32 [T][k]
- *   ws       device workspace (zero-filled before first use, left zero-filled)
+ *   ws       device workspace (see above: its counters start at zero and are
+ *            left at zero)
  * Errors: INVALID_ARG, UNSUPPORTED (T outside 1..64, E outside 1..256,
- * k > E or k > 16, D % 8, D beyond about 1400 * min(16, 1024 / E) * 16),
+ * k > E or k > 16, D % 8, D > 12288),
  * ALIGNMENT, WORKSPACE, HIP. */
 int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k,
                    int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws,

@@ -335,7 +335,7 @@ int q4_dequant_affine4(const void* w_packed, int64_t N, int64_t K, float* out, v
 
 size_t moe_route_workspace_bytes(int T, int D, int E) {
   if (T < 1 || D < 1 || E < 1 || E > 256) return 0;
-  return kWsCounterBytes + size_t(route_blocks(D, E)) * size_t(T) * size_t(E) * sizeof(float);
+  return kWsCounterBytes + size_t(route_splits(D)) * size_t(T) * size_t(E) * sizeof(float);
 }
 
 int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k, int renormalize, float* logits,
@@ -350,8 +350,8 @@ int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, in
   if (E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", __func__, E);
   if (k > E || k > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d must be <= E=%d and <= 16", __func__, k, E);
   if (D % 8) return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d is not a multiple of 8", __func__, D);
-  if (route_lds_bytes(D, E) > 150 * 1024)
-    return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d too large for E=%d (router block exceeds LDS)", __func__, D, E);
+  if (route_rows(D) > kRouteMaxRows)
+    return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d > %d", __func__, D, kRouteMaxSplits * kRouteMaxRows);
   REQUIRE_ALIGNED(x);
   REQUIRE_ALIGNED(w_router);
   REQUIRE_ALIGNED(topk_idx);
@@ -374,8 +374,8 @@ int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, in
   r.w = topk_w;
   r.counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsRouteCounter);
   r.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
-  r.nblk = route_blocks(D, E);
-  r.rows = route_rows(D, E);
+  r.nsplit = route_splits(D);
+  r.rows = route_rows(D);
   if (int e = launch_route(r, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   return ok();
 }

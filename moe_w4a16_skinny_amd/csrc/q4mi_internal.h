@@ -86,31 +86,29 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
 int launch_dequant(int fmt, const uint8_t* w, int64_t panel_bytes, int64_t N, int64_t K, float g,
                    float* out, void* stream);
 
-// Router split of D over at most kRouteMaxBlocks workgroups of
-// kRouteThreads threads (8 waves).  A wave computes 16 experts x 16 tokens
-// with fp32 MFMAs over a slice of the workgroup's rows (8 / column blocks
-// slices when E < 128, summed in LDS in slice order); the last workgroup to
-// finish adds the blocks' partial logits in block order.
-constexpr int kRouteThreads = 512;
-constexpr int kRouteMaxBlocks = 16;
-Q4_HD inline int route_slices(int E) {
-  const int cb = (E + 15) / 16;
-  return cb >= 8 ? 1 : 8 / cb;
+// Router grid: (16-expert column blocks) x (splits of D), workgroups of
+// kRouteThreads threads (4 waves).  A workgroup computes the logits of its
+// 16 experts for every token over its rows of D; its waves split those rows
+// (a multiple of 16 each) and their partial sums are added in LDS in wave
+// order.  The last workgroup to finish adds the D-splits' partial logits in
+// split order and takes the top-k.
+constexpr int kRouteThreads = 256;
+constexpr int kRouteMaxSplits = 8;
+constexpr int kRouteMaxRows = 1536;  // rows of D per workgroup (staged x: 96 KiB)
+Q4_HD inline int route_eblocks(int E) { return (E + 15) / 16; }
+Q4_HD inline int route_splits(int D) {
+  const int s = (D + 255) / 256;
+  return s < 1 ? 1 : (s > kRouteMaxSplits ? kRouteMaxSplits : s);
 }
-Q4_HD inline int route_rows(int D, int E) {  // rows per workgroup: a multiple of 16 per slice
-  const int unit = 16 * route_slices(E);
-  int nb = (D + 4 * unit - 1) / (4 * unit);  // at least 64 rows per slice
-  nb = nb < 1 ? 1 : (nb > kRouteMaxBlocks ? kRouteMaxBlocks : nb);
-  const int per = (D + nb - 1) / nb;
-  return (per + unit - 1) / unit * unit;
+Q4_HD inline int route_rows(int D) {  // rows per split: a multiple of 64 (16 per wave)
+  const int s = route_splits(D);
+  return ((D + s - 1) / s + 63) / 64 * 64;
 }
-Q4_HD inline int route_blocks(int D, int E) { return (D + route_rows(D, E) - 1) / route_rows(D, E); }
-// staged x (rows x 16 tokens, fp32) + slice sums / logits (64 KiB holds both
-// slices * 16 * E <= 4096 and T * E <= 16384 floats)
-// (the staged-x area, at least 16 KiB, later holds 8 waves x 256 keys)
-Q4_HD inline size_t route_lds_bytes(int D, int E) {
-  const size_t xs = static_cast<size_t>(route_rows(D, E)) * 64;
-  return (xs < 16384 ? 16384 : xs) + 65536;
+// staged x [rows][16] fp32, reused by the last workgroup for the logits
+// [T][E] (T <= 64, E <= 256: at most 64 KiB); then the waves' partial sums
+Q4_HD inline size_t route_lds_bytes(int D) {
+  const size_t xs = static_cast<size_t>(route_rows(D)) * 64;
+  return (xs < 65536 ? 65536 : xs) + 4096;
 }
 
 struct RouteArgs {
@@ -120,10 +118,10 @@ struct RouteArgs {
   float* logits;        // nullable [T][E]
   int32_t* idx;         // [T][k]
   float* w;             // [T][k]
-  float* partial;       // workspace [nblk][T][E]
+  float* partial;       // workspace [splits][T][E]
   unsigned* counter;    // workspace counter
-  int nblk;             // workgroups splitting D
-  int rows;             // rows of D per workgroup
+  int nsplit;           // splits of D
+  int rows;             // rows of D per split (a multiple of 64)
 };
 int launch_route(const RouteArgs& r, void* stream);
 

@@ -33,130 +33,217 @@ using namespace dev;
 
 // ------------------------------------------------------------------ router
 
-// Ordered 41-bit key of (logit, expert): larger logit first, then lower
-// expert index (9 bits, E <= 256); distinct and non-zero for every expert (a
-// NaN logit ranks below -inf); 0 marks "no expert".
-__device__ __forceinline__ unsigned long long route_key(float v, int e) {
-  unsigned ord = 0u;
-  if (v == v) {
-    if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
-    const unsigned b = __float_as_uint(v);
-    ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  }
-  return (static_cast<unsigned long long>(ord) << 9) | (511u - static_cast<unsigned>(e)) + 0ull;
+// Order-preserving 32-bit code of a logit: a larger logit gets a larger
+// code, -0 and +0 the same one; NaN gets 1, below every number; 0 marks "no
+// expert" (taken, or past E).  Equal codes are told apart by expert index
+// (the lower wins).
+__device__ __forceinline__ unsigned route_ord(float v) {
+  if (v != v) return 1u;
+  if (v == 0.0f) v = 0.0f;
+  const unsigned b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-// logit of a key (inverse of the order map; NaN keys never reach this)
-__device__ __forceinline__ float route_key_value(unsigned long long key) {
-  const unsigned ord = static_cast<unsigned>(key >> 9);
-  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+// logit of a code (inverse of the order map; 1 gives a NaN)
+__device__ __forceinline__ float route_ord_value(unsigned o) {
+  return o == 1u ? __uint_as_float(0x7FC00000u) : __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// Wave-wide reductions with DPP: row_shr 1, 2, 4, 8 leave each row's total in
-// its lane 15, row_bcast 15 and 31 fold the rows into lane 63, which is then
-// read into a scalar register (a fixed combination order).  Lanes shifted in
-// from outside a row read 0, the identity of both reductions used here.
+// DPP lane move (bound_ctrl: a lane whose source is outside the row reads 0)
 template <int CTRL>
 __device__ __forceinline__ unsigned dpp_u32(unsigned x) {
   return static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_max_key(unsigned long long k) {
-  const unsigned lo = dpp_u32<CTRL>(static_cast<unsigned>(k));
-  const unsigned hi = dpp_u32<CTRL>(static_cast<unsigned>(k >> 32));
-  const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
-  return o > k ? o : k;
-}
-__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
-  k = dpp_max_key<0x111>(k);  // row_shr:1
-  k = dpp_max_key<0x112>(k);  // row_shr:2
-  k = dpp_max_key<0x114>(k);  // row_shr:4
-  k = dpp_max_key<0x118>(k);  // row_shr:8
-  k = dpp_max_key<0x142>(k);  // row_bcast:15
-  k = dpp_max_key<0x143>(k);  // row_bcast:31
-  const unsigned lo = __builtin_amdgcn_readlane(static_cast<unsigned>(k), 63);
-  const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(k >> 32), 63);
-  return (static_cast<unsigned long long>(hi) << 32) | lo;
+__device__ __forceinline__ unsigned dpp_max_u32(unsigned x) {
+  const unsigned o = dpp_u32<CTRL>(x);
+  return o > x ? o : x;
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
   return x + __uint_as_float(dpp_u32<CTRL>(__float_as_uint(x)));
 }
-__device__ __forceinline__ float wave_sum(float x) {
-  x = dpp_add<0x111>(x);
-  x = dpp_add<0x112>(x);
-  x = dpp_add<0x114>(x);
-  x = dpp_add<0x118>(x);
-  x = dpp_add<0x142>(x);
-  x = dpp_add<0x143>(x);
-  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 63));
+
+// Reductions over the 16 lanes of a row, result in every lane: quad_perm
+// [1,0,3,2] and [2,3,0,1] combine the lanes of a quad, row_half_mirror (lane
+// i with 7 - i) and row_mirror (i with 15 - i) join quads and halves; every
+// lane combines the same values in the same pairing order.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_min_u32(unsigned x) {
+  const unsigned o = dpp_u32<CTRL>(x);
+  return o < x ? o : x;
+}
+__device__ __forceinline__ unsigned row_max_u32(unsigned x) {
+  x = dpp_max_u32<0xB1>(x);
+  x = dpp_max_u32<0x4E>(x);
+  x = dpp_max_u32<0x141>(x);
+  return dpp_max_u32<0x140>(x);
+}
+__device__ __forceinline__ unsigned row_min_u32(unsigned x) {
+  x = dpp_min_u32<0xB1>(x);
+  x = dpp_min_u32<0x4E>(x);
+  x = dpp_min_u32<0x141>(x);
+  return dpp_min_u32<0x140>(x);
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x = dpp_add<0xB1>(x);
+  x = dpp_add<0x4E>(x);
+  x = dpp_add<0x141>(x);
+  return dpp_add<0x140>(x);
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
-  extern __shared__ float rsm[];  // [rows][16] staged x (fp32), then [slices][16][E] sums / [T][E] logits
-  const int T = r.T, D = r.D, E = r.E;
-  const int tid = threadIdx.x;
-  const int R = r.rows;  // a multiple of 16 * (row slices)
-  const int d0 = blockIdx.x * R;
-  float* xs = rsm;
-  float* red = rsm + (R * 16 > 4096 ? R * 16 : 4096);  // after the staged-x area (>= 16 KiB)
-  const _Float16* x = reinterpret_cast<const _Float16*>(r.x);
+// Top-k of the logits lg[T][E] (LDS) and their softmax, a token per 16-lane
+// row (four per wave); lane p of the row holds experts p + 16 j, j < J (E <=
+// 16 J).  Each of the k rounds takes the row-wide maximum of the codes still
+// in play, then the row-wide minimum expert index holding it, and retires
+// that expert; lane s keeps the round-s choice.  Softmax over all E with the
+// first choice as the maximum.
+template <int J>
+__device__ void route_topk_rows(const RouteArgs& r, const float* lg) {
+  const int T = r.T, E = r.E;
+  const int lane = threadIdx.x & 63, p = lane & 15;
+  for (int t0 = (threadIdx.x >> 6) * 4; t0 < T; t0 += (blockDim.x >> 6) * 4) {
+    const int t = t0 + (lane >> 4);
+    const bool ok = t < T;
+    const float* l = lg + static_cast<size_t>(ok ? t : t0) * E;
+    float v[J];
+    unsigned ord[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int ee = p + 16 * j;
+      v[j] = ee < E ? l[ee] : 0.f;
+      ord[j] = (ok && ee < E) ? route_ord(v[j]) : 0u;
+    }
+    unsigned first = 0u, my_ord = 0u, my_e = 0u;
+    for (int s = 0; s < r.k; ++s) {
+      unsigned lm = 0u;
+#pragma unroll
+      for (int j = 0; j < J; ++j) lm = max(lm, ord[j]);
+      const unsigned m = row_max_u32(lm);
+      unsigned ci = 0xFFFFu;
+#pragma unroll
+      for (int j = 0; j < J; ++j) ci = min(ci, ord[j] == m ? static_cast<unsigned>(p + 16 * j) : 0xFFFFu);
+      const unsigned ce = row_min_u32(ci);
+#pragma unroll
+      for (int j = 0; j < J; ++j) ord[j] = static_cast<unsigned>(p + 16 * j) == ce ? 0u : ord[j];
+      if (s == 0) first = m;
+      if (p == s) {
+        my_e = ce;
+        my_ord = m;
+      }
+    }
+    const float mx = route_ord_value(first);
+    float se = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) se += p + 16 * j < E ? expf(v[j] - mx) : 0.f;
+    se = row_sum(se);
+    const float pm = p < r.k ? expf(route_ord_value(my_ord) - mx) : 0.f;
+    const float ws = row_sum(pm);
+    if (ok && p < r.k) {
+      const float pr = pm / se;
+      r.idx[t * r.k + p] = static_cast<int>(my_e);
+      r.w[t * r.k + p] = r.renormalize ? pr / (ws / se) : pr;
+    }
+  }
+}
 
-  // Tokens in groups of 16: stage x (zeros past T and past D) as [row][16],
-  // then v_mfma_f32_16x16x4_f32 jobs of 16 experts x a slice of the rows:
-  // lane (c, q) = (lane & 15, lane >> 4) supplies A = x[token c][row 4i + q]
-  // and B = W_r[row 4i + q][expert e0 + c]; its accumulator holds expert
-  // e0 + c of tokens 4q + r.  Slices are summed in LDS in slice order.
+constexpr int kRouteBatch = 12;  // 16-row steps of router weights loaded before their MFMAs
+
+// Logits of 16 experts (column block eb) for every token over one split of
+// D (rows [r0, r0 + R)), then, in the last workgroup, their sum over the
+// splits and the top-k.  Tokens go in groups of 16: x is staged as
+// [row][16] fp32 (zeros past T and past D); wave w takes rows r0 + w R/4 ..
+// with v_mfma_f32_16x16x4_f32: lane (c, q) = (lane & 15, lane >> 4) supplies
+// A = x[token c][row 4i + q] and B = W_r[row 4i + q][expert e0 + c], and its
+// accumulator holds expert e0 + c of tokens 4q + r.  The router weights of up
+// to kRouteBatch 16-row steps are loaded at once, the first batch right
+// behind the x loads, and the staging barrier waits only for the x stores,
+// so a wave waits for one round trip per batch.  Four independent
+// accumulator chains are added in a fixed order; the waves' partial sums
+// are added in LDS in wave order.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
+  extern __shared__ float rsm[];  // [R][16] staged x (fp32; the last workgroup's [T][E] logits), then [4][256] sums
+  const int T = r.T, D = r.D, E = r.E, R = r.rows;
+  const int tid = threadIdx.x;
+  const int neb = (E + 15) / 16;
+  const int eb = blockIdx.x % neb, ds = blockIdx.x / neb;
+  const int e0 = eb * 16, r0 = ds * R;
+  const int xs_floats = R * 16 > 16384 ? R * 16 : 16384;
+  float* xs = rsm;
+  float* red = rsm + xs_floats;
+  const _Float16* x = reinterpret_cast<const _Float16*>(r.x);
   const int lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, kq = lane >> 4;
-  const int cb = (E + 15) / 16;              // 16-expert column blocks
-  const int ns = cb >= 8 ? 1 : 8 / cb;       // row slices per column block
-  const int rps = R / ns;                    // rows per slice (a multiple of 16)
+  const int rw = R / (kRouteThreads / 64);  // rows per wave (a multiple of 16)
+  const int i0w = wv * rw, i1w = i0w + rw;  // this wave's rows, relative to r0
+  const float* wcol = r.wr + min(e0 + c, E - 1);
+
+  float bv[kRouteBatch][4];
+  auto load_batch = [&](int i0) {
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int dd = min(i0 + 16 * b + 4 * j + kq, i1w - 1);  // past the wave's rows: a valid row, unused
+        bv[b][j] = wcol[static_cast<size_t>(min(r0 + dd, D - 1)) * E];
+      }
+  };
+  // x staging: item q = (chunk q >> 4 of 8 rows, token q & 15), one 16-byte
+  // load of 8 consecutive f16 of the token's row (D % 8 == 0, so a chunk is
+  // wholly inside or outside D), written as xs[row][token]
+  const int nq = R * 2;  // R / 8 chunks x 16 tokens
   for (int t0 = 0; t0 < T; t0 += 16) {
     const int tn = min(16, T - t0);
-    for (int q0 = 0; q0 < R * 16; q0 += 8 * kRouteThreads) {
-      float v[8];
+    for (int q0 = 0; q0 < nq; q0 += 4 * kRouteThreads) {
+      u32x4 v[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 4; ++u) {
         const int q = q0 + u * kRouteThreads + tid;
-        const int dd = q >> 4, t = q & 15;
-        const bool ok = q < R * 16 && t < tn && d0 + dd < D;
-        const float xv = static_cast<float>(x[ok ? static_cast<size_t>(t0 + t) * D + d0 + dd : 0]);
-        v[u] = ok ? xv : 0.f;
+        const int dd = (q >> 4) * 8, t = q & 15;
+        const bool ok = q < nq && t < tn && r0 + dd < D;
+        v[u] = ok ? *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t0 + t) * D + r0 + dd)
+                  : u32x4{0u, 0u, 0u, 0u};
       }
+      if (q0 == 0) load_batch(i0w);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 4; ++u) {
         const int q = q0 + u * kRouteThreads + tid;
-        if (q < R * 16) xs[q] = v[u];
-      }
-    }
-    __syncthreads();
-    for (int job = wv; job < cb * ns; job += kRouteThreads / 64) {
-      const int cbk = job % cb, sl = job / cb;
-      const int e0 = cbk * 16;
-      const float* wcol = r.wr + min(e0 + c, E - 1);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int i0 = sl * rps; i0 < (sl + 1) * rps; i0 += 16) {
-        float av[4], bv[4];
+        if (q < nq) {
+          const int dd = (q >> 4) * 8, t = q & 15;
+          const f16x8 h = __builtin_bit_cast(f16x8, v[u]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int dd = i0 + 4 * j + kq;
-          av[j] = xs[dd * 16 + c];
-          bv[j] = wcol[static_cast<size_t>(min(d0 + dd, D - 1)) * E];
+          for (int i = 0; i < 8; ++i) xs[(dd + i) * 16 + t] = static_cast<float>(h[i]);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc, 0, 0, 0);
-      }
-      if (e0 + c < E) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) red[(sl * 16 + 4 * kq + rr) * E + e0 + c] = acc[rr];
       }
     }
+    // LDS stores done (s_waitcnt lgkmcnt(0), vmcnt and expcnt left at their
+    // maximum: the weight batch stays in flight), then the barrier
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    f32x4 acc4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc4[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = i0w; i0 < i1w; i0 += 16 * kRouteBatch) {
+      if (i0 != i0w) load_batch(i0);
+#pragma unroll
+      for (int b = 0; b < kRouteBatch; ++b) {
+        if (i0 + 16 * b < i1w) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc4[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[(i0 + 16 * b + 4 * j + kq) * 16 + c], bv[b][j], acc4[j],
+                                                           0, 0, 0);
+        }
+      }
+    }
+    const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) red[wv * 256 + (4 * kq + rr) * 16 + c] = acc[rr];
     __syncthreads();
-    for (int q = tid; q < tn * E; q += kRouteThreads) {
-      const int t = q / E, ee = q - t * E;
+    {
+      const int t = tid >> 4, cc = tid & 15;  // 256 threads: token t, expert e0 + cc
       float sum = 0.f;
-      for (int j = 0; j < ns; ++j) sum += red[(j * 16 + t) * E + ee];
-      store_coherent(r.partial + (static_cast<size_t>(blockIdx.x) * T + t0 + t) * E + ee, sum);
+#pragma unroll
+      for (int w = 0; w < kRouteThreads / 64; ++w) sum += red[w * 256 + tid];
+      if (t < tn && e0 + cc < E) store_coherent(r.partial + (static_cast<size_t>(ds) * T + t0 + t) * E + e0 + cc, sum);
     }
     __syncthreads();  // xs and red are reused
   }
@@ -167,78 +254,42 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
   __syncthreads();
   if (!s_last) return;
 
-  // last workgroup: the blocks' partials of 4 items per thread are loaded at
-  // once, then summed in block order
-  float* lg = red;  // reuse: [T][E]
-  const int nb = gridDim.x;
-  for (int q0 = 0; q0 < T * E; q0 += 4 * kRouteThreads) {
-    float v[4][kRouteMaxBlocks];
+  // last workgroup: every thread loads the splits' partials of 4 logits at
+  // once (16-byte loads when T E is a multiple of 4, so that they stay
+  // aligned; scalar ones otherwise), then sums them in split order
+  float* lg = xs;  // reuse: [T][E]
+  const int ns = r.nsplit;
+  const int TE = T * E;
+  const bool quads = (TE & 3) == 0;
+  for (int q = 4 * tid; q < TE; q += 4 * kRouteThreads) {
+    f32x4 v[kRouteMaxSplits];
+    if (quads) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = q0 + u * kRouteThreads + tid;
+      for (int b = 0; b < kRouteMaxSplits; ++b)
+        v[b] = b < ns ? load_coherent4(r.partial + static_cast<size_t>(b) * TE + q) : f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
 #pragma unroll
-      for (int b = 0; b < kRouteMaxBlocks; ++b)
-        v[u][b] = (b < nb && q < T * E) ? load_coherent(r.partial + static_cast<size_t>(b) * T * E + q) : 0.f;
+      for (int b = 0; b < kRouteMaxSplits; ++b)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[b][u] = (b < ns && q + u < TE) ? load_coherent(r.partial + static_cast<size_t>(b) * TE + q + u) : 0.f;
     }
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < kRouteMaxSplits; ++b) sum += v[b];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int q = q0 + u * kRouteThreads + tid;
-      float sum = 0.f;
-#pragma unroll
-      for (int b = 0; b < kRouteMaxBlocks; ++b) sum += v[u][b];
-      if (q < T * E) {
-        lg[q] = sum;
-        if (r.logits) r.logits[q] = sum;
+      if (q + u < TE) {
+        lg[q + u] = sum[u];
+        if (r.logits) r.logits[q + u] = sum[u];
       }
     }
   }
   __syncthreads();
-
-  // Per token (one wave; lane l holds experts l + 64 j): k rounds of a
-  // wave-wide maximum of the not-yet-chosen keys (keys are distinct, so each
-  // round picks exactly one expert, in decreasing order, ties to the lower
-  // index); softmax over all E with the first choice as the maximum.
-  for (int t = wv; t < T; t += kRouteThreads / 64) {
-    const float* l = lg + static_cast<size_t>(t) * E;
-    float v[4];
-    unsigned long long key[4];
-    int slot[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ee = lane + 64 * j;
-      v[j] = ee < E ? l[ee] : -INFINITY;
-      key[j] = ee < E ? route_key(v[j], ee) : 0ull;
-      slot[j] = -1;
-    }
-    unsigned long long first = 0ull;
-    for (int s = 0; s < r.k; ++s) {
-      unsigned long long mine = 0ull;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mine = (slot[j] < 0 && key[j] > mine) ? key[j] : mine;
-      const unsigned long long best = wave_max_key(mine);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) slot[j] = key[j] == best ? s : slot[j];
-      if (s == 0) first = best;
-    }
-    const float mx = route_key_value(first);
-    float se = 0.f, ws = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p = lane + 64 * j < E ? expf(v[j] - mx) : 0.f;
-      se += p;
-      ws += slot[j] >= 0 ? p : 0.f;
-    }
-    se = wave_sum(se);
-    ws = wave_sum(ws);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (slot[j] >= 0) {
-        const float p = expf(v[j] - mx) / se;
-        r.idx[t * r.k + slot[j]] = lane + 64 * j;
-        r.w[t * r.k + slot[j]] = r.renormalize ? p / (ws / se) : p;
-      }
-    }
-  }
+  if (E <= 128)
+    route_topk_rows<8>(r, lg);
+  else
+    route_topk_rows<16>(r, lg);
   if (tid == 0) atomicExch(r.counter, 0u);
 }
 
@@ -558,7 +609,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
 
 int launch_route(const RouteArgs& r, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t need = route_lds_bytes(r.D, r.E);
+  const size_t need = route_lds_bytes(r.D);
   static size_t lds_allowed = 48 * 1024;
   if (need > lds_allowed) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel),
@@ -569,7 +620,7 @@ int launch_route(const RouteArgs& r, void* stream) {
     }
     lds_allowed = need;
   }
-  hipLaunchKernelGGL(route_kernel, dim3(r.nblk), dim3(kRouteThreads), need, s, r);
+  hipLaunchKernelGGL(route_kernel, dim3(route_eblocks(r.E) * r.nsplit), dim3(kRouteThreads), need, s, r);
   return static_cast<int>(hipGetLastError());
 }
 
