@@ -435,13 +435,31 @@ __device__ void build_groups(const MoeArgs& m, MoeGroups& G) {
   __syncthreads();
 }
 
+// Issue priority of a wave by the number of its items not yet entered (0..3):
+// on a CU shared by waves with different amounts of work left, the ones with
+// more left go first, so that the CU's waves finish closer together.
+__device__ __forceinline__ void prio_by_items_left(int left) {
+  if (left >= 3)
+    __builtin_amdgcn_s_setprio(3);
+  else if (left == 2)
+    __builtin_amdgcn_s_setprio(2);
+  else if (left == 1)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ float gelu_tanh(float u) {
   const float z = 0.7978845608028654f * fmaf(0.044715f * u * u, u, u);
   return 0.5f * u * (1.0f + tanhf(z));
 }
 
-// Work items are dealt round-robin over every wave of the grid: wave gw of NW
-// takes items gw, gw + NW, ...; its g-th item is gw + g NW.
+// Work items are dealt round-robin over the workgroups first, then over the
+// waves of a workgroup: wave w of workgroup b is wave gw = b + w gridDim of
+// NW and takes items gw, gw + NW, ...; its g-th item is gw + g NW.  Every
+// workgroup (and so every CU) then gets the same number of items up to one,
+// and consecutive items, such as the shared expert's, land on different
+// workgroups.
 __device__ __forceinline__ int items_of_wave(int nitems, int gw, int NW) {
   return gw < nitems ? (nitems - gw + NW - 1) / NW : 0;
 }
@@ -462,7 +480,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   const int o = lane >> 4, c = lane & 15;
   const int npp = m.F / 16;
   const int nitems = G.nact * npp;
-  const int gw = blockIdx.x * W + w, NW = gridDim.x * W;
+  const int gw = blockIdx.x + gridDim.x * w, NW = gridDim.x * W;
   const int ng = min(items_of_wave(nitems, gw, NW), NGW);
   const int nfull = static_cast<int>(full_tiles(m.D));
   const bool half = has_half_tile(m.D);
@@ -475,6 +493,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
     e = G.act[a];
   };
   auto group = [&](int gi, GroupPtrs<2>& gp) {
+    prio_by_items_left(ng - gi);
     int e, jp;
     item(gi, e, jp);
     gp.panel[0] = m.gate + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jp) * m.gate_panel_bytes;
@@ -522,7 +541,7 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   const int npan = m.D / 16;
   const int ngp = (npan + P - 1) / P;  // panel groups per expert
   const int nitems = G.nact * ngp;
-  const int gw = blockIdx.x * W + w, NW = gridDim.x * W;
+  const int gw = blockIdx.x + gridDim.x * w, NW = gridDim.x * W;
   const int ng = min(items_of_wave(nitems, gw, NW), NGW);
   const int nfull = static_cast<int>(full_tiles(m.F));
   const bool half = has_half_tile(m.F);
@@ -535,6 +554,7 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
     e = G.act[a];
   };
   auto group = [&](int gi, GroupPtrs<P>& gp) {
+    prio_by_items_left(ng - gi);
     int e, q;
     item(gi, e, q);
 #pragma unroll
