@@ -382,22 +382,27 @@ int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, in
 
 // ---- grouped MoE ---------------------------------------------------------
 
-// scratch after the counter region: h [npairs][F] f16, o [npairs][D] fp32, rowof [T k] int32
-static size_t moe_ws_layout(const q4_moe_desc* w, int T, int k, size_t* h_off, size_t* o_off, size_t* r_off) {
+// scratch after the counter region: h [npairs][F] f16, o [npairs][D] fp32,
+// rowof [T k] int32, the grouping table (moe_grp_words int32)
+static size_t moe_ws_layout(const q4_moe_desc* w, int T, int k, size_t* h_off, size_t* o_off, size_t* r_off,
+                            size_t* g_off) {
   const size_t npairs = size_t(T) * size_t(k) + (w->has_shared ? size_t(T) : 0);
   const size_t hbytes = (npairs * size_t(w->F) * 2 + 255) / 256 * 256;
   const size_t obytes = (npairs * size_t(w->D) * 4 + 255) / 256 * 256;
   const size_t rbytes = (size_t(T) * size_t(k) * 4 + 255) / 256 * 256;
+  const size_t gbytes = (moe_grp_words(w->E, T, k) * 4 + 255) / 256 * 256;
   *h_off = kWsCounterBytes;
   *o_off = *h_off + hbytes;
   *r_off = *o_off + obytes;
-  return *r_off + rbytes;
+  *g_off = *r_off + rbytes;
+  return *g_off + gbytes;
 }
 
 size_t moe_workspace_bytes(const q4_moe_desc* w, int T, int k) {
   if (!w || T < 1 || k < 1 || w->D < 1 || w->F < 1) return 0;
   size_t h, o, r;
-  return moe_ws_layout(w, T, k, &h, &o, &r);
+  size_t g;
+  return moe_ws_layout(w, T, k, &h, &o, &r, &g);
 }
 
 int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_idx, const float* topk_w, int T,
@@ -433,8 +438,8 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
   if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
   REQUIRE_ALIGNED(ws);
   size_t h_off, o_off;
-  size_t r_off = 0;
-  const size_t need = moe_ws_layout(w, T, k, &h_off, &o_off, &r_off);
+  size_t r_off = 0, g_off = 0;
+  const size_t need = moe_ws_layout(w, T, k, &h_off, &o_off, &r_off, &g_off);
   if (ws_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, need);
   MoeArgs m{};
   m.E = w->E;
@@ -461,6 +466,7 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
   m.h = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + h_off);
   m.o = reinterpret_cast<float*>(static_cast<char*>(ws) + o_off);
   m.rowof = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + r_off);
+  m.grp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + g_off);
   if (int e = launch_moe(m, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   return ok();
 }

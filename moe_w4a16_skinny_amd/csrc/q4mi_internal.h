@@ -143,7 +143,13 @@ struct MoeArgs {
   uint16_t* h;             // workspace f16 [npairs][F]
   float* o;                // workspace fp32 [npairs][D]
   int32_t* rowof;          // workspace [T * k]: pair -> scratch row (-1: none)
+  int32_t* grp;            // workspace: the expert grouping, written by gate/up, read by down
 };
+// the grouping table in the workspace (int32 words): nact, then act, cnt and
+// base [E + 1] each, then tok and slot as int16 [T k + T] each
+inline size_t moe_grp_words(int E, int T, int k) {
+  return 4 + 3 * (static_cast<size_t>(E) + 1) + static_cast<size_t>(T) * (k + 1);
+}
 int launch_moe(const MoeArgs& m, void* stream);
 
 }  // namespace q4mi

@@ -449,6 +449,45 @@ __device__ __forceinline__ void prio_by_items_left(int left) {
     __builtin_amdgcn_s_setprio(0);
 }
 
+// The grouping as the down kernel needs it (counts, row bases, active
+// experts, row -> token and slot), passed from gate/up through the
+// workspace: gate/up's workgroup 0 writes it after building it, and every
+// down workgroup reads it into LDS instead of building it again (the kernel
+// boundary orders the two).
+__device__ void publish_groups(const MoeArgs& m, const MoeGroups& G) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int E1 = m.E + 1, nrow = m.T * m.k + m.T;
+  int32_t* g = m.grp;
+  if (tid == 0) g[0] = G.nact;
+  for (int e = tid; e < E1; e += nt) {
+    g[4 + e] = G.act[e];
+    g[4 + E1 + e] = G.cnt[e];
+    g[4 + 2 * E1 + e] = G.base[e];
+  }
+  short* ts = reinterpret_cast<short*>(g + 4 + 3 * E1);
+  for (int q = tid; q < nrow; q += nt) {
+    ts[q] = G.tok[q];
+    ts[nrow + q] = G.slot[q];
+  }
+}
+__device__ void fetch_groups(const MoeArgs& m, MoeGroups& G) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int E1 = m.E + 1, nrow = m.T * m.k + m.T;
+  const int32_t* g = m.grp;
+  if (tid == 0) G.nact = g[0];
+  for (int e = tid; e < E1; e += nt) {
+    G.act[e] = g[4 + e];
+    G.cnt[e] = g[4 + E1 + e];
+    G.base[e] = g[4 + 2 * E1 + e];
+  }
+  const short* ts = reinterpret_cast<const short*>(g + 4 + 3 * E1);
+  for (int q = tid; q < nrow; q += nt) {
+    G.tok[q] = ts[q];
+    G.slot[q] = ts[nrow + q];
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ float gelu_tanh(float u) {
   const float z = 0.7978845608028654f * fmaf(0.044715f * u * u, u, u);
   return 0.5f * u * (1.0f + tanhf(z));
@@ -473,8 +512,10 @@ template <int W, int DP>
 __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW) {
   __shared__ MoeGroups G;
   build_groups(m, G);
-  if (blockIdx.x == 0)  // the pair -> row map, for the combine
+  if (blockIdx.x == 0) {  // the pair -> row map, for the combine; the grouping, for down
     for (int q = threadIdx.x; q < m.T * m.k; q += blockDim.x) m.rowof[q] = G.rowof[q];
+    publish_groups(m, G);
+  }
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = lane >> 4, c = lane & 15;
@@ -534,7 +575,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
 template <int P, int W, int DP>
 __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   __shared__ MoeGroups G;
-  build_groups(m, G);
+  fetch_groups(m, G);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = lane >> 4, c = lane & 15;
