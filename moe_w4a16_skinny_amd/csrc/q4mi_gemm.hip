@@ -47,12 +47,15 @@ struct GemmParams {
   int ntiles;      // packed tiles per panel, half tile included
   int half_t;      // packed index of the half tile, -1 if none
   int KS, KR;      // k-splits and tiles per split
-  int KW;          // waves splitting a workgroup's k-range (one group per wave if > 1)
+  int KW;          // waves splitting a workgroup's k-range (one group per wave if > 1), a power of two
+  int kw_shift;    // log2(KW)
   int PB;          // panels per workgroup block
   int nblocks;     // panel blocks
   int res_off;     // byte offset of the result area in dynamic LDS
   int rs;          // result row stride in floats (PB * 16 + 4)
+  unsigned ks_magic;   // ceil(2^32 / KS): block of a workgroup without a division
   unsigned nc4_magic;  // ceil(2^32 / (PB * 4)): row of an epilogue item without a division
+  unsigned nc4_magic_last;  // the same for the last block's (panels left) * 4
   float* partial;  // [KS][M][N] fp32 (KS > 1)
   unsigned* bcnt;  // [nblocks] arrival counters (KS > 1), left at zero
 };
@@ -116,20 +119,23 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
   __shared__ int s_last;
   const GemmArgs& g = kp.g;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int KS = kp.KS, KW = kp.KW;
-  const int PWv = W / KW;                                  // wave columns (panel groups in parallel)
-  const int kw = w % KW, pw = w / KW;
-  const int ks = blockIdx.x % KS;
-  const int pb = blockIdx.x / KS;
+  // (no integer division: KW and W are powers of two, KS by its magic)
+  const int KS = kp.KS, KW = kp.KW, kws = kp.kw_shift;
+  constexpr int kWShift = W == 8 ? 3 : (W == 4 ? 2 : (W == 2 ? 1 : 0));
+  static_assert((1 << kWShift) == W, "W is a power of two");
+  const int PWv = W >> kws;                                // wave columns (panel groups in parallel)
+  const int kw = w & (KW - 1), pw = w >> kws;
+  const int pb = KS == 1 ? static_cast<int>(blockIdx.x) : static_cast<int>(__umulhi(blockIdx.x, kp.ks_magic));
+  const int ks = static_cast<int>(blockIdx.x) - pb * KS;
   const int kt0 = ks * kp.KR;
   const int KRg = min(kp.ntiles, kt0 + kp.KR) - kt0;       // this workgroup's tiles
-  const int KRw = (KRg + KW - 1) / KW;                     // per k-split wave
+  const int KRw = (KRg + KW - 1) >> kws;                   // per k-split wave
   const int wt0 = min(KRg, kw * KRw);
   const int wtn = min(KRg, wt0 + KRw) - wt0;
   const int p0 = pb * kp.PB;
   const int pend = min(kp.npanels, p0 + kp.PB);
   const int ngb = (pend - p0 + P - 1) / P;                 // panel groups in the block
-  const int ng = ngb > pw ? (ngb - pw + PWv - 1) / PWv : 0; // this wave's: pw, pw + PWv, ...
+  const int ng = ngb > pw ? (ngb - pw + PWv - 1) >> (kWShift - kws) : 0;  // this wave's: pw, pw + PWv, ...
   const int M = g.M, rs = kp.rs;
   float* const res = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kp.res_off);
   float* const wres = res + static_cast<size_t>(kw) * M * rs;  // this wave's k-slice block
@@ -185,15 +191,10 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
   // thread sums the KW k-slices of its group, then stores 4 outputs (or 4
   // partials) in one vector store, so a wave writes 64 consecutive groups.
   const int nc4 = (pend - p0) * 4;  // 4-column groups per row
-  // row of item q: q / nc4 by a multiply and a correction (the magic is for
-  // PB * 4: exact up to one step, except in a last block with fewer panels,
-  // whose few items correct by more steps)
-  auto item_row = [&](int q) {
-    int m = static_cast<int>(__umulhi(static_cast<unsigned>(q), kp.nc4_magic));
-    while (m * nc4 > q) --m;
-    while ((m + 1) * nc4 <= q) ++m;
-    return m;
-  };
+  // row of item q: q / nc4 by a multiply with ceil(2^32 / nc4) (exact while
+  // q nc4 < 2^32, which the launch checks)
+  const unsigned row_magic = pb == kp.nblocks - 1 ? kp.nc4_magic_last : kp.nc4_magic;
+  auto item_row = [&](int q) { return static_cast<int>(__umulhi(static_cast<unsigned>(q), row_magic)); };
   const int items = M * nc4;
   const bool wave_rows = (nc4 & 63) == 0;  // each wave-wide batch of items lies in one row
   for (int q0 = 0; q0 < items; q0 += 64 * W) {
@@ -462,10 +463,20 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
   kp.nblocks = (kp.npanels + kp.PB - 1) / kp.PB;
   kp.rs = kp.PB * 16 + 4;
   kp.nc4_magic = static_cast<unsigned>(((1ull << 32) + kp.PB * 4 - 1) / (kp.PB * 4));
+  const int last_nc4 = (kp.npanels - (kp.nblocks - 1) * kp.PB) * 4;
+  kp.nc4_magic_last = static_cast<unsigned>(((1ull << 32) + last_nc4 - 1) / last_nc4);
+  kp.ks_magic = static_cast<unsigned>(((1ull << 32) + kp.KS - 1) / kp.KS);
+  kp.kw_shift = 0;
+  while ((1 << kp.kw_shift) < cfg.KW) ++kp.kw_shift;
   if (cfg.RING && g.K % 64 != 0) return static_cast<int>(hipErrorInvalidConfiguration);
   kp.res_off = static_cast<int>(gemm_res_offset(g.M, kp.KR, cfg.RING != 0, cfg.W, cfg.D));
   if (kp.KS > kMaxKS) return static_cast<int>(hipErrorInvalidConfiguration);
-  if (kp.KW < 1 || cfg.W % kp.KW != 0 || kp.PB < 1) return static_cast<int>(hipErrorInvalidConfiguration);
+  if (kp.KW < 1 || cfg.W % kp.KW != 0 || (1 << kp.kw_shift) != kp.KW || kp.PB < 1)
+    return static_cast<int>(hipErrorInvalidConfiguration);
+  // the magics give exact quotients while dividend * divisor < 2^32
+  if (static_cast<int64_t>(g.M) * kp.PB * 4 * (kp.PB * 4) >= (1ll << 32) ||
+      static_cast<int64_t>(kp.nblocks) * kp.KS * kp.KS >= (1ll << 32))
+    return static_cast<int>(hipErrorInvalidConfiguration);
   if (kp.KS > 1) {
     if (kp.nblocks > kMaxSplitBlocks) return static_cast<int>(hipErrorInvalidConfiguration);
     kp.bcnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsBlockCounters);
