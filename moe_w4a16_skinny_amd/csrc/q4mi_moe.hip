@@ -9,14 +9,16 @@
 // of launches per layer whatever the expert count.]
 //
 // Launch sequence of moe_grouped_qgemm (one stream, no host synchronization):
-//   1. gate_up: grid (F/16 panel pairs / PW, experts).  Every workgroup
-//      derives its expert's (token, slot) list from topk_idx with wave
-//      ballots (stable in token, slot order), exits if the expert has no
-//      tokens, and streams gate panel j and up panel j together so that
-//      h = gelu_tanh(g_gate acc_g) * (g_up acc_u) is formed in registers and
-//      written as f16 to the expert-sorted scratch h[pair][F].
-//   2. down: grid (D/16 panels / (P PW), experts); rows are the expert's
-//      contiguous h rows; o[pair][D] = w_pair * g_down * acc in fp32.
+//   1. gate_up: a fixed grid of 512 workgroups.  Every workgroup builds the
+//      expert grouping (the (token, slot) pairs sorted by expert, stable in
+//      token order) in LDS from topk_idx; workgroup 0 also writes it to the
+//      workspace.  Work items (active expert, gate panel j + up panel j) are
+//      dealt over the waves; h = gelu_tanh(g_gate acc_g) * (g_up acc_u) is
+//      formed in registers and written as f16 to the expert-sorted scratch
+//      h[row][F].
+//   2. down: the same grid; reads the grouping back, items (active expert,
+//      group of P panels of W_down) over the expert's contiguous h rows;
+//      o[row][D] = w_pair * g_down * acc in fp32.
 //   3. combine: y[t] = sum over slots in order + shared row (fixed order).
 //
 // moe_route_topk: one kernel; workgroups split D and write partial logits,
@@ -254,35 +256,53 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
   __syncthreads();
   if (!s_last) return;
 
-  // last workgroup: every thread loads the splits' partials of 4 logits at
-  // once (16-byte loads when T E is a multiple of 4, so that they stay
-  // aligned; scalar ones otherwise), then sums them in split order
+  // last workgroup: every thread loads the splits' partials of 2 x 4 logits
+  // at once with 16-byte loads (when T E is a multiple of 4, so that they
+  // stay aligned; one logit per thread otherwise), then sums them in split
+  // order.  The loads are unconditional (indexes past the end are clamped,
+  // their values dropped), so that they all issue before the first wait.
   float* lg = xs;  // reuse: [T][E]
   const int ns = r.nsplit;
   const int TE = T * E;
-  const bool quads = (TE & 3) == 0;
-  for (int q = 4 * tid; q < TE; q += 4 * kRouteThreads) {
-    f32x4 v[kRouteMaxSplits];
-    if (quads) {
+  auto put = [&](int q, float v) {
+    lg[q] = v;
+    if (r.logits) r.logits[q] = v;
+  };
+  if ((TE & 3) == 0) {
+    constexpr int kQ = 4 * kRouteThreads;  // logits per pass of the workgroup
+    for (int q0 = 4 * tid; q0 < TE; q0 += 2 * kQ) {
+      f32x4 v[2][kRouteMaxSplits];
 #pragma unroll
-      for (int b = 0; b < kRouteMaxSplits; ++b)
-        v[b] = b < ns ? load_coherent4(r.partial + static_cast<size_t>(b) * TE + q) : f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
+      for (int h = 0; h < 2; ++h) {
+        const int qc = min(q0 + h * kQ, TE - 4);
 #pragma unroll
-      for (int b = 0; b < kRouteMaxSplits; ++b)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          v[b][u] = (b < ns && q + u < TE) ? load_coherent(r.partial + static_cast<size_t>(b) * TE + q + u) : 0.f;
-    }
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < kRouteMaxSplits; ++b) sum += v[b];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (q + u < TE) {
-        lg[q + u] = sum[u];
-        if (r.logits) r.logits[q + u] = sum[u];
+        for (int b = 0; b < kRouteMaxSplits; ++b)
+          v[h][b] = load_coherent4(r.partial + static_cast<size_t>(min(b, ns - 1)) * TE + qc);
       }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = q0 + h * kQ;
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < kRouteMaxSplits; ++b)
+          if (b < ns) sum += v[h][b];
+        if (q < TE) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) put(q + u, sum[u]);
+        }
+      }
+    }
+  } else {
+    for (int q = tid; q < TE; q += kRouteThreads) {
+      float v[kRouteMaxSplits];
+#pragma unroll
+      for (int b = 0; b < kRouteMaxSplits; ++b)
+        v[b] = load_coherent(r.partial + static_cast<size_t>(min(b, ns - 1)) * TE + q);
+      float sum = 0.f;
+#pragma unroll
+      for (int b = 0; b < kRouteMaxSplits; ++b)
+        if (b < ns) sum += v[b];
+      put(q, sum);
     }
   }
   __syncthreads();
@@ -315,29 +335,51 @@ struct MoeGroups {
   int rowof[kMoeMaxPairs];     // pair t k + s -> scratch row (-1: invalid index or dropped)
   short tok[kMoeMaxPairs + 16];   // scratch row -> token
   short slot[kMoeMaxPairs + 16];  // scratch row -> slot (-1: shared expert)
+  float gs0[kMoeMaxE + 1];        // g_gate and g_up of every expert, loaded with the
+  float gs1[kMoeMaxE + 1];        // table so that the epilogue waits on no global load
+};
+// What down keeps of the grouping (read from the workspace), plus g_down of
+// every expert and the routing weights [T k], loaded with it.  Smaller than
+// MoeGroups, so that two down workgroups still fit in a CU's LDS.
+struct MoeDownTable {
+  int cnt[kMoeMaxE + 1];
+  int base[kMoeMaxE + 1];
+  int act[kMoeMaxE + 1];
+  int nact;
+  short tok[kMoeMaxPairs + 16];
+  short slot[kMoeMaxPairs + 16];
+  float gs0[kMoeMaxE + 1];
+  float twl[kMoeMaxPairs];
+  float fac[kMoeMaxPairs + 16];  // row -> its routing weight (1 for the shared expert)
 };
 
+// (also loads the gate/up global scales of every expert into gs0 / gs1)
 __device__ void build_groups(const MoeArgs& m, MoeGroups& G) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int E = m.E, k = m.k, n = m.T * k;
+  const int ne = E + m.has_shared;
   for (int e = tid; e <= E; e += nt) {
     G.cnt[e] = 0;
     if (e < E) G.tmask[e] = 0u;
   }
   if (tid == 0) G.dup = 0;
-  for (int q = tid; q < n; q += nt) {
-    const int e = m.idx[q];
-    G.idx[q] = (e >= 0 && e < E) ? e : -1;
+  for (int q = tid; q < max(n, ne); q += nt) {  // one batch of loads
+    const int e = q < n ? m.idx[q] : -1;
+    const float ga = q < ne ? m.g_gate[q] : 0.f, gb = q < ne ? m.g_up[q] : 0.f;
+    if (q < n) G.idx[q] = (e >= 0 && e < E) ? e : -1;
+    if (q < ne) {
+      G.gs0[q] = ga;
+      G.gs1[q] = gb;
+    }
   }
   __syncthreads();
   for (int q = tid; q < n; q += nt) {
     const int e = G.idx[q];
     if (e < 0) continue;
-    const int t = q / k, s0 = t * k;
+    const int t = q / k;
     atomicAdd(&G.cnt[e], 1);
-    atomicOr(&G.tmask[e], 1u << t);
-    for (int j = s0; j < q; ++j)
-      if (G.idx[j] == e) G.dup = 1;
+    // of two slots of one token naming the same expert, the later OR sees the bit set
+    if (atomicOr(&G.tmask[e], 1u << t) & (1u << t)) G.dup = 1;
   }
   __syncthreads();
   if (tid < 64) {
@@ -354,16 +396,14 @@ __device__ void build_groups(const MoeArgs& m, MoeGroups& G) {
         sa += G.cnt[e] > 0 ? 1 : 0;
       }
     }
-    int xc = sc, xa = sa;
+    // both scans in one word (each sum is at most T k + E < 2^16)
+    int x = (sc << 16) | sa;
     for (int off = 1; off < 64; off <<= 1) {
-      const int yc = __shfl_up(xc, off), ya = __shfl_up(xa, off);
-      if (lane >= off) {
-        xc += yc;
-        xa += ya;
-      }
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
     }
-    xc -= sc;
-    xa -= sa;
+    int xc = (x >> 16) - sc;
+    int xa = (x & 0xFFFF) - sa;
     for (int j = 0; j < per; ++j) {
       const int e = e0 + j;
       if (e < E) {
@@ -470,28 +510,67 @@ __device__ void publish_groups(const MoeArgs& m, const MoeGroups& G) {
     ts[nrow + q] = G.slot[q];
   }
 }
-__device__ void fetch_groups(const MoeArgs& m, MoeGroups& G) {
+// (also loads g_down of every expert into gs0 and the routing weights into twl)
+__device__ void fetch_groups(const MoeArgs& m, MoeDownTable& G) {
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int E1 = m.E + 1, nrow = m.T * m.k + m.T;
+  const int E1 = m.E + 1, nrow = m.T * m.k + m.T, npair = m.T * m.k;
+  const int ne = m.E + m.has_shared;
   const int32_t* g = m.grp;
-  if (tid == 0) G.nact = g[0];
-  for (int e = tid; e < E1; e += nt) {
-    G.act[e] = g[4 + e];
-    G.cnt[e] = g[4 + E1 + e];
-    G.base[e] = g[4 + 2 * E1 + e];
-  }
   const short* ts = reinterpret_cast<const short*>(g + 4 + 3 * E1);
-  for (int q = tid; q < nrow; q += nt) {
-    G.tok[q] = ts[q];
-    G.slot[q] = ts[nrow + q];
+  if (tid == 0) G.nact = g[0];
+  for (int i = tid; i < max(E1, nrow); i += nt) {  // one batch of loads
+    int a = 0, c = 0, b = 0;
+    short tk = 0, sl = 0;
+    float gd = 0.f, tw = 0.f;
+    if (i < E1) {
+      a = g[4 + i];
+      c = g[4 + E1 + i];
+      b = g[4 + 2 * E1 + i];
+    }
+    if (i < ne) gd = m.g_down[i];
+    if (i < nrow) {
+      tk = ts[i];
+      sl = ts[nrow + i];
+    }
+    if (i < npair) tw = m.tw[i];
+    if (i < E1) {
+      G.act[i] = a;
+      G.cnt[i] = c;
+      G.base[i] = b;
+    }
+    if (i < ne) G.gs0[i] = gd;
+    if (i < nrow) {
+      G.tok[i] = tk;
+      G.slot[i] = sl;
+    }
+    if (i < npair) G.twl[i] = tw;
+  }
+  __syncthreads();
+  for (int i = tid; i < nrow; i += nt) {
+    const int sl = G.slot[i];
+    G.fac[i] = sl < 0 ? 1.0f : G.twl[G.tok[i] * m.k + sl];
   }
   __syncthreads();
 }
 
+// GELU, tanh form: 0.5 u (1 + tanh z), z = sqrt(2/pi) (u + 0.044715 u^3).
+// Since 1 + tanh z = 2 / (1 + e^(-2z)), this is u / (1 + e^(-2z)): one
+// hardware exp2 and one reciprocal (a few ulp; e^(-2z) = inf gives 0, and
+// 0 gives u, so both tails saturate exactly).
 __device__ __forceinline__ float gelu_tanh(float u) {
   const float z = 0.7978845608028654f * fmaf(0.044715f * u * u, u, u);
-  return 0.5f * u * (1.0f + tanhf(z));
+  const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * z);  // e^(-2z) = 2^(-2z log2 e)
+  return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
+
+// it / d for the item indexes (it d < 2^32): multiply-high by ceil(2^32 / d)
+struct DivBy {
+  unsigned d, mag;
+  __device__ explicit DivBy(unsigned dd) : d(dd), mag(dd > 1 ? 0xFFFFFFFFu / dd + 1u : 0u) {}
+  __device__ int operator()(int it) const {
+    return d > 1 ? static_cast<int>(__umulhi(static_cast<unsigned>(it), mag)) : it;
+  }
+};
 
 // Work items are dealt round-robin over the workgroups first, then over the
 // waves of a workgroup: wave w of workgroup b is wave gw = b + w gridDim of
@@ -526,10 +605,11 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   const int nfull = static_cast<int>(full_tiles(m.D));
   const bool half = has_half_tile(m.D);
 
+  const DivBy by_npp(static_cast<unsigned>(npp));
   auto item = [&](int gi, int& e, int& jp) {
     int it = gw + gi * NW;
     it = it < nitems ? it : nitems - 1;  // past the wave's items: in-bounds, never computed
-    const int a = it / npp;
+    const int a = by_npp(it);
     jp = it - a * npp;
     e = G.act[a];
   };
@@ -554,7 +634,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
     int e, jp;
     item(gi, e, jp);
     const int me = min(G.cnt[e], 16), base = G.base[e];
-    const float gg = m.g_gate[e], gu = m.g_up[e];
+    const float gg = G.gs0[e], gu = G.gs1[e];
     const f32x4 rg = wout[(gi * 2 + 0) * 64 + lane], ru = wout[(gi * 2 + 1) * 64 + lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -574,7 +654,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
 // g_down * acc in fp32.
 template <int P, int W, int DP>
 __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
-  __shared__ MoeGroups G;
+  __shared__ MoeDownTable G;
   fetch_groups(m, G);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -587,10 +667,11 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   const int nfull = static_cast<int>(full_tiles(m.F));
   const bool half = has_half_tile(m.F);
 
+  const DivBy by_ngp(static_cast<unsigned>(ngp));
   auto item = [&](int gi, int& e, int& q) {
     int it = gw + gi * NW;
     it = it < nitems ? it : nitems - 1;
-    const int a = it / ngp;
+    const int a = by_ngp(it);
     q = it - a * ngp;
     e = G.act[a];
   };
@@ -614,24 +695,23 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   if (nitems > 0)
     stream_groups<kNvfp4, P, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.F, group, pre,
                                         pre, epi, epi_add);
+  const int nrow = m.T * m.k + m.T;
   for (int gi = 0; gi < ng; ++gi) {
     int e, q;
     item(gi, e, q);
     const int me = min(G.cnt[e], 16), base = G.base[e];
-    const float gd = m.g_down[e];
+    const float gd = G.gs0[e];
+    float wp[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wp[r] = G.fac[min(base + 4 * o + r, nrow - 1)];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int pi = q * P + p;
-      if (pi >= npan) continue;
       const f32x4 v = wout[(gi * P + p) * 64 + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * o + r;
-        if (row < me) {
-          const int sl = G.slot[base + row];
-          const float wp = sl < 0 ? 1.0f : m.tw[G.tok[base + row] * m.k + sl];
-          m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wp * (gd * v[r]);
-        }
+        if (pi < npan && row < me) m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wp[r] * (gd * v[r]);
       }
     }
   }

@@ -183,6 +183,25 @@ def test_moe_small_layers(T, D, E, F, k, shared):
     check_moe(moe, mw, idx, w, what=f"T={T} D={D} E={E} F={F} k={k} shared={shared}")
 
 
+def test_moe_token_names_expert_twice():
+    # not something a top-k router produces, but the layer takes any index
+    # table: both pairs count (the grouping then ranks pairs without the
+    # per-expert token masks); small layer, then the 129-expert one (> 64 pairs)
+    moe, mw = layer(960, T=4, D=128, E=6, F=64, k=3, has_shared=True)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    dup = idx.copy()
+    dup[1, 2] = dup[1, 0]
+    dup[3, 1] = dup[3, 0]
+    check_moe(moe, mw, dup, w, what="small layer, two tokens naming an expert twice")
+    moe, mw = layer(104)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    dup = idx.copy()
+    dup[5, 7] = dup[5, 0]
+    dup[12, 3] = dup[12, 1]
+    assert np.bincount(dup.ravel(), minlength=moe.E).max() <= 16
+    check_moe(moe, mw, dup, w, what="129-expert layer, two tokens naming an expert twice")
+
+
 def test_moe_invalid_index_dropped():
     moe, mw = layer(950, T=4, D=128, E=6, F=64, k=2, has_shared=True)
     _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
