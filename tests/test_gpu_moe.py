@@ -202,6 +202,16 @@ def test_moe_token_names_expert_twice():
     check_moe(moe, mw, dup, w, what="129-expert layer, two tokens naming an expert twice")
 
 
+def test_moe_no_valid_pair_no_shared_gives_zero():
+    moe, mw = layer(951, T=3, D=128, E=6, F=64, k=2, has_shared=False)
+    bad = np.full((3, 2), 7, np.int32)   # every index outside 0..E-1
+    bad[1, 0] = -1
+    w = np.full((3, 2), 0.5)
+    for dt in (torch.float32, torch.float16):
+        y = run_moe(moe, mw, bad, w, out_dtype=dt)
+        assert np.array_equal(y, np.zeros_like(y))
+
+
 def test_moe_invalid_index_dropped():
     moe, mw = layer(950, T=4, D=128, E=6, F=64, k=2, has_shared=True)
     _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
