@@ -768,13 +768,13 @@ int launch_route(const RouteArgs& r, void* stream) {
 int launch_moe(const MoeArgs& m, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nexp = m.E + m.has_shared;
-  constexpr int GU_W = 4, DN_P = 2, DN_W = 4, kWG = 512;  // two 4-wave workgroups per CU
-  const int NW = kWG * 4;
+  constexpr int GU_W = 8, DN_P = 2, DN_W = 8, kWG = 256;  // one 8-wave workgroup per CU
+  const int gu_nw = kWG * GU_W, dn_nw = kWG * DN_W;  // waves in the grid
   const int npp = m.F / 16;
-  const int gu_ngw = (nexp * npp + NW - 1) / NW;  // items per wave at most
+  const int gu_ngw = (nexp * npp + gu_nw - 1) / gu_nw;  // items per wave at most
   const size_t gu_lds = static_cast<size_t>(GU_W) * gu_ngw * 2 * 64 * 16;
   const int ngp = (m.D / 16 + DN_P - 1) / DN_P;
-  const int dn_ngw = (nexp * ngp + NW - 1) / NW;
+  const int dn_ngw = (nexp * ngp + dn_nw - 1) / dn_nw;
   const size_t dn_lds = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
   if (gu_lds > 96 * 1024 || dn_lds > 96 * 1024) return static_cast<int>(hipErrorInvalidConfiguration);
   static size_t gu_allowed = 48 * 1024, dn_allowed = 48 * 1024;
