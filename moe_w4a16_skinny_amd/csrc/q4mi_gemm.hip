@@ -362,6 +362,7 @@ int launch_fmt(const GemmParams& kp, const GemmCfg& cfg, hipStream_t s) {
     return cfg.RING ? launch_cfg<FMT, P_, W_, D_, true>(kp, s) : launch_cfg<FMT, P_, W_, D_, false>(kp, s);
   Q4_CFG(1, 4, 4)
   Q4_CFG(2, 4, 4)
+  Q4_CFG(2, 8, 2)
   Q4_CFG(2, 8, 4)
   Q4_CFG(4, 4, 4)
   Q4_CFG(4, 8, 4)
@@ -398,7 +399,10 @@ GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
   // needed for the staged activations to fit in LDS.
   c.P = 2;
   c.W = 8;
-  c.D = npanels >= 4096 ? 8 : 4;  // long streams: more bytes in flight per wave
+  // tiles in flight per wave: more is not better here; measured on one
+  // MI355X, 2 (37 KB per CU) beats 4 for the 44 MB affine matrices and 4
+  // beats 8 for the 415 MB lm_head; the ring below uses 4
+  c.D = npanels >= 4096 ? 4 : 2;
   auto shape = [&](int KS) {
     GemmCfg x = c;
     x.KS = KS;
@@ -422,8 +426,9 @@ GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N) {
   c = shape(KS);
   c.RING = 0;
   if (ring_ok && M > 8 && c.KW == c.W && c.PB == c.P &&
-      gemm_lds_bytes(M, ntiles, c.KW, c.PB, true, c.W, c.D) <= kGemmLdsMax) {
+      gemm_lds_bytes(M, ntiles, c.KW, c.PB, true, c.W, 4) <= kGemmLdsMax) {
     c.RING = 1;
+    c.D = 4;
     return c;
   }
   while (!fits(c) && KS < kMaxKS && KS < ntiles) c = shape(++KS);

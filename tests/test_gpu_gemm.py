@@ -25,7 +25,9 @@ CFGS = ["1,4,4,1,1,4", "1,4,4,3,1,8", "2,4,4,1,1,8", "2,4,4,4,1,8", "2,8,4,1,1,1
         "4,8,4,1,2,16",
         # activations moved by each wave into its own LDS ring
         "2,8,4,1,8,2,1", "2,8,4,2,4,4,1", "1,4,4,3,2,2,1", "4,8,4,1,2,8,1", "2,4,8,1,1,8,1", "4,4,6,2,1,16,1",
-        "2,4,4,1,1,16,1"]
+        "2,4,4,1,1,16,1",
+        # two tiles in flight
+        "2,8,2,1,4,4", "2,8,2,2,2,8", "2,8,2,1,1,16"]
 
 
 def q4():
