@@ -273,16 +273,16 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
       atomicMax(g.keys + threadIdx.x, sbest[threadIdx.x]);
     wait_stores();  // the key atomics have been performed
     __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned prev = count_arrival(g.counter);
-      if (prev == static_cast<unsigned>(kp.nblocks - 1)) {
-        // keys are read with atomics, which act at the coherence point
-        for (int m = 0; m < M; ++m) {
-          const unsigned long long k = atomicExch(g.keys + m, 0ull);
-          g.argmax[m] = k == 0ull ? -1 : static_cast<int>(0xFFFFFFFFu - static_cast<unsigned>(k & 0xFFFFFFFFull));
-        }
-        atomicExch(g.counter, 0u);
+    if (threadIdx.x == 0) s_last = count_arrival(g.counter) == static_cast<unsigned>(kp.nblocks - 1);
+    __syncthreads();
+    if (s_last) {
+      // the last workgroup: one thread per row reads (and clears) its key
+      // with an atomic, which acts at the coherence point; all rows at once
+      if (static_cast<int>(threadIdx.x) < M) {
+        const unsigned long long k = atomicExch(g.keys + threadIdx.x, 0ull);
+        g.argmax[threadIdx.x] = k == 0ull ? -1 : static_cast<int>(0xFFFFFFFFu - static_cast<unsigned>(k & 0xFFFFFFFFull));
       }
+      if (threadIdx.x == 0) atomicExch(g.counter, 0u);
     }
   }
 }
