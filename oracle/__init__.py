@@ -18,7 +18,8 @@ Pages cited:
             64-value group sums, tree_round's argmax), "Gates" (float64 bound).
   [DOC]     TensorSharp docs, Gemma 4 -- section 3.2 "Per-layer (MoE)",
             4.6 "MoE" (router matmul, softmax, top-k, weighted sum of
-            experts), 14 "Completed: Expert-batched FFN (GEGLU)".
+            experts), 4.8 "Logit softcap", 14 "Completed: Expert-batched
+            FFN (GEGLU)".
 """
 from .formats import (e2m1_value, e4m3_value, unpack_nibbles, nvfp4_dequant,
                       nvfp4_dequant_f32, bf16_value, affine_dequant, affine_dequant_f32)
@@ -26,11 +27,14 @@ from .gemm import (gemm_ref, gemm_abs_bound, nvfp4_gemm_ref, affine_gemm_ref,
                    affine_gemm_groupsum, argmax_ref)
 from .moe import (gelu_tanh, gelu_tanh_deriv, softmax, route_topk, moe_ref,
                   moe_ref_grouped, moe_abs_bound)
+from .sampling import (philox4, uniform_bits_to_f32, sample_uniforms, gumbel, softcap,
+                       sample_scores, sample_tokens)
 
 __all__ = [
     "e2m1_value", "e4m3_value", "unpack_nibbles", "nvfp4_dequant", "nvfp4_dequant_f32",
     "bf16_value", "affine_dequant", "affine_dequant_f32", "gemm_ref", "gemm_abs_bound",
     "nvfp4_gemm_ref", "affine_gemm_ref", "affine_gemm_groupsum", "argmax_ref",
     "gelu_tanh", "gelu_tanh_deriv", "softmax", "route_topk", "moe_ref", "moe_ref_grouped",
-    "moe_abs_bound",
+    "moe_abs_bound", "philox4", "uniform_bits_to_f32", "sample_uniforms", "gumbel", "softcap",
+    "sample_scores", "sample_tokens",
 ]
