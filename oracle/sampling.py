@@ -16,7 +16,9 @@ from Philox4x32-10, a counter-based generator with a published definition
 3", SC 2011), so that the GPU can draw them inside the lm_head kernel and
 the oracle can draw the very same bits:
   key     = (seed mod 2^32, seed >> 32)
-  counter = (n // 4, m, offset, 0), word n % 4 of the output for column n
+  counter = (n, m // 4, offset, 0), word m % 4 of the output for row m
+            (one generator call gives the noise of four rows of a column,
+            the rows an MFMA accumulator lane holds)
   U       = (2 (x >> 9) + 1) 2^-24, in (0, 1), exact in float32
   G       = -ln(-ln U)
   token   = argmax_n (z[m, n] / T + G[m, n]) for T > 0, argmax_n z for T = 0,
@@ -97,15 +99,16 @@ def uniform_bits_to_f32(x: np.ndarray) -> np.ndarray:
 
 def sample_uniforms(seed: int, offset: int, M: int, N: int) -> np.ndarray:
     """U[m][n] (float32) for the lm_head's noise, as read by the kernel."""
-    n4 = np.arange((N + 3) // 4, dtype=np.uint32)
-    mm = np.arange(M, dtype=np.uint32)
-    c0 = np.broadcast_to(n4[None, :], (M, n4.size))
-    c1 = np.broadcast_to(mm[:, None], (M, n4.size))
-    c2 = np.full((M, n4.size), offset & 0xFFFFFFFF, np.uint32)
-    c3 = np.zeros((M, n4.size), np.uint32)
+    M4 = (M + 3) // 4
+    nn = np.arange(N, dtype=np.uint32)
+    m4 = np.arange(M4, dtype=np.uint32)
+    c0 = np.broadcast_to(nn[None, :], (M4, N))
+    c1 = np.broadcast_to(m4[:, None], (M4, N))
+    c2 = np.full((M4, N), offset & 0xFFFFFFFF, np.uint32)
+    c3 = np.zeros((M4, N), np.uint32)
     key = (np.uint32(seed & 0xFFFFFFFF), np.uint32((seed >> 32) & 0xFFFFFFFF))
-    x = philox4((c0, c1, c2, c3), key, bits=32)
-    words = np.stack(x, axis=-1).reshape(M, -1)[:, :N]
+    x = philox4((c0, c1, c2, c3), key, bits=32)          # word r of block (m4, n) -> row 4 m4 + r
+    words = np.stack(x, axis=1).reshape(4 * M4, N)[:M]
     return uniform_bits_to_f32(words)
 
 

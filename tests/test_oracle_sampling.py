@@ -60,12 +60,12 @@ def test_uniform_map_range_and_exactness():
 
 
 def test_sample_uniforms_layout():
-    seed, off, M, N = 0x0123456789ABCDEF, 77, 3, 10
+    seed, off, M, N = 0x0123456789ABCDEF, 77, 6, 10
     u = S.sample_uniforms(seed, off, M, N)
     assert u.shape == (M, N)
     for m in range(M):
         for n in range(N):
-            w = S.philox4((n // 4, m, off, 0), (seed & 0xFFFFFFFF, seed >> 32), bits=32)[n % 4]
+            w = S.philox4((n, m // 4, off, 0), (seed & 0xFFFFFFFF, seed >> 32), bits=32)[m % 4]
             assert u[m, n] == S.uniform_bits_to_f32(np.array([int(w)], np.uint32))[0]
     assert not np.array_equal(u, S.sample_uniforms(seed, off + 1, M, N))
     assert not np.array_equal(u, S.sample_uniforms(seed + 1, off, M, N))
