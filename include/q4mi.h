@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define Q4MI_ABI_VERSION 1
+#define Q4MI_ABI_VERSION 2
 
 enum {
   Q4_OK = 0,
@@ -143,6 +143,27 @@ int qgemm_nvfp4(const void* w_packed, float global_scale, const void* a, int M, 
                 int64_t N, void* out, int out_dtype, int32_t* argmax, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* NVFP4 lm_head with fused sampling: the GEMM of qgemm_nvfp4, then per row
+ * one token.  [DOC 4.8 "Logit softcap"]: z = softcap * tanh(y / softcap) if
+ * softcap > 0, else z = y.  [README "Everything it has"]: temperature
+ * sampling by the Gumbel-max trick, temperature 0 being greedy:
+ *   token[m] = argmax_n (z[m][n] / temperature + G[m][n])   (temperature > 0)
+ *   token[m] = argmax_n z[m][n]                              (temperature == 0)
+ * in fp32, lowest index on ties, NaN scores skipped (-1 if all are NaN).
+ * G = -ln(-ln U), U = (2 (x >> 9) + 1) 2^-24 from Philox4x32-10 (Salmon et
+ * al., SC 2011) with key (seed & 0xffffffff, seed >> 32), counter (n, m / 4,
+ * offset, 0), word m % 4.  Advance `offset` (or change the seed) per step.
+ *   logits   device [M][N] of out_dtype (Q4_F32, Q4_F16, Q4_BF16) receiving z,
+ *            or NULL to skip storing the logits
+ *   token    device int32[M]
+ *   ws       as for qgemm_nvfp4 with want_argmax = 1
+ * Errors: as qgemm_nvfp4; INVALID_ARG also for temperature < 0, NaN or inf,
+ * a NaN or infinite softcap, or a NULL token. */
+int qgemm_nvfp4_sample(const void* w_packed, float global_scale, const void* a, int M, int64_t K,
+                       int64_t N, float softcap, float temperature, uint64_t seed, uint32_t offset,
+                       void* logits, int out_dtype, int32_t* token, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* MLX-style affine 4-bit W4A16 GEMM [ISSUE "Why now": qlinear's affine
  * path in groups of 64 with activation group sums].  w = q*scale + bias per
  * 64 weights along K; the product is computed as
@@ -222,6 +243,10 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
 /* ---------------------------------------------------------------------------
  * Test exports: the same device dequantization the GEMMs use, written out.
  * ------------------------------------------------------------------------- */
+
+/* out[m][n] (device fp32 [M][N]) = the uniform U that qgemm_nvfp4_sample
+ * draws for row m, column n with this seed and offset. */
+int q4_sample_uniforms(uint64_t seed, uint32_t offset, int M, int64_t N, float* out, void* stream);
 
 /* out[n][k] (device fp32 [N][K]) = fp32(e2m1 * e4m3 * g) from the packed matrix. */
 int q4_dequant_nvfp4(const void* w_packed, float global_scale, int64_t N, int64_t K, float* out,

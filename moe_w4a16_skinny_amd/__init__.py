@@ -46,6 +46,9 @@ _SIGS = {
     "q4_affine4_unpack": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "qgemm_nvfp4_workspace_bytes": (_sz, [_i32, _i64, _i64, _i32]),
     "qgemm_nvfp4": (_i32, [_vp, _f32, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "qgemm_nvfp4_sample": (_i32, [_vp, _f32, _vp, _i32, _i64, _i64, _f32, _f32, C.c_uint64, C.c_uint32, _vp, _i32,
+                                  _vp, _vp, _sz, _vp]),
+    "q4_sample_uniforms": (_i32, [C.c_uint64, C.c_uint32, _i32, _i64, _vp, _vp]),
     "qgemm_affine4_workspace_bytes": (_sz, [_i32, _i64, _i64]),
     "qgemm_affine4": (_i32, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _sz, _vp]),
     "moe_route_workspace_bytes": (_sz, [_i32, _i32, _i32]),
@@ -206,6 +209,34 @@ def qgemm_nvfp4(w_packed, global_scale: float, a, N: int, out=None, out_dtype=No
     _check(_lib.qgemm_nvfp4(_tptr(w_packed), float(global_scale), _tptr(a), M, K, N, _tptr(out),
                             _dtype_code(out.dtype), _tptr(amax), _tptr(ws), wsb, _stream()))
     return (out, amax[:M]) if want_argmax else out
+
+
+def qgemm_nvfp4_sample(w_packed, global_scale: float, a, N: int, softcap: float = 0.0, temperature: float = 0.0,
+                       seed: int = 0, offset: int = 0, want_logits: bool = True, out_dtype=None):
+    """lm_head with fused sampling: (logits z [M][N] or None, token int32 [M]).
+
+    z = softcap * tanh(y / softcap) (softcap > 0); token = argmax(z / T + Gumbel
+    noise) for T > 0, argmax z for T = 0."""
+    torch = _torch()
+    M, K = a.shape
+    out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device) if want_logits else None
+    tok = torch.empty((16,), dtype=torch.int32, device=a.device)
+    wsb = _lib.qgemm_nvfp4_workspace_bytes(M, K, N, 1)
+    ws = workspace(wsb, a.device)
+    _check(_lib.qgemm_nvfp4_sample(_tptr(w_packed), float(global_scale), _tptr(a), M, K, N, float(softcap),
+                                   float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF,
+                                   _tptr(out), _dtype_code(out.dtype if out is not None else torch.float32),
+                                   _tptr(tok), _tptr(ws), wsb, _stream()))
+    return out, tok[:M]
+
+
+def q4_sample_uniforms(seed: int, offset: int, M: int, N: int, device=None):
+    """The uniforms U[M][N] (fp32) that qgemm_nvfp4_sample draws (test export)."""
+    torch = _torch()
+    out = torch.empty((M, N), dtype=torch.float32, device=device or "cuda")
+    _check(_lib.q4_sample_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, M, N, _tptr(out),
+                                   _stream()))
+    return out
 
 
 def qgemm_affine4(w_packed, a, N: int, out=None, out_dtype=None):

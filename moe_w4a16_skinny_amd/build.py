@@ -1,6 +1,6 @@
 """Build libq4mi.so in-tree with hipcc for gfx950.
 
-    python -m moe_w4a16_skinny_amd.build
+    python moe_w4a16_skinny_amd/build.py   (a path, not -m: the package import would load the old library)
 """
 from __future__ import annotations
 

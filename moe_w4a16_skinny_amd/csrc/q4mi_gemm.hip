@@ -105,12 +105,66 @@ __device__ __forceinline__ unsigned long long max_key_64(unsigned long long k) {
   return k;
 }
 
+// ---- fused sampling ---------------------------------------------------------
+// [TensorSharp docs, Gemma 4, 4.8 "Logit softcap"]: z = cap tanh(y / cap).
+// [gemma-cuda-hybrid README, "Everything it has"]: temperature sampling by
+// the Gumbel-max trick (temperature 0: greedy).  The noise generator is
+// Philox4x32-10 (Salmon et al., SC 2011): key (seed lo, seed hi), counter
+// (column n, row / 4, offset, 0), word row % 4; U = (2 (x >> 9) + 1) 2^-24 in
+// (0, 1), exact in fp32; G = -ln(-ln U).  One call gives the four rows of a
+// column that an MFMA accumulator lane holds.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, unsigned k0, unsigned k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const unsigned hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const unsigned hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+__device__ __forceinline__ float uniform_of(unsigned x) {
+  return static_cast<float>(((x >> 9) << 1) | 1u) * 0x1p-24f;  // exact: an odd integer < 2^24, times 2^-24
+}
+// -ln(-ln U) with the hardware base-2 log (1 ulp over the whole U grid,
+// including next to 1, measured on MI355X): a few 1e-6 absolute
+__device__ __forceinline__ float gumbel_of(float u) {
+  constexpr float kLn2 = 0.69314718055994531f;
+  const float t = -__builtin_amdgcn_logf(u) * kLn2;  // -ln U > 0
+  return -__builtin_amdgcn_logf(t) * kLn2;
+}
+// cap tanh(y / cap) as cap (1 - 2 / (1 + e^(2y/cap))): exp2 and a reciprocal,
+// a few 1e-7 absolute in tanh; saturates to +-cap
+__device__ __forceinline__ float softcap_of(float y, float cap) {
+  const float e = __builtin_amdgcn_exp2f(y * (2.8853900817779268f / cap));  // e^(2 y / cap)
+  return cap * (1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e));
+}
+// the sampling key of row m, column n from the final logit y
+__device__ __forceinline__ unsigned long long sample_key(const GemmArgs& g, float y, float noise, int n) {
+  const float z = g.softcap > 0.f ? softcap_of(y, g.softcap) : y;
+  const float sc = g.inv_temp > 0.f ? fmaf(z, g.inv_temp, noise) : z;
+  return argmax_key(sc, n);
+}
+// noise of rows 4 q .. 4 q + 3 of column n (all 0 when greedy)
+__device__ __forceinline__ f32x4 gumbel4(const GemmArgs& g, int n, int q) {
+  if (!(g.inv_temp > 0.f)) return f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 x = philox4x32_10(u32x4{static_cast<unsigned>(n), static_cast<unsigned>(q), g.offset, 0u}, g.seed_lo,
+                                g.seed_hi);
+  return f32x4{gumbel_of(uniform_of(x.x)), gumbel_of(uniform_of(x.y)), gumbel_of(uniform_of(x.z)),
+               gumbel_of(uniform_of(x.w))};
+}
+
 // RING: every wave moves its own tiles' activations into an LDS ring
 // together with their weight loads (kARing) instead of the workgroup
 // staging its k-range up front; chosen when each wave streams a single panel
 // group, so that staging would save no re-reads and only hold back the first
 // tile's math until the whole range has landed.
-template <int FMT, int P, int W, int D, bool RING>
+// SAMPLE: the fused-sampling variant (qgemm_nvfp4_sample); the plain GEMM
+// kernels carry none of its code.
+template <int FMT, int P, int W, int D, bool RING, bool SAMPLE>
 __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
   // dynamic LDS: staged activations (+ zero row), or with RING the W rings
   // of D slots; then KW row-major result blocks [M][rs]
@@ -170,7 +224,31 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
     if constexpr (!RING) stage_wait<D * P * 2>();  // D tiles of P panels: codes + scales
   };
   auto col_of = [&](int gi) { return (pw + gi * PWv) * P * 16; };  // block-local first column
-  auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash_rows<P, false>(wres, rs, col_of(gi), M, acc); };
+  // sampling with final per-group results (one k-range, one k-split wave, no
+  // half tile added later): each lane ranks its 4 rows x P columns as soon as
+  // the group is done, during the stream, with one generator call per column
+  const bool keys_in_stream = SAMPLE && g.argmax && KS == 1 && KW == 1 && kp.half_t < 0;
+  unsigned long long skey[4] = {0ull, 0ull, 0ull, 0ull};  // rows 4 (lane >> 4) + r
+  auto epi = [&](int gi, f32x4 (&acc)[P][2]) {
+    stash_rows<P, false>(wres, rs, col_of(gi), M, acc);
+    if (SAMPLE && keys_in_stream) {
+      const int lane = threadIdx.x & 63, o = lane >> 4, c = lane & 15;
+      const int pan0 = p0 + (pw + gi * PWv) * P;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const f32x4 v = acc[p][0] + acc[p][1];  // the value the epilogue reads back
+        const int n = (pan0 + p) * 16 + c;
+        const f32x4 gn = gumbel4(g, n, o);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (pan0 + p < pend && 4 * o + r < M) {
+            const unsigned long long kk = sample_key(g, gs * v[r], gn[r], n);
+            skey[r] = kk > skey[r] ? kk : skey[r];
+          }
+        }
+      }
+    }
+  };
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_rows<P, true>(wres, rs, col_of(gi), M, acc); };
   const ALds al = alds_view(reinterpret_cast<const char*>(lds), KRg, M, wt0);
   const ARing rg = aring_view(lds_offset(lds) + static_cast<unsigned>(w * D * kRingSlot));
@@ -186,6 +264,12 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
     for (int gi = 0; gi < ng; ++gi) stash_rows<P, false>(wres, rs, col_of(gi), M, z);
   }
   __syncthreads();
+  if (SAMPLE && keys_in_stream) {
+    const int o = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (skey[r] != 0ull) atomicMax(&sbest[4 * o + r], skey[r]);
+  }
 
   // Epilogue over the block's outputs, row-major in 4-column groups: every
   // thread sums the KW k-slices of its group, then stores 4 outputs (or 4
@@ -195,7 +279,26 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
   // q nc4 < 2^32, which the launch checks)
   const unsigned row_magic = pb == kp.nblocks - 1 ? kp.nc4_magic_last : kp.nc4_magic;
   auto item_row = [&](int q) { return static_cast<int>(__umulhi(static_cast<unsigned>(q), row_magic)); };
-  const int items = M * nc4;
+  // sampling: store the softcapped logits (if wanted) and, unless the keys
+  // were taken in the stream, rank the 4 columns (one generator call each,
+  // word m % 4)
+  auto finish_sample = [&](int m, int n, size_t off, f32x4 y, bool with_keys, unsigned long long& key) {
+    f32x4 z = y;
+    if (g.softcap > 0.f) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[j] = softcap_of(y[j], g.softcap);
+    }
+    if (g.out) (void)store_out4(g.out, g.out_dtype, off, z);
+    if (with_keys && g.argmax) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float noise = gumbel4(g, n + j, m >> 2)[m & 3];
+        const unsigned long long kj = sample_key(g, y[j], noise, n + j);
+        key = kj > key ? kj : key;
+      }
+    }
+  };
+  const int items = (SAMPLE && !g.out && keys_in_stream) ? 0 : M * nc4;
   const bool wave_rows = (nc4 & 63) == 0;  // each wave-wide batch of items lies in one row
   for (int q0 = 0; q0 < items; q0 += 64 * W) {
     const int q = q0 + static_cast<int>(threadIdx.x);
@@ -210,12 +313,16 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
       const int n = p0 * 16 + c4 * 4;
       const size_t off = static_cast<size_t>(m) * g.N + n;
       if (KS == 1) {
-        const f32x4 y = store_out4(g.out, g.out_dtype, off, gs * v);
-        if (g.argmax) {
+        if constexpr (SAMPLE) {
+          finish_sample(m, n, off, gs * v, !keys_in_stream, key);
+        } else {
+          const f32x4 y = store_out4(g.out, g.out_dtype, off, gs * v);
+          if (g.argmax) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const unsigned long long kj = argmax_key(y[j], n + j);
-            key = kj > key ? kj : key;
+            for (int j = 0; j < 4; ++j) {
+              const unsigned long long kj = argmax_key(y[j], n + j);
+              key = kj > key ? kj : key;
+            }
           }
         }
       } else {
@@ -252,16 +359,20 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
         f32x4 sacc = v[0];
 #pragma unroll
         for (int j = 1; j < kMaxKS; ++j) sacc += v[j];
-        const f32x4 y = store_out4(g.out, g.out_dtype, off, gs * sacc);
-        if (g.argmax) {
-          unsigned long long key = 0ull;
+        unsigned long long key = 0ull;
+        if constexpr (SAMPLE) {
+          finish_sample(m, n, off, gs * sacc, true, key);
+        } else {
+          const f32x4 y = store_out4(g.out, g.out_dtype, off, gs * sacc);
+          if (g.argmax) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const unsigned long long kj = argmax_key(y[j], n + j);
-            key = kj > key ? kj : key;
+            for (int j = 0; j < 4; ++j) {
+              const unsigned long long kj = argmax_key(y[j], n + j);
+              key = kj > key ? kj : key;
+            }
           }
-          if (key) atomicMax(&sbest[m], key);
         }
+        if (g.argmax && key) atomicMax(&sbest[m], key);
       }
       if (threadIdx.x == 0) atomicExch(kp.bcnt + pb, 0u);
     }
@@ -285,6 +396,18 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
       if (threadIdx.x == 0) atomicExch(g.counter, 0u);
     }
   }
+}
+
+// ---- test export: the sampling noise's uniforms -------------------------------
+__global__ __launch_bounds__(256) void sample_uniforms_kernel(GemmArgs g, int M, int N, float* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x, q = blockIdx.y;  // rows 4 q .. 4 q + 3
+  if (n >= N) return;
+  const u32x4 x = philox4x32_10(u32x4{static_cast<unsigned>(n), static_cast<unsigned>(q), g.offset, 0u}, g.seed_lo,
+                                g.seed_hi);
+  const unsigned w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (4 * q + r < M) out[static_cast<size_t>(4 * q + r) * N + n] = uniform_of(w[r]);
 }
 
 // ---- test export: write out the dequantized weights -----------------------
@@ -338,12 +461,12 @@ __global__ __launch_bounds__(64) void dequant_kernel(const uint8_t* __restrict__
 }
 
 
-template <int FMT, int P, int W, int D, bool RING>
+template <int FMT, int P, int W, int D, bool RING, bool SAMPLE>
 int launch_cfg(const GemmParams& kp, hipStream_t s) {
   const size_t lds = gemm_lds_bytes(kp.g.M, kp.KR, kp.KW, kp.PB, RING, W, D);
   static size_t lds_allowed = 48 * 1024;  // per instantiation: raise the dynamic LDS limit on demand
   if (lds > lds_allowed) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_kernel<FMT, P, W, D, RING>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_kernel<FMT, P, W, D, RING, SAMPLE>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the next call
@@ -351,15 +474,15 @@ int launch_cfg(const GemmParams& kp, hipStream_t s) {
     }
     lds_allowed = lds;
   }
-  hipLaunchKernelGGL((qgemm_kernel<FMT, P, W, D, RING>), dim3(kp.nblocks * kp.KS), dim3(64 * W), lds, s, kp);
+  hipLaunchKernelGGL((qgemm_kernel<FMT, P, W, D, RING, SAMPLE>), dim3(kp.nblocks * kp.KS), dim3(64 * W), lds, s, kp);
   return static_cast<int>(hipGetLastError());
 }
 
-template <int FMT>
+template <int FMT, bool SAMPLE>
 int launch_fmt(const GemmParams& kp, const GemmCfg& cfg, hipStream_t s) {
 #define Q4_CFG(P_, W_, D_) \
   if (cfg.P == P_ && cfg.W == W_ && cfg.D == D_)              \
-    return cfg.RING ? launch_cfg<FMT, P_, W_, D_, true>(kp, s) : launch_cfg<FMT, P_, W_, D_, false>(kp, s);
+    return cfg.RING ? launch_cfg<FMT, P_, W_, D_, true, SAMPLE>(kp, s) : launch_cfg<FMT, P_, W_, D_, false, SAMPLE>(kp, s);
   Q4_CFG(1, 4, 4)
   Q4_CFG(2, 4, 4)
   Q4_CFG(2, 8, 2)
@@ -490,7 +613,19 @@ int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* 
   if (gemm_lds_bytes(g.M, kp.KR, kp.KW, kp.PB, cfg.RING != 0, cfg.W, cfg.D) > kGemmLdsMax)
     return static_cast<int>(hipErrorInvalidConfiguration);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return fmt == kNvfp4 ? launch_fmt<kNvfp4>(kp, cfg, s) : launch_fmt<kAffine>(kp, cfg, s);
+  if (fmt != kNvfp4) return g.sample ? static_cast<int>(hipErrorInvalidConfiguration) : launch_fmt<kAffine, false>(kp, cfg, s);
+  return g.sample ? launch_fmt<kNvfp4, true>(kp, cfg, s) : launch_fmt<kNvfp4, false>(kp, cfg, s);
+}
+
+int launch_sample_uniforms(unsigned seed_lo, unsigned seed_hi, unsigned offset, int M, int64_t N, float* out,
+                           void* stream) {
+  GemmArgs g{};
+  g.seed_lo = seed_lo;
+  g.seed_hi = seed_hi;
+  g.offset = offset;
+  hipLaunchKernelGGL(sample_uniforms_kernel, dim3(static_cast<unsigned>((N + 255) / 256), (M + 3) / 4), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), g, M, static_cast<int>(N), out);
+  return static_cast<int>(hipGetLastError());
 }
 
 int launch_dequant(int fmt, const uint8_t* w, int64_t pb, int64_t N, int64_t K, float gsc, float* out,

@@ -252,12 +252,23 @@ size_t qgemm_affine4_workspace_bytes(int M, int64_t K, int64_t N) {
   return b > kWsCounterBytes ? b : 0;
 }
 
+struct SampleSpec {  // qgemm_nvfp4_sample's extra arguments
+  float softcap, temperature;
+  uint64_t seed;
+  uint32_t offset;
+};
+
 static int gemm_common(int fmt, const char* fn, const void* w_packed, float gscale, const void* a, int M,
                        int64_t K, int64_t N, void* out, int out_dtype, int32_t* argmax, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream, const SampleSpec* sp = nullptr) {
   if (!w_packed) return fail(Q4_ERR_INVALID_ARG, "%s: w_packed is NULL", fn);
   if (!a) return fail(Q4_ERR_INVALID_ARG, "%s: a is NULL", fn);
-  if (!out) return fail(Q4_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  if (!out && !sp) return fail(Q4_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  if (sp && !argmax) return fail(Q4_ERR_INVALID_ARG, "%s: token is NULL", fn);
+  if (sp && !(sp->temperature >= 0.0f && sp->temperature <= 3.0e38f))
+    return fail(Q4_ERR_INVALID_ARG, "%s: temperature=%g is not a finite number >= 0", fn, double(sp->temperature));
+  if (sp && !(sp->softcap <= 3.0e38f))  // NaN or inf
+    return fail(Q4_ERR_INVALID_ARG, "%s: softcap=%g is not finite", fn, double(sp->softcap));
   if (M < 1 || M > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: M=%d outside 1..16 (skinny GEMM only)", fn, M);
   if (int rc = check_nk(fn, N, K, fmt == kNvfp4 ? 16 : 64)) return rc;
   if (fmt == kNvfp4 && out_dtype != Q4_F32 && out_dtype != Q4_F16 && out_dtype != Q4_BF16)
@@ -266,7 +277,7 @@ static int gemm_common(int fmt, const char* fn, const void* w_packed, float gsca
     return fail(Q4_ERR_INVALID_ARG, "%s: out_dtype=%d is not Q4_F32 or Q4_BF16", fn, out_dtype);
   if (!aligned16(w_packed)) return fail(Q4_ERR_ALIGNMENT, "%s: w_packed is not 16-byte aligned", fn);
   if (!aligned16(a)) return fail(Q4_ERR_ALIGNMENT, "%s: a is not 16-byte aligned", fn);
-  if (!aligned16(out)) return fail(Q4_ERR_ALIGNMENT, "%s: out is not 16-byte aligned", fn);
+  if (out && !aligned16(out)) return fail(Q4_ERR_ALIGNMENT, "%s: out is not 16-byte aligned", fn);
   const size_t need = fmt == kNvfp4 ? qgemm_nvfp4_workspace_bytes(M, K, N, argmax != nullptr)
                                     : qgemm_affine4_workspace_bytes(M, K, N);
   if (need) {
@@ -291,6 +302,14 @@ static int gemm_common(int fmt, const char* fn, const void* w_packed, float gsca
   g.argmax = argmax;
   g.counter = argmax ? reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsArgmaxCounter) : nullptr;
   g.keys = argmax ? reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + kWsArgmaxKeys) : nullptr;
+  if (sp) {
+    g.sample = 1;
+    g.softcap = sp->softcap > 0.0f ? sp->softcap : 0.0f;
+    g.inv_temp = sp->temperature > 0.0f ? static_cast<float>(1.0 / double(sp->temperature)) : 0.0f;
+    g.seed_lo = static_cast<unsigned>(sp->seed & 0xFFFFFFFFu);
+    g.seed_hi = static_cast<unsigned>(sp->seed >> 32);
+    g.offset = sp->offset;
+  }
   const GemmCfg cfg = choose_gemm_cfg(fmt, M, K, N);
   if (int e = launch_gemm(fmt, g, cfg, ws, stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
@@ -301,6 +320,24 @@ int qgemm_nvfp4(const void* w_packed, float global_scale, const void* a, int M, 
                 int out_dtype, int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
   return gemm_common(kNvfp4, __func__, w_packed, global_scale, a, M, K, N, out, out_dtype, argmax, ws, ws_bytes,
                      stream);
+}
+
+int qgemm_nvfp4_sample(const void* w_packed, float global_scale, const void* a, int M, int64_t K, int64_t N,
+                       float softcap, float temperature, uint64_t seed, uint32_t offset, void* logits, int out_dtype,
+                       int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+  const SampleSpec sp{softcap, temperature, seed, offset};
+  return gemm_common(kNvfp4, __func__, w_packed, global_scale, a, M, K, N, logits, out_dtype, token, ws, ws_bytes,
+                     stream, &sp);
+}
+
+int q4_sample_uniforms(uint64_t seed, uint32_t offset, int M, int64_t N, float* out, void* stream) {
+  REQUIRE_PTR(out);
+  if (M < 1 || N < 1 || N > (int64_t(1) << 31) - 1 || int64_t(M) * N > (int64_t(1) << 40))
+    return fail(Q4_ERR_UNSUPPORTED, "%s: M=%d N=%lld out of range", __func__, M, (long long)N);
+  if (int e = launch_sample_uniforms(static_cast<unsigned>(seed & 0xFFFFFFFFu), static_cast<unsigned>(seed >> 32),
+                                     offset, M, N, out, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
 }
 
 int qgemm_affine4(const void* w_packed, const void* a, int M, int64_t K, int64_t N, void* out, int out_dtype,

@@ -67,6 +67,13 @@ struct GemmArgs {
   int32_t* argmax;           // nullable
   unsigned* counter;         // argmax workspace: completion counter
   unsigned long long* keys;  // argmax workspace: per-row packed (value, index) keys
+  // fused sampling (qgemm_nvfp4_sample): z = softcap(g acc) is what gets
+  // stored (out may be null) and the row keys rank z / T + Gumbel noise, or
+  // z itself for T = 0, in fp32
+  int sample;
+  float softcap;             // > 0: z = softcap tanh(y / softcap)
+  float inv_temp;            // 1 / T, 0 for greedy
+  unsigned seed_lo, seed_hi, offset;
 };
 
 struct GemmCfg {
@@ -85,6 +92,8 @@ size_t gemm_workspace(int fmt, int M, int64_t K, int64_t N);
 int launch_gemm(int fmt, const GemmArgs& g, const GemmCfg& cfg, void* ws, void* stream);
 int launch_dequant(int fmt, const uint8_t* w, int64_t panel_bytes, int64_t N, int64_t K, float g,
                    float* out, void* stream);
+int launch_sample_uniforms(unsigned seed_lo, unsigned seed_hi, unsigned offset, int M, int64_t N, float* out,
+                           void* stream);
 
 // Router grid: (16-expert column blocks) x (splits of D), workgroups of
 // kRouteThreads threads (4 waves).  A workgroup computes the logits of its
