@@ -96,6 +96,11 @@ def traffic_for(workload, kind):
 
 # ------------------------------------------------------------------ workloads
 
+def torch_f32():
+    import torch
+    return torch.float32
+
+
 class GemmWork:
     def __init__(self, name, spec, hot):
         import numpy as np
@@ -131,12 +136,14 @@ class GemmWork:
         for i in range(self.copies):
             self.wbuf[i * self.stride:i * self.stride + nb].copy_(base)
         del base
-        out_dt = {"f32": torch.float32, "f16": torch.float16}[spec.get("out", "f32")]
-        self.out = torch.empty((M, N), dtype=out_dt, device="cuda")
-        self.want_argmax = bool(spec.get("argmax"))
+        self.sample = spec.get("sample")  # fused sampling: softcap, temperature; tokens only
+        out_kind = spec.get("out", "f32")
+        out_dt = {"f32": torch.float32, "f16": torch.float16, "none": torch.float32}[out_kind]
+        self.out = torch.empty((M, N), dtype=out_dt, device="cuda") if out_kind != "none" else None
+        self.want_argmax = bool(spec.get("argmax")) or bool(self.sample)
         self.amax = torch.empty(16, dtype=torch.int32, device="cuda")
         if spec["kind"] == "nvfp4":
-            self.wsb = q4.raw().qgemm_nvfp4_workspace_bytes(M, K, N, int(bool(spec.get("argmax"))))
+            self.wsb = q4.raw().qgemm_nvfp4_workspace_bytes(M, K, N, int(self.want_argmax))
         else:
             self.wsb = q4.raw().qgemm_affine4_workspace_bytes(M, K, N)
         self.ws = q4.workspace(max(self.wsb, 256))
@@ -151,7 +158,13 @@ class GemmWork:
         w = C.c_void_p(self.wbuf.data_ptr() + (self.i % self.copies) * self.stride)
         self.i += 1
         s = q4._stream()
-        if self.spec["kind"] == "nvfp4":
+        if self.sample:  # one offset per step, so that every step draws fresh noise
+            rc = lib.qgemm_nvfp4_sample(w, self.g, C.c_void_p(self.a.data_ptr()), self.M, self.K, self.N,
+                                        float(self.sample["softcap"]), float(self.sample["temperature"]),
+                                        0x5EED, self.i, None, q4._dtype_code(torch_f32()),
+                                        C.c_void_p(self.amax.data_ptr()), C.c_void_p(self.ws.data_ptr()),
+                                        self.ws.numel(), s)
+        elif self.spec["kind"] == "nvfp4":
             rc = lib.qgemm_nvfp4(w, self.g, C.c_void_p(self.a.data_ptr()), self.M, self.K, self.N,
                                  C.c_void_p(self.out.data_ptr()), q4._dtype_code(self.out.dtype),
                                  C.c_void_p(self.amax.data_ptr()) if self.want_argmax else None,
@@ -164,9 +177,12 @@ class GemmWork:
             q4._check(rc)
 
     def config(self):
-        return {"workload": self.name, "M": self.M, "K": self.K, "N": self.N,
-                "weights": self.spec["kind"], "out": self.spec.get("out", "f32"),
-                "fused_argmax": self.want_argmax, "weight_copies_rotated": self.copies}
+        c = {"workload": self.name, "M": self.M, "K": self.K, "N": self.N,
+             "weights": self.spec["kind"], "out": self.spec.get("out", "f32"),
+             "fused_argmax": self.want_argmax, "weight_copies_rotated": self.copies}
+        if self.sample:
+            c["fused_sampling"] = dict(self.sample, noise="Philox4x32-10 Gumbel-max, offset = step")
+        return c
 
     def cpu_oracle_sample(self, seconds):
         """Time the oracle on row blocks of the same weights for about `seconds`."""

@@ -326,6 +326,9 @@ WORKLOADS = {
     "nvfp4_verify_m16_k4096_n8192": dict(kind="nvfp4", seed=102, M=16, K=4096, N=8192, out="f16"),
     "nvfp4_lmhead_m16_k2816_n262144": dict(kind="nvfp4", seed=103, M=16, K=2816, N=262144,
                                            out="f32", argmax=True),
+    # the same lm_head with fused sampling: softcap 30, temperature 1, only the tokens kept
+    "nvfp4_lmhead_sample_m16_k2816_n262144": dict(kind="nvfp4", seed=103, M=16, K=2816, N=262144,
+                                                  out="none", sample=dict(softcap=30.0, temperature=1.0)),
     "moe_t16_d2816_e128s1_f704_top8": dict(kind="moe", seed=104, T=16, D=2816, E=128, F=704, k=8,
                                            has_shared=True),
     "affine4_m1_k5120_n15360": dict(kind="affine", seed=105, M=1, K=5120, N=15360, out="f32"),
