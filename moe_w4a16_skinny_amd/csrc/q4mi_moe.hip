@@ -27,6 +27,8 @@
 // expert index) and resets the counter.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "q4mi_tiles.h"
 
 namespace q4mi {
@@ -601,20 +603,22 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   const int npp = m.F / 16;
   const int nitems = G.nact * npp;
   const int gw = blockIdx.x + gridDim.x * w, NW = gridDim.x * W;
-  const int ng = min(items_of_wave(nitems, gw, NW), NGW);
+  // a wave's items go in chunks of at most NGW (its stash slots)
+  const int ntot = items_of_wave(nitems, gw, NW);
+  int c0 = 0, ng = 0;  // current chunk: items c0 .. c0 + ng
   const int nfull = static_cast<int>(full_tiles(m.D));
   const bool half = has_half_tile(m.D);
 
   const DivBy by_npp(static_cast<unsigned>(npp));
   auto item = [&](int gi, int& e, int& jp) {
-    int it = gw + gi * NW;
+    int it = gw + (c0 + gi) * NW;
     it = it < nitems ? it : nitems - 1;  // past the wave's items: in-bounds, never computed
     const int a = by_npp(it);
     jp = it - a * npp;
     e = G.act[a];
   };
   auto group = [&](int gi, GroupPtrs<2>& gp) {
-    prio_by_items_left(ng - gi);
+    prio_by_items_left(ntot - c0 - gi);
     int e, jp;
     item(gi, e, jp);
     gp.panel[0] = m.gate + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jp) * m.gate_panel_bytes;
@@ -627,21 +631,23 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   auto pre = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[2][2]) { stash<2>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[2][2]) { stash_add<2>(wout, gi, acc); };
-  if (nitems > 0)
-    stream_groups<kNvfp4, 2, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.D, group, pre,
-                                        pre, epi, epi_add);
-  for (int gi = 0; gi < ng; ++gi) {
-    int e, jp;
-    item(gi, e, jp);
-    const int me = min(G.cnt[e], 16), base = G.base[e];
-    const float gg = G.gs0[e], gu = G.gs1[e];
-    const f32x4 rg = wout[(gi * 2 + 0) * 64 + lane], ru = wout[(gi * 2 + 1) * 64 + lane];
+  for (; c0 < ntot; c0 += NGW) {
+    ng = min(NGW, ntot - c0);
+    stream_groups<kNvfp4, 2, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.D,
+                                          group, pre, pre, epi, epi_add);
+    for (int gi = 0; gi < ng; ++gi) {
+      int e, jp;
+      item(gi, e, jp);
+      const int me = min(G.cnt[e], 16), base = G.base[e];
+      const float gg = G.gs0[e], gu = G.gs1[e];
+      const f32x4 rg = wout[(gi * 2 + 0) * 64 + lane], ru = wout[(gi * 2 + 1) * 64 + lane];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * o + r;
-      if (row < me) {
-        const float h = gelu_tanh(gg * rg[r]) * (gu * ru[r]);
-        reinterpret_cast<_Float16*>(m.h)[static_cast<size_t>(base + row) * m.F + jp * 16 + c] = (_Float16)h;
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * o + r;
+        if (row < me) {
+          const float h = gelu_tanh(gg * rg[r]) * (gu * ru[r]);
+          reinterpret_cast<_Float16*>(m.h)[static_cast<size_t>(base + row) * m.F + jp * 16 + c] = (_Float16)h;
+        }
       }
     }
   }
@@ -663,20 +669,21 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   const int ngp = (npan + P - 1) / P;  // panel groups per expert
   const int nitems = G.nact * ngp;
   const int gw = blockIdx.x + gridDim.x * w, NW = gridDim.x * W;
-  const int ng = min(items_of_wave(nitems, gw, NW), NGW);
+  const int ntot = items_of_wave(nitems, gw, NW);  // in chunks of at most NGW, as in gate/up
+  int c0 = 0, ng = 0;
   const int nfull = static_cast<int>(full_tiles(m.F));
   const bool half = has_half_tile(m.F);
 
   const DivBy by_ngp(static_cast<unsigned>(ngp));
   auto item = [&](int gi, int& e, int& q) {
-    int it = gw + gi * NW;
+    int it = gw + (c0 + gi) * NW;
     it = it < nitems ? it : nitems - 1;
     const int a = by_ngp(it);
     q = it - a * ngp;
     e = G.act[a];
   };
   auto group = [&](int gi, GroupPtrs<P>& gp) {
-    prio_by_items_left(ng - gi);
+    prio_by_items_left(ntot - c0 - gi);
     int e, q;
     item(gi, e, q);
 #pragma unroll
@@ -692,26 +699,28 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   auto pre = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash<P>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
-  if (nitems > 0)
-    stream_groups<kNvfp4, P, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.F, group, pre,
-                                        pre, epi, epi_add);
   const int nrow = m.T * m.k + m.T;
-  for (int gi = 0; gi < ng; ++gi) {
-    int e, q;
-    item(gi, e, q);
-    const int me = min(G.cnt[e], 16), base = G.base[e];
-    const float gd = G.gs0[e];
-    float wp[4];
+  for (; c0 < ntot; c0 += NGW) {
+    ng = min(NGW, ntot - c0);
+    stream_groups<kNvfp4, P, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.F,
+                                          group, pre, pre, epi, epi_add);
+    for (int gi = 0; gi < ng; ++gi) {
+      int e, q;
+      item(gi, e, q);
+      const int me = min(G.cnt[e], 16), base = G.base[e];
+      const float gd = G.gs0[e];
+      float wp[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wp[r] = G.fac[min(base + 4 * o + r, nrow - 1)];
+      for (int r = 0; r < 4; ++r) wp[r] = G.fac[min(base + 4 * o + r, nrow - 1)];
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int pi = q * P + p;
-      const f32x4 v = wout[(gi * P + p) * 64 + lane];
+      for (int p = 0; p < P; ++p) {
+        const int pi = q * P + p;
+        const f32x4 v = wout[(gi * P + p) * 64 + lane];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * o + r;
-        if (pi < npan && row < me) m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wp[r] * (gd * v[r]);
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * o + r;
+          if (pi < npan && row < me) m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wp[r] * (gd * v[r]);
+        }
       }
     }
   }
@@ -770,13 +779,19 @@ int launch_moe(const MoeArgs& m, void* stream) {
   const int nexp = m.E + m.has_shared;
   constexpr int GU_W = 8, DN_P = 2, DN_W = 8, kWG = 256;  // one 8-wave workgroup per CU
   const int gu_nw = kWG * GU_W, dn_nw = kWG * DN_W;  // waves in the grid
+  // stash slots per wave (items parked until the wave's stream ends): as many
+  // as a wave has items at most, up to what 96 KiB of LDS holds; a wave with
+  // more items streams them in chunks of that many
+  constexpr size_t kStashLds = 96 * 1024;
   const int npp = m.F / 16;
-  const int gu_ngw = (nexp * npp + gu_nw - 1) / gu_nw;  // items per wave at most
+  const int gu_cap = static_cast<int>(kStashLds / (size_t(GU_W) * 2 * 64 * 16));
+  const int gu_ngw = std::min((nexp * npp + gu_nw - 1) / gu_nw, gu_cap);
   const size_t gu_lds = static_cast<size_t>(GU_W) * gu_ngw * 2 * 64 * 16;
   const int ngp = (m.D / 16 + DN_P - 1) / DN_P;
-  const int dn_ngw = (nexp * ngp + dn_nw - 1) / dn_nw;
+  const int dn_cap = static_cast<int>(kStashLds / (size_t(DN_W) * DN_P * 64 * 16));
+  const int dn_ngw = std::min((nexp * ngp + dn_nw - 1) / dn_nw, dn_cap);
   const size_t dn_lds = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
-  if (gu_lds > 96 * 1024 || dn_lds > 96 * 1024) return static_cast<int>(hipErrorInvalidConfiguration);
+  if (gu_ngw < 1 || dn_ngw < 1) return static_cast<int>(hipErrorInvalidConfiguration);
   static size_t gu_allowed = 48 * 1024, dn_allowed = 48 * 1024;
   if (gu_lds > gu_allowed) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4>),

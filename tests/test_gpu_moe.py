@@ -183,6 +183,15 @@ def test_moe_small_layers(T, D, E, F, k, shared):
     check_moe(moe, mw, idx, w, what=f"T={T} D={D} E={E} F={F} k={k} shared={shared}")
 
 
+@pytest.mark.parametrize("D,F", [(128, 3072), (6144, 64)])
+def test_moe_more_items_than_stash_slots(D, F):
+    # 65 experts x 192 panel items > 6 stash slots x 2048 waves: waves stream
+    # their items in two chunks (gate/up for F = 3072, down for D = 6144)
+    moe, mw = layer(970 + D + F, T=4, D=D, E=64, F=F, k=2, has_shared=True)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    check_moe(moe, mw, idx, w, what=f"D={D} F={F}: items in chunks")
+
+
 def test_moe_token_names_expert_twice():
     # not something a top-k router produces, but the layer takes any index
     # table: both pairs count (the grouping then ranks pairs without the
