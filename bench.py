@@ -73,7 +73,8 @@ def sources_sha256(kind):
     """Hash of the kernel sources a workload runs (traffic figures are tied to it)."""
     import hashlib
     csrc = os.path.join(ROOT, "moe_w4a16_skinny_amd", "csrc")
-    names = ["q4mi_tiles.h", "q4mi_internal.h"] + (["q4mi_moe.hip"] if kind == "moe" else ["q4mi_gemm.hip"])
+    names = ["q4mi_tiles.h", "q4mi_internal.h"] + [{"moe": "q4mi_moe.hip", "quant": "q4mi_quant.hip"}
+                                                   .get(kind, "q4mi_gemm.hip")]
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(csrc, n), "rb") as f:
@@ -268,6 +269,67 @@ class MoeWork:
         return self.alg_bytes / el / 1e9, f"1 full oracle layer (router + {self.active}+1 experts, T={m.T}) in {el:.1f}s"
 
 
+class QuantWork:
+    """One step = q4_nvfp4_quantize of an fp32 [N][K] matrix with the global
+    scale taken from its amax: a pass for the amax, a pass that quantizes and
+    writes the packed layout."""
+
+    def __init__(self, name, spec, hot):
+        import torch
+
+        import moe_w4a16_skinny_amd as q4
+        import synth
+        self.name, self.spec, self.q4 = name, spec, q4
+        N, K = spec["N"], spec["K"]
+        self.N, self.K = N, K
+        t0 = time.time()
+        w = synth.normal_f32(spec["seed"], synth.TAG_WEIGHT, N, K, spec["std"])
+        self.w_host = w
+        self.w = torch.from_numpy(w).cuda()  # N * K * 4 bytes >= 2 GiB at the tied-embedding size: no rotation
+        log(f"[bench] {name}: matrix generated in {time.time() - t0:.1f}s")
+        self.nb = q4.q4_nvfp4_packed_bytes(N, K)
+        self.packed = torch.empty((self.nb,), dtype=torch.uint8, device="cuda")
+        self.g = torch.empty((1,), dtype=torch.float32, device="cuda")
+        self.wsb = q4.raw().q4_nvfp4_quantize_workspace_bytes()
+        self.ws = q4.workspace(self.wsb)
+        # algorithmic bytes: the amax pass reads w; the quantizing pass reads w
+        # again and writes codes (K/2 per row) and scales (K/16 per row)
+        self.alg_bytes = 2 * N * K * 4 + N * K // 2 + N * K // 16 + 4
+        self.kind = "quant"
+        self.kernel_names = ["quantize step: quant_zero_kernel + quant_amax_kernel + quant_pack_kernel"]
+        self.dtype = "f32"
+        self.copies = 1
+
+    def step(self):
+        import ctypes as C
+        q4 = self.q4
+        rc = q4.raw().q4_nvfp4_quantize(C.c_void_p(self.w.data_ptr()), self.N, self.K, 0.0,
+                                        C.c_void_p(self.packed.data_ptr()), self.nb, C.c_void_p(self.g.data_ptr()),
+                                        C.c_void_p(self.ws.data_ptr()), self.ws.numel(), q4._stream())
+        if rc != 0:
+            q4._check(rc)
+
+    def config(self):
+        return {"workload": self.name, "N": self.N, "K": self.K, "input": "fp32, N(0, 0.02)",
+                "global_scale": "amax / (448 * 6), computed on the device", "output": "packed NVFP4"}
+
+    def cpu_oracle_sample(self, seconds):
+        """The oracle quantizer on 1024-row blocks (each taking its own amax) for about `seconds`."""
+        import oracle
+        rows = min(self.N, 1024)
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            r0 = (done * rows) % self.N
+            oracle.nvfp4_quantize_f32(self.w_host[r0:r0 + rows])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        bytes_done = done * rows * self.alg_bytes / self.N
+        return bytes_done / el / 1e9, f"{done} oracle quantizations of {rows} rows (K={self.K}) in {el:.1f}s"
+
+
 class CopyWork:
     """A plain device copy of known size, for scaling the HBM byte counters."""
 
@@ -307,6 +369,8 @@ def main():
         spec = synth.WORKLOADS[name]
         if spec["kind"] == "moe":
             work = MoeWork(name, spec, args.hot)
+        elif spec["kind"] == "quant":
+            work = QuantWork(name, spec, args.hot)
         else:
             work = GemmWork(name, spec, args.hot)
 

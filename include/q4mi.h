@@ -100,6 +100,31 @@ int q4_nvfp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int6
 int q4_nvfp4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales);
 
 /* Bytes of the packed affine matrix [N][K]; 0 unless N % 16 == 0 and K % 64 == 0. */
+/* Bytes of device workspace q4_nvfp4_quantize needs when it computes the
+ * global scale itself (one scratch word past the counter area). */
+size_t q4_nvfp4_quantize_workspace_bytes(void);
+
+/* NVFP4 quantizer on the device [README: the NVFP4 quantization kernel of
+ * its kernel list; "Why it's NVIDIA-only": E2M1 x E4M3/16 x fp32 global].
+ * Quantizes fp32 weights and writes them in the packed layout of
+ * q4_nvfp4_repack (the result equals q4_nvfp4_repack of the codes and
+ * scales it chose):
+ *   g = global_scale if > 0, else amax|w| / (448 * 6) (fp32)
+ *   s = E4M3(amax of the 16-group / 6 / g), nearest even, saturating at 448
+ *   code = E2M1(w / (e4m3(s) * g)), nearest even, saturating at 6; +0 for a
+ *          group whose decoded scale is 0
+ * each step one fp32 operation in that order.
+ *   w        device fp32 [N][K] row-major, 16-byte aligned, finite values
+ *   packed   device buffer of packed_bytes >= q4_nvfp4_packed_bytes(N, K)
+ *   g_out    device fp32[1] receiving g, or NULL
+ *   ws       device workspace of q4_nvfp4_quantize_workspace_bytes() bytes
+ *            when global_scale <= 0 (NULL otherwise); no zero-fill needed
+ * Errors: INVALID_ARG (NULL w or packed, short packed buffer, non-finite
+ * global_scale), UNSUPPORTED (N % 16, K % 16, K too large), ALIGNMENT,
+ * WORKSPACE, HIP. */
+int q4_nvfp4_quantize(const float* w, int64_t N, int64_t K, float global_scale, void* packed,
+                      size_t packed_bytes, float* g_out, void* ws, size_t ws_bytes, void* stream);
+
 size_t q4_affine4_packed_bytes(int64_t N, int64_t K);
 
 /* Pack canonical affine 4-bit (host codes u8[N][K/2], scale and bias as bf16

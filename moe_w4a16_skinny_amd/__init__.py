@@ -49,6 +49,8 @@ _SIGS = {
     "qgemm_nvfp4_sample": (_i32, [_vp, _f32, _vp, _i32, _i64, _i64, _f32, _f32, C.c_uint64, C.c_uint32, _vp, _i32,
                                   _vp, _vp, _sz, _vp]),
     "q4_sample_uniforms": (_i32, [C.c_uint64, C.c_uint32, _i32, _i64, _vp, _vp]),
+    "q4_nvfp4_quantize_workspace_bytes": (_sz, []),
+    "q4_nvfp4_quantize": (_i32, [_vp, _i64, _i64, _f32, _vp, _sz, _vp, _vp, _sz, _vp]),
     "qgemm_affine4_workspace_bytes": (_sz, [_i32, _i64, _i64]),
     "qgemm_affine4": (_i32, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _sz, _vp]),
     "moe_route_workspace_bytes": (_sz, [_i32, _i32, _i32]),
@@ -237,6 +239,27 @@ def q4_sample_uniforms(seed: int, offset: int, M: int, N: int, device=None):
     _check(_lib.q4_sample_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, M, N, _tptr(out),
                                    _stream()))
     return out
+
+
+def q4_nvfp4_quantize(w, global_scale: float = 0.0, packed=None):
+    """NVFP4-quantize fp32 weights w [N][K] on the device into the packed layout.
+
+    global_scale <= 0 takes g = amax|w| / (448 * 6).  Returns (packed uint8
+    tensor of q4_nvfp4_packed_bytes(N, K), g as a float32 tensor [1])."""
+    torch = _torch()
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 2:
+        raise ValueError("w must be a contiguous fp32 [N][K] tensor")
+    N, K = w.shape
+    nb = _lib.q4_nvfp4_packed_bytes(N, K)
+    if packed is None:
+        packed = torch.empty((max(nb, 1),), dtype=torch.uint8, device=w.device)
+    g = torch.empty((1,), dtype=torch.float32, device=w.device)
+    use_ws = not (float(global_scale) > 0.0)
+    wsb = _lib.q4_nvfp4_quantize_workspace_bytes() if use_ws else 0
+    ws = workspace(wsb, w.device) if use_ws else None
+    _check(_lib.q4_nvfp4_quantize(_tptr(w), N, K, float(global_scale), _tptr(packed), packed.numel(), _tptr(g),
+                                  _tptr(ws), wsb, _stream()))
+    return packed[:nb], g
 
 
 def qgemm_affine4(w_packed, a, N: int, out=None, out_dtype=None):

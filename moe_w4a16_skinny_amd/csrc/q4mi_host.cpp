@@ -159,6 +159,34 @@ int q4_nvfp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int6
   return ok();
 }
 
+size_t q4_nvfp4_quantize_workspace_bytes(void) { return kWsCounterBytes + 256; }
+
+int q4_nvfp4_quantize(const float* w, int64_t N, int64_t K, float global_scale, void* packed, size_t packed_bytes,
+                      float* g_out, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(packed);
+  if (int rc = check_nk(__func__, N, K, 16)) return rc;
+  if (packed_bytes < q4_nvfp4_packed_bytes(N, K))
+    return fail(Q4_ERR_INVALID_ARG, "%s: packed_bytes=%zu < %zu", __func__, packed_bytes, q4_nvfp4_packed_bytes(N, K));
+  if (global_scale != global_scale || global_scale > 3.0e38f || global_scale < -3.0e38f)
+    return fail(Q4_ERR_INVALID_ARG, "%s: global_scale=%g is not finite", __func__, double(global_scale));
+  if (full_tiles(K) + 1 > 65535) return fail(Q4_ERR_UNSUPPORTED, "%s: K=%lld too large", __func__, (long long)K);
+  REQUIRE_ALIGNED(w);
+  REQUIRE_ALIGNED(packed);
+  unsigned* amax = nullptr;
+  if (!(global_scale > 0.0f)) {  // the global scale comes from the tensor's amax: one scratch word
+    if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
+    if (ws_bytes < q4_nvfp4_quantize_workspace_bytes())
+      return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, q4_nvfp4_quantize_workspace_bytes());
+    REQUIRE_ALIGNED(ws);
+    amax = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsCounterBytes);
+  }
+  if (int e = launch_quantize(w, N, K, global_scale > 0.0f ? global_scale : 0.0f, amax,
+                              static_cast<uint8_t*>(packed), g_out, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
+}
+
 int q4_nvfp4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales) {
   REQUIRE_PTR(packed);
   REQUIRE_PTR(codes);

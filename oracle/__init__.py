@@ -29,7 +29,7 @@ from .moe import (gelu_tanh, gelu_tanh_deriv, softmax, route_topk, moe_ref,
                   moe_ref_grouped, moe_abs_bound)
 from .sampling import (philox4, uniform_bits_to_f32, sample_uniforms, gumbel, softcap,
                        sample_scores, sample_tokens)
-from .quantize import e4m3_encode_rne, e2m1_encode_rne, nvfp4_quantize_f32
+from .quantize import e4m3_encode_rne, e2m1_encode_rne, nvfp4_global_scale_f32, nvfp4_quantize_f32
 
 __all__ = [
     "e2m1_value", "e4m3_value", "unpack_nibbles", "nvfp4_dequant", "nvfp4_dequant_f32",
@@ -37,5 +37,6 @@ __all__ = [
     "nvfp4_gemm_ref", "affine_gemm_ref", "affine_gemm_groupsum", "argmax_ref",
     "gelu_tanh", "gelu_tanh_deriv", "softmax", "route_topk", "moe_ref", "moe_ref_grouped",
     "moe_abs_bound", "philox4", "uniform_bits_to_f32", "sample_uniforms", "gumbel", "softcap",
-    "sample_scores", "sample_tokens", "e4m3_encode_rne", "e2m1_encode_rne", "nvfp4_quantize_f32",
+    "sample_scores", "sample_tokens", "e4m3_encode_rne", "e2m1_encode_rne", "nvfp4_global_scale_f32",
+    "nvfp4_quantize_f32",
 ]

@@ -62,6 +62,13 @@ def e2m1_encode_rne(x: np.ndarray) -> np.ndarray:
     return (idx.astype(np.uint8) | (sign << 3)).astype(np.uint8)
 
 
+def nvfp4_global_scale_f32(w: np.ndarray) -> np.float32:
+    """g = amax|w| / (448 * 6), one float32 division (0 for an all-zero w)."""
+    w = np.asarray(w, F32)
+    amax = np.max(np.abs(w)) if w.size else F32(0)
+    return F32(F32(amax) / F32(2688.0))
+
+
 def nvfp4_quantize_f32(w: np.ndarray, global_scale: float | None = None):
     """fp32 [N][K] (K % 16 == 0) -> (codes u8[N][K/2] low nibble = even k,
     scales u8[N][K/16], g float32), every step in float32."""
@@ -70,8 +77,7 @@ def nvfp4_quantize_f32(w: np.ndarray, global_scale: float | None = None):
     if K % 16:
         raise ValueError("K must be a multiple of 16")
     if global_scale is None or global_scale <= 0:
-        amax = np.max(np.abs(w)) if w.size else F32(0)
-        g = F32(F32(amax) / F32(2688.0))
+        g = nvfp4_global_scale_f32(w)
     else:
         g = F32(global_scale)
     blk = w.reshape(N, K // 16, 16)

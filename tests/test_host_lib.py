@@ -183,3 +183,35 @@ def test_repack_refusals():
         q4.q4_affine4_repack(np.zeros((16, 48), np.uint8), np.zeros((16, 1), np.uint16), np.zeros((16, 1), np.uint16))
     assert ei.value.status == q4.Q4_ERR_UNSUPPORTED and "K=96" in str(ei.value)
     assert q4.q4_nvfp4_packed_bytes(16, 24) == 0 and q4.q4_affine4_packed_bytes(16, 96) == 0
+
+
+def test_quantize_refusals_without_gpu():
+    lib = q4.raw()
+    buf = (C.c_uint8 * 4096)()
+    al = (C.addressof(buf) + 15) & ~15
+    p = C.c_void_p(al)
+    mis = C.c_void_p(al + 4)
+    nb = lib.q4_nvfp4_packed_bytes(16, 64)
+    wsb = lib.q4_nvfp4_quantize_workspace_bytes()
+    assert wsb > 0
+    cases = [
+        (lambda: lib.q4_nvfp4_quantize(None, 16, 64, 0.0, p, nb, None, p, wsb, None), q4.Q4_ERR_INVALID_ARG, "w"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 64, 0.0, None, nb, None, p, wsb, None), q4.Q4_ERR_INVALID_ARG, "packed"),
+        (lambda: lib.q4_nvfp4_quantize(p, 15, 64, 0.0, p, nb, None, p, wsb, None), q4.Q4_ERR_UNSUPPORTED, "N=15"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 72, 0.0, p, nb, None, p, wsb, None), q4.Q4_ERR_UNSUPPORTED, "K=72"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 64, 0.0, p, nb - 1, None, p, wsb, None), q4.Q4_ERR_INVALID_ARG,
+         "packed_bytes"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 64, float("nan"), p, nb, None, p, wsb, None), q4.Q4_ERR_INVALID_ARG,
+         "not finite"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 64, float("-inf"), p, nb, None, p, wsb, None), q4.Q4_ERR_INVALID_ARG,
+         "not finite"),
+        (lambda: lib.q4_nvfp4_quantize(mis, 16, 64, 0.0, p, nb, None, p, wsb, None), q4.Q4_ERR_ALIGNMENT, "w is"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 64, 0.0, mis, nb, None, p, wsb, None), q4.Q4_ERR_ALIGNMENT, "packed is"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 64, 0.0, p, nb, None, None, 0, None), q4.Q4_ERR_WORKSPACE, "ws is NULL"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 64, 0.0, p, nb, None, p, wsb - 1, None), q4.Q4_ERR_WORKSPACE,
+         "ws_bytes"),
+        (lambda: lib.q4_nvfp4_quantize(p, 16, 64, 0.0, p, nb, None, mis, wsb, None), q4.Q4_ERR_ALIGNMENT, "ws is"),
+    ]
+    for call, code, needle in cases:
+        assert call() == code, needle
+        assert needle in _err(code), (needle, _err(code))
