@@ -20,12 +20,25 @@ namespace {
 
 __global__ void quant_zero_kernel(unsigned* word) { *word = 0u; }
 
-// max |w| over n values into *amax (fp32 bits; non-negative floats order as
-// unsigned integers); NaN values are skipped by fmaxf
-__global__ __launch_bounds__(256) void quant_amax_kernel(const float* __restrict__ w, size_t n, unsigned* amax) {
-  float m = 0.f;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
-    m = fmaxf(m, fabsf(w[i]));
+// max |w| over n4 float4 values into *amax (fp32 bits; non-negative floats
+// order as unsigned integers); NaN values are skipped by fmaxf.  Four
+// independent loads in flight per lane.
+__device__ __forceinline__ float amax4(float m, float4 v) {
+  return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+__global__ __launch_bounds__(256) void quant_amax_kernel(const float4* __restrict__ w, size_t n4, unsigned* amax) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * 256;
+  size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    const float4 a = w[i], b = w[i + stride], c = w[i + 2 * stride], d = w[i + 3 * stride];
+    m0 = amax4(m0, a);
+    m1 = amax4(m1, b);
+    m2 = amax4(m2, c);
+    m3 = amax4(m3, d);
+  }
+  for (; i < n4; i += stride) m0 = amax4(m0, w[i]);
+  float m = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   if ((threadIdx.x & 63) == 0) atomicMax(amax, __float_as_uint(m));
 }
@@ -54,51 +67,71 @@ __device__ __forceinline__ unsigned e2m1_encode(float x) {
   return mag | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-// One wave per (tile t, panel p): lane (o, c) quantizes row n = 16 p + c,
-// k = 128 t + 32 i + 8 o + 0..7 for each MFMA step i, and writes the code
-// dword where the GEMM's lane reads it; the group amax is shared with lane
-// o ^ 1 (lane ^ 16), and lanes with even o write the group's scale byte.
-__global__ __launch_bounds__(64) void quant_pack_kernel(const float* __restrict__ w, int K, int nfull, int64_t pb,
-                                                        float g_in, const unsigned* amax, uint8_t* __restrict__ packed,
-                                                        float* g_out, int64_t tail_off, int tail_bytes) {
-  const int t = blockIdx.y, p = blockIdx.x;
-  const int lane = threadIdx.x, o = lane >> 4, c = lane & 15;
-  const float g = g_in > 0.f ? g_in : __uint_as_float(*amax) / 2688.0f;
-  if (t == 0 && p == 0) {
-    if (lane == 0 && g_out) *g_out = g;
-    for (int i = lane; i < tail_bytes; i += 64) packed[tail_off + i] = 0;  // zero guard behind the last panel
-  }
-  const bool is_half = t == nfull;
-  const int steps = is_half ? 2 : 4;
-  const int64_t n = static_cast<int64_t>(p) * 16 + c;
-  uint8_t* base = packed + static_cast<int64_t>(p) * pb + static_cast<int64_t>(t) * kTileBytes;
-  uint8_t* sbase = base + (is_half ? kHalfCodeBytes : kTileCodeBytes);
-  for (int i = 0; i < steps; ++i) {
-    const int k0 = t * kTileK + 32 * i + 8 * o;
-    float v[8];
-    if (k0 < K) {  // K % 16 == 0: all 8 inside
-      const float4 a = *reinterpret_cast<const float4*>(w + n * K + k0);
-      const float4 b = *reinterpret_cast<const float4*>(w + n * K + k0 + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
+// One tile (STEPS = 4 MFMA k-steps of 32, or 2 for a half tile) of panel
+// rows n0..n0+15 by one wave: lane (o, c) quantizes row n0 + c at
+// k = kb + 32 i + 8 o + 0..7 for each step i and writes the code dwords where
+// the GEMM's lane reads them (one 16- or 8-byte store); the group amax is
+// shared with lane o ^ 1 (lane ^ 16), and lanes with even o write the scale
+// bytes of their groups (one store).
+template <int STEPS>
+__device__ __forceinline__ void quant_tile(const float* __restrict__ wrow, int K, int kb, int lane, float g,
+                                           uint8_t* __restrict__ base) {
+  const int o = lane >> 4, c = lane & 15;
+  float4 v[STEPS][2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  for (int i = 0; i < STEPS; ++i) {  // every load first: K % 16 == 0, so a chunk of 8 is all inside or all padding
+    const int k0 = kb + 32 * i + 8 * o;
+    if (k0 < K) {
+      v[i][0] = *reinterpret_cast<const float4*>(wrow + k0);
+      v[i][1] = *reinterpret_cast<const float4*>(wrow + k0 + 4);
+    } else {
+      v[i][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      v[i][1] = v[i][0];
     }
+  }
+  unsigned dw[STEPS], sc = 0u;
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i) {
+    const float x[8] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
     float la = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) la = fmaxf(la, fabsf(v[j]));
+    for (int j = 0; j < 8; ++j) la = fmaxf(la, fabsf(x[j]));
     const float gamax = fmaxf(la, __shfl_xor(la, 16));
     const unsigned s = g > 0.f ? e4m3_encode((gamax / 6.0f) / g) : 0u;
     const float S = e4m3_decode(s) * g;
-    unsigned dword = 0u;
+    unsigned d = 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const unsigned q = S > 0.f ? e2m1_encode(v[j] / S) : 0u;
-      dword |= q << (4 * j);  // byte b = codes of k0 + 2b (low nibble) and k0 + 2b + 1
-    }
-    *reinterpret_cast<unsigned*>(base + lane * (steps * 4) + i * 4) = dword;
-    if ((o & 1) == 0) sbase[(c * 2 + (o >> 1)) * steps + i] = static_cast<uint8_t>(s);
+    for (int j = 0; j < 8; ++j) d |= (S > 0.f ? e2m1_encode(x[j] / S) : 0u) << (4 * j);  // low nibble: even k
+    dw[i] = d;
+    sc |= s << (8 * i);
   }
+  uint8_t* sbase = base + STEPS * 256;  // the scales follow the 64 lanes' code dwords
+  if constexpr (STEPS == 4) {
+    *reinterpret_cast<uint4*>(base + lane * 16) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    if ((o & 1) == 0) *reinterpret_cast<unsigned*>(sbase + (c * 2 + (o >> 1)) * 4) = sc;
+  } else {
+    *reinterpret_cast<uint2*>(base + lane * 8) = make_uint2(dw[0], dw[1]);
+    if ((o & 1) == 0) *reinterpret_cast<unsigned short*>(sbase + (c * 2 + (o >> 1)) * 2) = static_cast<unsigned short>(sc);
+  }
+}
+
+// One workgroup of 4 waves per 16-row panel; wave q takes tiles q, q + 4, ...
+// so that the four waves read 2 KiB of each row side by side.
+__global__ __launch_bounds__(256) void quant_pack_kernel(const float* __restrict__ w, int K, int nfull, int ntiles,
+                                                         int64_t pb, float g_in, const unsigned* amax,
+                                                         uint8_t* __restrict__ packed, float* g_out, int64_t tail_off,
+                                                         int tail_bytes) {
+  const int p = blockIdx.x, q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float g = g_in > 0.f ? g_in : __uint_as_float(*amax) / 2688.0f;
+  if (p == 0) {
+    if (threadIdx.x == 0 && g_out) *g_out = g;
+    for (int i = threadIdx.x; i < tail_bytes; i += 256) packed[tail_off + i] = 0;  // zero guard behind the last panel
+  }
+  const float* wrow = w + (static_cast<int64_t>(p) * 16 + (lane & 15)) * K;
+  uint8_t* pbase = packed + static_cast<int64_t>(p) * pb;
+  for (int t = q; t < nfull; t += 4) quant_tile<4>(wrow, K, t * kTileK, lane, g, pbase + static_cast<int64_t>(t) * kTileBytes);
+  if (nfull < ntiles && q == nfull % 4)
+    quant_tile<2>(wrow, K, nfull * kTileK, lane, g, pbase + static_cast<int64_t>(nfull) * kTileBytes);
 }
 
 }  // namespace
@@ -108,15 +141,15 @@ int launch_quantize(const float* w, int64_t N, int64_t K, float g_in, unsigned* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!(g_in > 0.f)) {
     hipLaunchKernelGGL(quant_zero_kernel, dim3(1), dim3(1), 0, s, amax);
-    const size_t n = static_cast<size_t>(N) * static_cast<size_t>(K);
-    const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096));
-    hipLaunchKernelGGL(quant_amax_kernel, dim3(blocks), dim3(256), 0, s, w, n, amax);
+    const size_t n4 = static_cast<size_t>(N) * static_cast<size_t>(K) / 4;  // N * K % 256 == 0
+    const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n4 + 255) / 256, 2048));
+    hipLaunchKernelGGL(quant_amax_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(w), n4, amax);
   }
   const int nfull = static_cast<int>(full_tiles(K));
   const int ntiles = nfull + (has_half_tile(K) ? 1 : 0);
-  hipLaunchKernelGGL(quant_pack_kernel, dim3(static_cast<unsigned>(N / 16), static_cast<unsigned>(ntiles)), dim3(64), 0,
-                     s, w, static_cast<int>(K), nfull, panel_bytes(K), g_in, amax, packed, g_out,
-                     static_cast<int64_t>(N / 16) * panel_bytes(K), static_cast<int>(packed_tail(K)));
+  hipLaunchKernelGGL(quant_pack_kernel, dim3(static_cast<unsigned>(N / 16)), dim3(256), 0, s, w, static_cast<int>(K),
+                     nfull, ntiles, panel_bytes(K), g_in, amax, packed, g_out, static_cast<int64_t>(N / 16) * panel_bytes(K),
+                     static_cast<int>(packed_tail(K)));
   return static_cast<int>(hipGetLastError());
 }
 
