@@ -57,14 +57,43 @@ __device__ __forceinline__ float e4m3_decode(unsigned b) {
   const unsigned ex = (b >> 3) & 15u, mt = b & 7u;
   return ex == 0 ? static_cast<float>(mt) * 0x1p-9f : ldexpf(1.0f + static_cast<float>(mt) * 0.125f, int(ex) - 7);
 }
-// E2M1 code of x: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even
-// index (midpoints .25 and 1.25, 2.5, 5 go down; .75, 1.75, 3.5 go up),
-// saturating at 6; bit 3 is the sign bit of x
-__device__ __forceinline__ unsigned e2m1_encode(float x) {
-  const float a = fabsf(x);
-  const unsigned mag = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) + (a >= 1.75f ? 1u : 0u) +
-                       (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) + (a > 5.0f ? 1u : 0u);
-  return mag | ((__float_as_uint(x) >> 28) & 8u);
+// E2M1 codes of eight values into one dword (value j at nibble j) by the
+// hardware conversion with unit scale: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6},
+// ties to the even code, saturating at 6, the sign bit of the value in bit 3.
+__device__ __forceinline__ unsigned e2m1_x8(const float* q) {
+  unsigned d = 0u;
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[0], q[1], 1.0f, 0);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[2], q[3], 1.0f, 1);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[4], q[5], 1.0f, 2);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, q[6], q[7], 1.0f, 3);
+  return d;
+}
+
+// The codes of x[0..7] / S, the quotients correctly rounded.  For S in
+// [2^-60, 2^60] each quotient takes one multiply by r = RN(1/S) and one
+// correction: e = |x| - q0 S is exact (q0 is within an ulp and nothing
+// underflows where the code depends on it), and RN(q0 + e r) = RN(|x| / S)
+// because r is the correctly rounded reciprocal (Markstein's theorem).  The
+// sign is copied from x afterwards, so -0 keeps its sign bit.  Quotients are
+// capped at 8 first (beyond 6 every value saturates; an overflow of q0 to
+// inf makes the correction NaN, which fminf drops).  Outside that range of S
+// the quotients come from the IEEE division.
+__device__ __forceinline__ unsigned e2m1_div8(const float* x, float S) {
+  float q[8];
+  if (S >= 0x1p-60f && S <= 0x1p60f) {
+    const float r = 1.0f / S;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = fabsf(x[j]);
+      const float q0 = a * r;
+      const float e = fmaf(-q0, S, a);
+      q[j] = copysignf(fminf(fmaf(e, r, q0), 8.0f), x[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = copysignf(fminf(fabsf(x[j] / S), 8.0f), x[j]);
+  }
+  return e2m1_x8(q);
 }
 
 // One tile (STEPS = 4 MFMA k-steps of 32, or 2 for a half tile) of panel
@@ -99,10 +128,7 @@ __device__ __forceinline__ void quant_tile(const float* __restrict__ wrow, int K
     const float gamax = fmaxf(la, __shfl_xor(la, 16));
     const unsigned s = g > 0.f ? e4m3_encode((gamax / 6.0f) / g) : 0u;
     const float S = e4m3_decode(s) * g;
-    unsigned d = 0u;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) d |= (S > 0.f ? e2m1_encode(x[j] / S) : 0u) << (4 * j);  // low nibble: even k
-    dw[i] = d;
+    dw[i] = S > 0.f ? e2m1_div8(x, S) : 0u;  // low nibble: even k
     sc |= s << (8 * i);
   }
   uint8_t* sbase = base + STEPS * 256;  // the scales follow the 64 lanes' code dwords

@@ -99,6 +99,65 @@ def test_quantize_rounding_ties():
     assert np.array_equal(got, ref)
 
 
+F32 = np.float32
+E2M1_DECISIONS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)   # the magnitudes where the E2M1 code steps
+
+
+def as_matrix(groups, seed):
+    """groups of 16 values -> a [16][K] matrix (padding groups of noise)"""
+    rng = np.random.default_rng(seed)
+    groups = list(groups)
+    while len(groups) % 16:
+        groups.append(rng.standard_normal(16))
+    return np.concatenate(groups).astype(F32).reshape(16, -1)
+
+
+def test_quantize_encoder_near_every_decision():
+    # g = 1 and a group amax of 6 give S = 1, so the codes are those of the
+    # values themselves: every float within 2048 ulps of each E2M1 decision
+    # point, both signs, signed zeros and the smallest subnormals
+    vals = []
+    for t in E2M1_DECISIONS:
+        b = np.array([t], F32).view(np.uint32)[0]
+        vals.append((b + np.arange(-2048, 2049, dtype=np.int64)).astype(np.uint32).view(F32))
+    vals.append(np.array([0.0, 1e-45, 1e-40, 2.0 ** -126, 6.0, 5.999999], F32))
+    v = np.concatenate(vals)
+    v = np.concatenate([v, -v])
+    groups = [np.concatenate([[6.0 if i % 2 else -6.0], v[i:i + 15]]) for i in range(0, len(v), 15)]
+    groups[-1] = np.concatenate([groups[-1], np.zeros(16 - len(groups[-1]))])
+    w = as_matrix(groups, 3)
+    got, _ = run(w, 1.0)
+    ref, _ = expect_packed(w, 1.0)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("g", [1.0, 0.0123456789, 3.3e-7, 2.0 ** -70, 7.7e5])
+def test_quantize_quotients_near_every_decision(g):
+    # a full-precision S = RN(e4m3(s) * g) and values a few ulps either side of
+    # S times each decision point: the quotients w / S must round exactly as
+    # the IEEE division does
+    g = F32(g)
+    rng = np.random.default_rng(int(g.view(np.uint32)))
+    groups = []
+    for _ in range(512):
+        A = F32(6.0 * float(g) * 2.0 ** rng.uniform(-5.5, 8.7))
+        if not np.isfinite(A) or A == 0:
+            continue
+        _, sc, _ = oracle.nvfp4_quantize_f32(np.array([[A] + [0.0] * 15], F32), g)
+        S = F32(float(oracle.e4m3_value(sc[0, 0])) * float(g))
+        xs = [A]
+        for _ in range(15):
+            c = F32(float(rng.choice(E2M1_DECISIONS)) * float(S)).view(np.uint32)
+            x = np.array([c + rng.integers(-6, 7)], np.uint32).view(F32)[0]
+            x = min(x, A) * (1 if rng.integers(2) else -1)
+            xs.append(x)
+        groups.append(np.array(xs, F32))
+    w = as_matrix(groups, 4)
+    got, _ = run(w, float(g))
+    ref, _ = expect_packed(w, float(g))
+    assert np.array_equal(got, ref)
+
+
 def test_quantize_zero_matrix_and_all_equal():
     got, g = run(np.zeros((32, 256), np.float32))
     assert g == 0.0 and not got.any()
