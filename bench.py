@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "weight-stream HBM GB/s (% of ~8 TB/s) for W4A16 GEMM M=1/16 & top-8 MoE"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense f16 matrix-core peak
 DEFAULT_WORKLOAD = "nvfp4_verify_m16_k4096_n8192"
 ROTATE_BYTES = 2 << 30
 
@@ -121,6 +122,7 @@ class GemmWork:
             self.g = float(inp.g)
             self.alg_bytes = N * K // 2 + N * K // 16 + 4
             self.dtype = "f16"
+            self.flops = 2 * M * N * K  # the prefill rows (M > 16) make the product matrix-core bound
         else:
             inp = synth.affine_gemm(spec["seed"], M, K, N)
             packed = q4.q4_affine4_repack(inp.codes, inp.scale, inp.bias)
@@ -417,6 +419,8 @@ def main():
 
     value = work.alg_bytes * K / wall / 1e9
     achieved = work.alg_bytes / mean_launch / 1e9
+    flops = getattr(work, "flops", 0)
+    mfma_bound = flops / MFMA_F16_PEAK_TFLOPS / 1e12 > work.alg_bytes / HBM_PEAK_GBS / 1e9
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -433,14 +437,16 @@ def main():
         "config": work.config(),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(flops / mean_launch / 1e12, 2) if mfma_bound else round(achieved, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round((flops / mean_launch / 1e12 / MFMA_F16_PEAK_TFLOPS) if mfma_bound
+                          else achieved / HBM_PEAK_GBS, 4),
             "traffic": (traffic_for(name, getattr(work, "kind", "gemm")) if not args.copy_kernel else None),
             "kernel": work.kernel_names[0],
             "alg_bytes_per_launch": work.alg_bytes,
+            "flops_per_launch": flops,
             "mean_launch_us": round(mean_launch * 1e6, 3),
             "timing": "HIP graph of the K steps" if graph is not None else "eager launches",
             "empty_kernel_interval_us": round(launch_interval * 1e6, 3),

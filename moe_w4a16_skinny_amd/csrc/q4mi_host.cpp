@@ -280,6 +280,8 @@ size_t qgemm_affine4_workspace_bytes(int M, int64_t K, int64_t N) {
   return b > kWsCounterBytes ? b : 0;
 }
 
+constexpr int kMaxPrefillRows = 65536;  // M limit of the NVFP4 GEMM for M > 16
+
 struct SampleSpec {  // qgemm_nvfp4_sample's extra arguments
   float softcap, temperature;
   uint64_t seed;
@@ -297,7 +299,11 @@ static int gemm_common(int fmt, const char* fn, const void* w_packed, float gsca
     return fail(Q4_ERR_INVALID_ARG, "%s: temperature=%g is not a finite number >= 0", fn, double(sp->temperature));
   if (sp && !(sp->softcap <= 3.0e38f))  // NaN or inf
     return fail(Q4_ERR_INVALID_ARG, "%s: softcap=%g is not finite", fn, double(sp->softcap));
-  if (M < 1 || M > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: M=%d outside 1..16 (skinny GEMM only)", fn, M);
+  // more than 16 rows: NVFP4 only, without the fused argmax or sampling
+  const bool prefill = fmt == kNvfp4 && M > 16 && !argmax && !sp;
+  if (M < 1 || M > (prefill ? kMaxPrefillRows : 16))
+    return fail(Q4_ERR_UNSUPPORTED, "%s: M=%d outside 1..16 (1..%d for NVFP4 without argmax or sampling)", fn, M,
+                kMaxPrefillRows);
   if (int rc = check_nk(fn, N, K, fmt == kNvfp4 ? 16 : 64)) return rc;
   if (fmt == kNvfp4 && out_dtype != Q4_F32 && out_dtype != Q4_F16 && out_dtype != Q4_BF16)
     return fail(Q4_ERR_INVALID_ARG, "%s: out_dtype=%d is not Q4_F32, Q4_F16 or Q4_BF16", fn, out_dtype);
@@ -337,6 +343,10 @@ static int gemm_common(int fmt, const char* fn, const void* w_packed, float gsca
     g.seed_lo = static_cast<unsigned>(sp->seed & 0xFFFFFFFFu);
     g.seed_hi = static_cast<unsigned>(sp->seed >> 32);
     g.offset = sp->offset;
+  }
+  if (prefill) {
+    if (int e = launch_prefill(g, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
+    return ok();
   }
   const GemmCfg cfg = choose_gemm_cfg(fmt, M, K, N);
   if (int e = launch_gemm(fmt, g, cfg, ws, stream))

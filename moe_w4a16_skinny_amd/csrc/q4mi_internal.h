@@ -94,6 +94,9 @@ int launch_dequant(int fmt, const uint8_t* w, int64_t panel_bytes, int64_t N, in
                    float* out, void* stream);
 int launch_sample_uniforms(unsigned seed_lo, unsigned seed_hi, unsigned offset, int M, int64_t N, float* out,
                            void* stream);
+// NVFP4 GEMM for M > 16 rows (q4mi_prefill.hip); uses w, panel_bytes, a, M, K,
+// N, nfull, half, gscale, out, out_dtype of the arguments
+int launch_prefill(const GemmArgs& g, void* stream);
 // NVFP4 quantizer (q4mi_quant.hip); amax: one scratch word of the workspace
 int launch_quantize(const float* w, int64_t N, int64_t K, float g_in, unsigned* amax, uint8_t* packed, float* g_out,
                     void* stream);

@@ -118,7 +118,10 @@ def test_gemm_refusals_without_gpu():
     cases = [
         (lambda: lib.qgemm_nvfp4(None, 1.0, p, 1, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_INVALID_ARG, "w_packed"),
         (lambda: lib.qgemm_nvfp4(p, 1.0, p, 0, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "M=0"),
-        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 17, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "M=17"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 17, 64, 16, p, q4.Q4_F32, p, p, 4096, None), q4.Q4_ERR_UNSUPPORTED, "M=17"),
+        (lambda: lib.qgemm_nvfp4(p, 1.0, p, 65537, 64, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED,
+         "M=65537"),
+        (lambda: lib.qgemm_affine4(p, p, 17, 128, 16, p, q4.Q4_F32, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "M=17"),
         (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 24, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "N=24"),
         (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 72, 16, p, q4.Q4_F32, None, None, 0, None), q4.Q4_ERR_UNSUPPORTED, "K=72"),
         (lambda: lib.qgemm_nvfp4(p, 1.0, p, 1, 64, 16, p, 9, None, None, 0, None), q4.Q4_ERR_INVALID_ARG, "out_dtype"),
