@@ -333,6 +333,7 @@ WORKLOADS = {
                                            has_shared=True),
     # a prefill chunk of 512 rows through the verify-shaped weights (M > 16: the matrix-core regime)
     "nvfp4_prefill_m512_k4096_n8192": dict(kind="nvfp4", seed=106, M=512, K=4096, N=8192, out="f32"),
+    "nvfp4_prefill_m2048_k4096_n8192": dict(kind="nvfp4", seed=107, M=2048, K=4096, N=8192, out="f32"),
     # the tied embedding in fp32, N(0, 0.02), for the device quantizer
     "nvfp4_quantize_n262144_k2816": dict(kind="quant", seed=103, N=262144, K=2816, std=0.02),
     "affine4_m1_k5120_n15360": dict(kind="affine", seed=105, M=1, K=5120, N=15360, out="f32"),
