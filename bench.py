@@ -74,8 +74,8 @@ def sources_sha256(kind):
     """Hash of the kernel sources a workload runs (traffic figures are tied to it)."""
     import hashlib
     csrc = os.path.join(ROOT, "moe_w4a16_skinny_amd", "csrc")
-    names = ["q4mi_tiles.h", "q4mi_internal.h"] + [{"moe": "q4mi_moe.hip", "quant": "q4mi_quant.hip"}
-                                                   .get(kind, "q4mi_gemm.hip")]
+    names = ["q4mi_tiles.h", "q4mi_internal.h"] + [{"moe": "q4mi_moe.hip", "quant": "q4mi_quant.hip",
+                                                    "prefill": "q4mi_prefill.hip"}.get(kind, "q4mi_gemm.hip")]
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(csrc, n), "rb") as f:
@@ -151,8 +151,8 @@ class GemmWork:
             self.wsb = q4.raw().qgemm_affine4_workspace_bytes(M, K, N)
         self.ws = q4.workspace(max(self.wsb, 256))
         self.i = 0
-        self.kind = "gemm"
-        self.kernel_names = ["qgemm_kernel"]
+        self.kind = "prefill" if M > 16 else "gemm"  # more than 16 rows run the prefill kernel
+        self.kernel_names = ["qgemm_prefill_kernel" if M > 16 else "qgemm_kernel"]
 
     def step(self):
         import ctypes as C
