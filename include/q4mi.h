@@ -137,7 +137,8 @@ int q4_affine4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes,
                       uint16_t* scale_bf16, uint16_t* bias_bf16);
 
 /* ---------------------------------------------------------------------------
- * Skinny GEMMs.  y[m][n] = sum_k a[m][k] * w[n][k], 1 <= M <= 16.
+ * Skinny GEMMs.  y[m][n] = sum_k a[m][k] * w[n][k], 1 <= M <= 16 (NVFP4
+ * also more rows, see qgemm_nvfp4).
  * ------------------------------------------------------------------------- */
 
 /* Bytes of device workspace qgemm_nvfp4 needs for this shape (0 if none):
@@ -152,18 +153,22 @@ size_t qgemm_affine4_workspace_bytes(int M, int64_t K, int64_t N);
 /* NVFP4 W4A16 GEMM [README "Everything it has": the M <= 16 GEMM with
  * in-register FP4 -> f16 dequant; "Why it's NVIDIA-only": E2M1 x E4M3/16 x
  * fp32 global].  Each weight is e2m1(code) * e4m3(scale) * global_scale.
+ * More rows (17 <= M <= 65536, argmax NULL) -- prefill chunks and large
+ * verify blocks, the M > 16 product of [README "Everything it has"] -- run a
+ * matrix-core kernel with 64 x 128 output blocks; it needs no workspace
+ * (the query returns 0) and its results obey the same error bound.
  *   w_packed  device, from q4_nvfp4_repack of the [N][K] weights
  *   a         device f16 [M][K] row-major
  *   out       device [M][N] row-major of out_dtype (Q4_F32, Q4_F16 or Q4_BF16)
- *   argmax    device int32[M] or NULL.  If set, argmax[m] is the index of the
+ *   argmax    device int32[M] or NULL (M <= 16 only).  If set, argmax[m] is the index of the
  *             largest value of row m of `out` as stored, lowest index on ties,
  *             NaN values skipped (-1 if the whole row is NaN) -- tree_round's
  *             argmax of [ISSUE "Why now"], fused into the GEMM.
  *   ws        device workspace of ws_bytes >= the query (NULL if the query is
  *             0); it must be zero-filled before its first use, and every call
  *             leaves its counters at zero again.
- * Errors: INVALID_ARG, UNSUPPORTED (M outside 1..16, N % 16, K % 16),
- * ALIGNMENT, WORKSPACE, HIP. */
+ * Errors: INVALID_ARG, UNSUPPORTED (M outside 1..16 with argmax, outside
+ * 1..65536 without, N % 16, K % 16), ALIGNMENT, WORKSPACE, HIP. */
 int qgemm_nvfp4(const void* w_packed, float global_scale, const void* a, int M, int64_t K,
                 int64_t N, void* out, int out_dtype, int32_t* argmax, void* ws, size_t ws_bytes,
                 void* stream);
