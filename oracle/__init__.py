@@ -29,6 +29,7 @@ from .moe import (gelu_tanh, gelu_tanh_deriv, softmax, route_topk, moe_ref,
                   moe_ref_grouped, moe_abs_bound)
 from .sampling import (philox4, uniform_bits_to_f32, sample_uniforms, gumbel, softcap,
                        sample_scores, sample_tokens)
+from .block import rmsnorm, rmsnorm_bound, route_normed, moe_block_ref, moe_block_bound
 from .quantize import e4m3_encode_rne, e2m1_encode_rne, nvfp4_global_scale_f32, nvfp4_quantize_f32
 
 __all__ = [
@@ -38,5 +39,6 @@ __all__ = [
     "gelu_tanh", "gelu_tanh_deriv", "softmax", "route_topk", "moe_ref", "moe_ref_grouped",
     "moe_abs_bound", "philox4", "uniform_bits_to_f32", "sample_uniforms", "gumbel", "softcap",
     "sample_scores", "sample_tokens", "e4m3_encode_rne", "e2m1_encode_rne", "nvfp4_global_scale_f32",
+    "rmsnorm", "rmsnorm_bound", "route_normed", "moe_block_ref", "moe_block_bound",
     "nvfp4_quantize_f32",
 ]

@@ -50,6 +50,7 @@ TAG_EXPERT = 4
 TAG_AFF_CODES = 5
 TAG_AFF_SCALE = 6
 TAG_AFF_BIAS = 7
+TAG_BLOCK = 8
 
 _E4M3_MAX = 448.0
 _E2M1_MAX = 6.0
@@ -262,6 +263,38 @@ class MoeInputs:
         return self.gate[0][0].shape[0]
 
 
+@dataclass
+class MoeBlockInputs:
+    """A Gemma-4 MoE block: routed experts (no shared one), a dense gated FFN
+    branch, the router with its learned per-expert scale, the per-expert down
+    scale and five RMSNorm weight vectors; residual fp32 [T][D]."""
+    residual: np.ndarray    # f32 [T][D]
+    w_router: np.ndarray    # f32 [D][E]
+    router_scale: np.ndarray  # f32 [E]
+    down_scale: np.ndarray    # f32 [E]
+    gate: list
+    up: list
+    down: list
+    dense_gate: tuple       # (codes [Fd][D/2], scales [Fd][D/16], g)
+    dense_up: tuple
+    dense_down: tuple       # (codes [D][Fd/2], scales [D][Fd/16], g)
+    ffn_norm: np.ndarray    # f32 [D] each
+    post_ffw_norm_1: np.ndarray
+    pre_ffw_norm_2: np.ndarray
+    post_ffw_norm_2: np.ndarray
+    post_ffw_norm: np.ndarray
+    E: int
+    k: int
+
+    @property
+    def T(self):
+        return self.residual.shape[0]
+
+    @property
+    def D(self):
+        return self.residual.shape[1]
+
+
 def act_f16(seed: int, M: int, K: int) -> np.ndarray:
     return _rng(seed, TAG_ACT).standard_normal((M, K), dtype=np.float32).astype(np.float16)
 
@@ -320,6 +353,24 @@ def moe_layer(seed: int, T: int = 16, D: int = 2816, E: int = 128, F: int = 704,
                      [m[2] for m in mats], E, k, has_shared)
 
 
+def moe_block(seed: int, T: int = 16, D: int = 2816, E: int = 128, F: int = 704, F_dense: int = 2112,
+              k: int = 8) -> MoeBlockInputs:
+    """The MoE layer of moe_layer (routed experts only) plus: residual fp32
+    N(0, 1); the dense branch's gate/up [F_dense][D] and down [D][F_dense]
+    N(0, .02) NVFP4; router_scale, down_scale and the five norm weights
+    drawn 1 + N(0, .1) in fp32."""
+    layer = moe_layer(seed, T=T, D=D, E=E, F=F, k=k, has_shared=False)
+    residual = _rng(seed, TAG_BLOCK).standard_normal((T, D), dtype=np.float32)
+    base = TAG_BLOCK * 1_000_000
+    dg = nvfp4_weights(seed, F_dense, D, tag=base + 1)
+    du = nvfp4_weights(seed, F_dense, D, tag=base + 2)
+    dd = nvfp4_weights(seed, D, F_dense, tag=base + 3)
+    r = _rng(seed, TAG_BLOCK, 1)
+    one = lambda n: (1.0 + 0.1 * r.standard_normal(n)).astype(np.float32)
+    return MoeBlockInputs(residual, layer.w_router, one(E), one(E), layer.gate, layer.up, layer.down,
+                          dg, du, dd, one(D), one(D), one(D), one(D), one(D), E, k)
+
+
 # named workloads: sizes of the decode / speculative-verify shapes on the pages
 WORKLOADS = {
     "nvfp4_m1_k1024_n1024": dict(kind="nvfp4", seed=101, M=1, K=1024, N=1024, out="f32"),
@@ -331,6 +382,9 @@ WORKLOADS = {
                                                   out="none", sample=dict(softcap=30.0, temperature=1.0)),
     "moe_t16_d2816_e128s1_f704_top8": dict(kind="moe", seed=104, T=16, D=2816, E=128, F=704, k=8,
                                            has_shared=True),
+    # the whole Gemma-4 MoE block: dense branch (width 2112) + 128 routed experts top-8, norms
+    "moe_block_t16_d2816_e128_f704_fd2112_top8": dict(kind="moe_block", seed=108, T=16, D=2816, E=128, F=704,
+                                                      F_dense=2112, k=8),
     # a prefill chunk of 512 rows through the verify-shaped weights (M > 16: the matrix-core regime)
     "nvfp4_prefill_m512_k4096_n8192": dict(kind="nvfp4", seed=106, M=512, K=4096, N=8192, out="f32"),
     "nvfp4_prefill_m2048_k4096_n8192": dict(kind="nvfp4", seed=107, M=2048, K=4096, N=8192, out="f32"),
