@@ -271,6 +271,70 @@ class MoeWork:
         return self.alg_bytes / el / 1e9, f"1 full oracle layer (router + {self.active}+1 experts, T={m.T}) in {el:.1f}s"
 
 
+class MoeBlockWork:
+    """One step = moe_block_forward: input norms, router matmul, router norm and
+    top-k, dense branch, experts, combine (7 launches) on the residual."""
+
+    def __init__(self, name, spec, hot):
+        import numpy as np
+        import torch
+
+        import moe_w4a16_skinny_amd as q4
+        import synth
+        self.name, self.spec, self.q4 = name, spec, q4
+        t0 = time.time()
+        blk = synth.moe_block(spec["seed"], T=spec["T"], D=spec["D"], E=spec["E"], F=spec["F"],
+                              F_dense=spec["F_dense"], k=spec["k"])
+        self.blk = blk
+        bw = q4.moe_block_pack(blk)
+        log(f"[bench] {name}: block generated and packed in {time.time() - t0:.1f}s")
+        self.res0 = torch.from_numpy(blk.residual).cuda()
+        self.res = self.res0.clone()
+        ex, de = bw.experts, bw.dense
+        layer_bytes = sum(t.numel() for t in (ex.gate, ex.up, ex.down, de.gate, de.up, de.down))
+        self.copies = 1 if hot else max(2, -(-ROTATE_BYTES // layer_bytes))
+        self.blocks = [bw]
+        for _ in range(self.copies - 1):
+            e2 = q4.MoeWeights(ex.E, False, ex.D, ex.F, ex.gate.clone(), ex.up.clone(), ex.down.clone(), ex.g_gate,
+                               ex.g_up, ex.g_down)
+            d2 = q4.MoeWeights(1, False, de.D, de.F, de.gate.clone(), de.up.clone(), de.down.clone(), de.g_gate,
+                               de.g_up, de.g_down)
+            self.blocks.append(q4.MoeBlockWeights(e2, d2, bw.w_router, bw.router_scale, bw.down_scale, bw.norms,
+                                                  bw.eps))
+        self.i = 0
+        # algorithmic bytes: router matrix, dense branch, every expert that receives a token, residual in and out
+        import oracle
+        _, parts = oracle.moe_block_ref(blk, blk.residual, want_parts=True)
+        self.active = len(set(parts["idx"].ravel().tolist()))
+        D, F, Fd, T = blk.D, spec["F"], spec["F_dense"], blk.T
+        per = lambda f: 2 * (f * D // 2 + f * D // 16 + 4) + (D * f // 2 + D * f // 16 + 4)
+        self.alg_bytes = D * blk.E * 4 + per(Fd) + self.active * per(F) + 2 * T * D * 4
+        self.kind = "moe_block"
+        self.kernel_names = ["block step: block_norm_in + route + block_router + 2 x (moe_gate_up + moe_down + "
+                             "moe_combine) + block_combine"]
+        self.dtype = "f16"
+
+    def step(self):
+        bw = self.blocks[self.i % self.copies]
+        self.i += 1
+        # the residual is updated in place; each step starts from the same input
+        self.res.copy_(self.res0)
+        self.q4.moe_block_forward(bw, self.res, self.blk.k)
+
+    def config(self):
+        b = self.blk
+        return {"workload": self.name, "T": b.T, "D": b.D, "E": b.E, "F": self.spec["F"],
+                "F_dense": self.spec["F_dense"], "top_k": b.k, "active_experts": self.active, "weights": "nvfp4",
+                "weight_copies_rotated": self.copies}
+
+    def cpu_oracle_sample(self, seconds):
+        import oracle
+        t0 = time.perf_counter()
+        oracle.moe_block_ref(self.blk, self.blk.residual)
+        el = time.perf_counter() - t0
+        return self.alg_bytes / el / 1e9, f"1 full oracle block (T={self.blk.T}) in {el:.1f}s"
+
+
 class QuantWork:
     """One step = q4_nvfp4_quantize of an fp32 [N][K] matrix with the global
     scale taken from its amax: a pass for the amax, a pass that quantizes and
@@ -371,6 +435,8 @@ def main():
         spec = synth.WORKLOADS[name]
         if spec["kind"] == "moe":
             work = MoeWork(name, spec, args.hot)
+        elif spec["kind"] == "moe_block":
+            work = MoeBlockWork(name, spec, args.hot)
         elif spec["kind"] == "quant":
             work = QuantWork(name, spec, args.hot)
         else:

@@ -270,6 +270,51 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* The whole Gemma-4 MoE block around the experts [DOC 3.2 "Per-layer (MoE)",
+ * DOC 4.6 "MoE"; DOC 14 "Completed": ffn_down_exps.scale folded into the
+ * routing weights].  With RMSNorm(v; w) = v / sqrt(mean(v^2) + eps) * w per
+ * token row:
+ *   h1 = RMSNorm(r; ffn_norm)                b1 = dense FFN(h1)
+ *   h2 = RMSNorm(r; pre_ffw_norm_2)          z  = RMSNorm(h2 . W_r; 1) * router_scale
+ *   idx = top-k of softmax(z) (ties to the lower index), w = softmax(z)[idx] * down_scale[idx]
+ *   b2 = sum_j w_j FFN_idx_j(h2)
+ *   r += RMSNorm(RMSNorm(b1; post_ffw_norm_1) + RMSNorm(b2; post_ffw_norm_2); post_ffw_norm)
+ * The FFNs are those of moe_grouped_qgemm (gated GELU-tanh, h in f16); h1 and
+ * h2 enter them as f16. */
+typedef struct {
+  q4_moe_desc experts;        /* routed experts, has_shared = 0 */
+  q4_moe_desc dense;          /* the dense branch as a one-expert layer: E = 1, has_shared = 0,
+                                 F = its width, same D */
+  const float* w_router;      /* device fp32 [D][E] */
+  const float* router_scale;  /* device fp32 [E] (ffn_gate_inp.scale) */
+  const float* down_scale;    /* device fp32 [E] (ffn_down_exps.scale) or NULL for 1 */
+  const float* ffn_norm;      /* device fp32 [D] each */
+  const float* post_ffw_norm_1;
+  const float* pre_ffw_norm_2;
+  const float* post_ffw_norm_2;
+  const float* post_ffw_norm;
+  float eps;                  /* RMSNorm epsilon (> 0; 1e-6 in the tests) */
+} q4_moe_block_desc;
+
+/* Bytes of device workspace moe_block_forward needs (0 on invalid shapes). */
+size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k);
+
+/* One MoE block on the residual stream, in place.
+ *   residual device fp32 [T][D], updated r <- r + update
+ *   ws       device workspace of ws_bytes >= moe_block_workspace_bytes; its
+ *            first 32 KiB of counters start and end at zero, as for the
+ *            other entry points
+ * The block runs 7 launches on `stream`: the two input norms, the router
+ * matmul (moe_route_topk's kernel), the router normalization and top-k, the
+ * dense branch and the experts (moe_grouped_qgemm's kernels, sharing the
+ * workspace), and the combine.
+ * Errors: INVALID_ARG (NULL pointers, eps <= 0 or not finite, dense not a
+ * one-expert layer, D mismatch, has_shared set), the errors of
+ * moe_route_topk and moe_grouped_qgemm for these shapes, ALIGNMENT,
+ * WORKSPACE, HIP. */
+int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* ---------------------------------------------------------------------------
  * Test exports: the same device dequantization the GEMMs use, written out.
  * ------------------------------------------------------------------------- */

@@ -35,6 +35,12 @@ class q4_moe_desc(C.Structure):
                 ("g_gate", _vp), ("g_up", _vp), ("g_down", _vp)]
 
 
+class q4_moe_block_desc(C.Structure):
+    _fields_ = [("experts", q4_moe_desc), ("dense", q4_moe_desc), ("w_router", _vp), ("router_scale", _vp),
+                ("down_scale", _vp), ("ffn_norm", _vp), ("post_ffw_norm_1", _vp), ("pre_ffw_norm_2", _vp),
+                ("post_ffw_norm_2", _vp), ("post_ffw_norm", _vp), ("eps", _f32)]
+
+
 _SIGS = {
     "q4_abi_version": (_i32, []),
     "q4_last_error": (C.c_char_p, []),
@@ -57,6 +63,8 @@ _SIGS = {
     "moe_route_topk": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_workspace_bytes": (_sz, [C.POINTER(q4_moe_desc), _i32, _i32]),
     "moe_grouped_qgemm": (_i32, [C.POINTER(q4_moe_desc), _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "moe_block_workspace_bytes": (_sz, [C.POINTER(q4_moe_block_desc), _i32, _i32]),
+    "moe_block_forward": (_i32, [C.POINTER(q4_moe_block_desc), _vp, _i32, _i32, _vp, _sz, _vp]),
     "q4_dequant_nvfp4": (_i32, [_vp, _f32, _i64, _i64, _vp, _vp]),
     "q4_dequant_affine4": (_i32, [_vp, _i64, _i64, _vp, _vp]),
 }
@@ -350,3 +358,48 @@ def q4_dequant_affine4(w_packed, N: int, K: int):
     out = torch.empty((N, K), dtype=torch.float32, device=w_packed.device)
     _check(_lib.q4_dequant_affine4(_tptr(w_packed), N, K, _tptr(out), _stream()))
     return out
+
+
+@dataclass
+class MoeBlockWeights:
+    """Device-resident Gemma-4 MoE block (see q4_moe_block_desc)."""
+    experts: MoeWeights
+    dense: MoeWeights
+    w_router: object      # fp32 device tensors
+    router_scale: object
+    down_scale: object
+    norms: tuple          # ffn_norm, post_ffw_norm_1, pre_ffw_norm_2, post_ffw_norm_2, post_ffw_norm
+    eps: float = 1e-6
+
+    def desc(self) -> q4_moe_block_desc:
+        n = [t.data_ptr() for t in self.norms]
+        return q4_moe_block_desc(self.experts.desc(), self.dense.desc(), self.w_router.data_ptr(),
+                                 self.router_scale.data_ptr(),
+                                 self.down_scale.data_ptr() if self.down_scale is not None else None,
+                                 *n, float(self.eps))
+
+
+def moe_block_pack(blk, eps: float = 1e-6, device="cuda") -> MoeBlockWeights:
+    """Upload a block given as canonical NVFP4 triples and fp32 vectors (the
+    fields of a MoeBlockInputs-like object)."""
+    torch = _torch()
+    experts = moe_pack_experts(blk.gate, blk.up, blk.down, blk.E, False, device)
+    dense = moe_pack_experts([blk.dense_gate], [blk.dense_up], [blk.dense_down], 1, False, device)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+    norms = tuple(f(v) for v in (blk.ffn_norm, blk.post_ffw_norm_1, blk.pre_ffw_norm_2, blk.post_ffw_norm_2,
+                                 blk.post_ffw_norm))
+    return MoeBlockWeights(experts, dense, f(blk.w_router), f(blk.router_scale),
+                           f(blk.down_scale) if blk.down_scale is not None else None, norms, eps)
+
+
+def moe_block_forward(block: MoeBlockWeights, residual, k: int):
+    """One MoE block on the residual stream (fp32 [T][D] device tensor), in place; returns it."""
+    torch = _torch()
+    if residual.dtype != torch.float32 or not residual.is_contiguous():
+        raise ValueError("residual must be a contiguous fp32 [T][D] tensor")
+    T = residual.shape[0]
+    d = block.desc()
+    wsb = _lib.moe_block_workspace_bytes(C.byref(d), T, k)
+    ws = workspace(wsb, residual.device)
+    _check(_lib.moe_block_forward(C.byref(d), _tptr(residual), T, k, _tptr(ws), wsb, _stream()))
+    return residual

@@ -1,0 +1,184 @@
+// The Gemma-4 MoE block around the expert kernels: the RMSNorms, the
+// router's normalization and the combine.
+//
+// [DOC 3.2 "Per-layer (MoE)"], [DOC 4.6 "MoE"]: from the residual r,
+//   h1 = RMSNorm(r; ffn_norm), h2 = RMSNorm(r; pre_ffw_norm_2)
+//   z  = RMSNorm(h2 . W_r; unit weights) * ffn_gate_inp.scale, p = softmax(z),
+//        top-k of p; [DOC 14 "Completed"]: ffn_down_exps.scale folded into
+//        the kept weights
+//   b1 = dense FFN(h1), b2 = sum_j w_j FFN_idx_j(h2)   (the expert kernels)
+//   r += RMSNorm(RMSNorm(b1; post_ffw_norm_1) + RMSNorm(b2; post_ffw_norm_2);
+//                post_ffw_norm)
+// with RMSNorm(v; w) = v / sqrt(mean(v^2) + eps) * w.  The rows are few (one
+// per token) and short, so each kernel takes one token per workgroup; every
+// sum is reduced in a fixed order (deterministic).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "q4mi_internal.h"
+
+namespace q4mi {
+namespace {
+
+typedef _Float16 f16;
+
+// sum over the 256 threads: butterfly within each wave (lane 0's result),
+// then the four waves in order
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();  // red may still be read from a previous sum
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+__device__ __forceinline__ float inv_rms(float sum_sq, int n, float eps) {
+  return 1.0f / sqrtf(sum_sq / static_cast<float>(n) + eps);
+}
+
+// h1 = RMSNorm(r; w1), h2 = RMSNorm(r; w2) as f16 (the expert GEMMs' input)
+__global__ __launch_bounds__(256) void block_norm_in_kernel(const float* __restrict__ res, int D,
+                                                            const float* __restrict__ w1,
+                                                            const float* __restrict__ w2, float eps,
+                                                            f16* __restrict__ h1, f16* __restrict__ h2) {
+  __shared__ float red[4];
+  const float* row = res + static_cast<size_t>(blockIdx.x) * D;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) ss = fmaf(row[i], row[i], ss);
+  const float r = inv_rms(block_sum256(ss, red), D, eps);
+  f16* o1 = h1 + static_cast<size_t>(blockIdx.x) * D;
+  f16* o2 = h2 + static_cast<size_t>(blockIdx.x) * D;
+  for (int i = threadIdx.x; i < D; i += 256) {
+    const float v = row[i] * r;
+    o1[i] = static_cast<f16>(v * w1[i]);
+    o2[i] = static_cast<f16>(v * w2[i]);
+  }
+}
+
+// One wave per token: z = RMSNorm(logits) * scale over the E <= 256 logits
+// (lane l holds experts l, l + 64, l + 128, l + 192), softmax, then k rounds
+// of a wave-wide arg-max (larger z first, ties to the lower index, NaN never
+// chosen); w = p * down_scale.  Also writes the dense branch's one-expert
+// routing (expert 0, weight 1).
+__global__ __launch_bounds__(64) void block_router_kernel(const float* __restrict__ logits, int E, int k,
+                                                          const float* __restrict__ scale,
+                                                          const float* __restrict__ down_scale, float eps,
+                                                          int32_t* __restrict__ idx, float* __restrict__ w,
+                                                          int32_t* __restrict__ didx, float* __restrict__ dw) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const float* lr = logits + static_cast<size_t>(t) * E;
+  float z[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    z[j] = e < E ? lr[e] : 0.f;
+    ss = fmaf(z[j], z[j], ss);
+  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  ss = __shfl(ss, 0);
+  const float r = inv_rms(ss, E, eps);
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    z[j] = e < E ? z[j] * r * scale[e] : -INFINITY;
+    m = fmaxf(m, z[j]);
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float se = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) se += (lane + 64 * j < E) ? expf(z[j] - m) : 0.f;
+  for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
+  se = __shfl(se, 0);
+  unsigned taken = 0u;
+  for (int s = 0; s < k; ++s) {
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !(taken & (1u << j)) && (z[j] > bv || (z[j] == bv && e < be))) {
+        bv = z[j];
+        be = e;
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be != 0x7FFFFFFF && (be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == 0) {
+      const bool ok = be != 0x7FFFFFFF;
+      idx[t * k + s] = ok ? be : -1;
+      w[t * k + s] = ok ? expf(bv - m) / se * (down_scale ? down_scale[be] : 1.0f) : 0.f;
+    }
+  }
+  if (lane == 0) {
+    didx[t] = 0;
+    dw[t] = 1.0f;
+  }
+}
+
+// r += RMSNorm(RMSNorm(b1; p1) + RMSNorm(b2; p2); p)
+__device__ __forceinline__ float branch_sum(const float* b1, const float* b2, const float* p1, const float* p2,
+                                            float r1, float r2, int i) {
+  const float u = (b1[i] * r1) * p1[i];
+  const float v = (b2[i] * r2) * p2[i];
+  return u + v;
+}
+__global__ __launch_bounds__(256) void block_combine_kernel(const float* __restrict__ b1,
+                                                            const float* __restrict__ b2, int D,
+                                                            const float* __restrict__ p1,
+                                                            const float* __restrict__ p2,
+                                                            const float* __restrict__ p, float eps,
+                                                            float* __restrict__ res) {
+  __shared__ float red[4];
+  const size_t o = static_cast<size_t>(blockIdx.x) * D;
+  const float* x1 = b1 + o;
+  const float* x2 = b2 + o;
+  float s1 = 0.f, s2 = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) {
+    s1 = fmaf(x1[i], x1[i], s1);
+    s2 = fmaf(x2[i], x2[i], s2);
+  }
+  const float r1 = inv_rms(block_sum256(s1, red), D, eps);
+  const float r2 = inv_rms(block_sum256(s2, red), D, eps);
+  float s3 = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) {
+    const float s = branch_sum(x1, x2, p1, p2, r1, r2, i);
+    s3 = fmaf(s, s, s3);
+  }
+  const float r3 = inv_rms(block_sum256(s3, red), D, eps);
+  float* out = res + o;
+  for (int i = threadIdx.x; i < D; i += 256) out[i] += (branch_sum(x1, x2, p1, p2, r1, r2, i) * r3) * p[i];
+}
+
+}  // namespace
+
+int launch_block_norm_in(const float* res, int T, int D, const float* w1, const float* w2, float eps, void* h1,
+                         void* h2, void* stream) {
+  hipLaunchKernelGGL(block_norm_in_kernel, dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream), res, D, w1, w2,
+                     eps, static_cast<f16*>(h1), static_cast<f16*>(h2));
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_block_router(const float* logits, int T, int E, int k, const float* scale, const float* down_scale,
+                        float eps, int32_t* idx, float* w, int32_t* didx, float* dw, void* stream) {
+  hipLaunchKernelGGL(block_router_kernel, dim3(T), dim3(64), 0, static_cast<hipStream_t>(stream), logits, E, k, scale,
+                     down_scale, eps, idx, w, didx, dw);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_block_combine(const float* b1, const float* b2, int T, int D, const float* p1, const float* p2,
+                         const float* p, float eps, float* res, void* stream) {
+  hipLaunchKernelGGL(block_combine_kernel, dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream), b1, b2, D, p1, p2,
+                     p, eps, res);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace q4mi

@@ -2,6 +2,7 @@
 // queries, and the extern "C" entry points that enqueue the HIP kernels.
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 
@@ -543,6 +544,99 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
   m.rowof = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + r_off);
   m.grp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + g_off);
   if (int e = launch_moe(m, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
+}
+
+// ---- MoE block -----------------------------------------------------------
+// Workspace: [0, sub) is shared by the router and the two grouped calls (run
+// one after another on the stream), then the block's own buffers.
+struct BlockWs {
+  size_t sub, h1, h2, logits, idx, w, ridx, rw, didx, dw, b1, b2, total;
+};
+static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+static BlockWs block_ws(const q4_moe_block_desc* b, int T, int k) {
+  BlockWs L{};
+  const int D = b->experts.D, E = b->experts.E;
+  L.sub = up256(std::max(std::max(moe_route_workspace_bytes(T, D, E), moe_workspace_bytes(&b->experts, T, k)),
+                         moe_workspace_bytes(&b->dense, T, 1)));
+  size_t o = L.sub;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up256(bytes);
+    return at;
+  };
+  L.h1 = take(size_t(T) * D * 2);
+  L.h2 = take(size_t(T) * D * 2);
+  L.logits = take(size_t(T) * E * 4);
+  L.idx = take(size_t(T) * k * 4);
+  L.w = take(size_t(T) * k * 4);
+  L.ridx = take(size_t(T) * k * 4);
+  L.rw = take(size_t(T) * k * 4);
+  L.didx = take(size_t(T) * 4);
+  L.dw = take(size_t(T) * 4);
+  L.b1 = take(size_t(T) * D * 4);
+  L.b2 = take(size_t(T) * D * 4);
+  L.total = o;
+  return L;
+}
+
+size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k) {
+  if (!b || T < 1 || k < 1 || b->experts.D < 1 || b->experts.E < 1) return 0;
+  return block_ws(b, T, k).total;
+}
+
+int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k, void* ws, size_t ws_bytes,
+                      void* stream) {
+  REQUIRE_PTR(b);
+  REQUIRE_PTR(residual);
+  REQUIRE_PTR(b->w_router);
+  REQUIRE_PTR(b->router_scale);
+  REQUIRE_PTR(b->ffn_norm);
+  REQUIRE_PTR(b->post_ffw_norm_1);
+  REQUIRE_PTR(b->pre_ffw_norm_2);
+  REQUIRE_PTR(b->post_ffw_norm_2);
+  REQUIRE_PTR(b->post_ffw_norm);
+  if (!(b->eps > 0.0f && b->eps < 3.0e38f))
+    return fail(Q4_ERR_INVALID_ARG, "%s: eps=%g must be finite and > 0", __func__, double(b->eps));
+  if (b->experts.has_shared != 0)
+    return fail(Q4_ERR_INVALID_ARG, "%s: the routed experts may not have a shared expert (the dense branch is it)",
+                __func__);
+  if (b->dense.E != 1 || b->dense.has_shared != 0 || b->dense.D != b->experts.D)
+    return fail(Q4_ERR_INVALID_ARG, "%s: dense must be a one-expert layer (E=1, has_shared=0) of D=%d", __func__,
+                b->experts.D);
+  if (T < 1 || T > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d outside 1..16", __func__, T);
+  if (b->experts.E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", __func__, b->experts.E);
+  REQUIRE_ALIGNED(residual);
+  if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
+  REQUIRE_ALIGNED(ws);
+  const BlockWs L = block_ws(b, T, k);
+  if (ws_bytes < L.total) return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, L.total);
+  char* base = static_cast<char*>(ws);
+  const int D = b->experts.D, E = b->experts.E;
+  if (int e = launch_block_norm_in(residual, T, D, b->ffn_norm, b->pre_ffw_norm_2, b->eps, base + L.h1, base + L.h2,
+                                   stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  if (int rc = moe_route_topk(base + L.h2, b->w_router, T, D, E, k, 0, reinterpret_cast<float*>(base + L.logits),
+                              reinterpret_cast<int32_t*>(base + L.ridx), reinterpret_cast<float*>(base + L.rw), ws,
+                              L.sub, stream))
+    return rc;
+  if (int e = launch_block_router(reinterpret_cast<const float*>(base + L.logits), T, E, k, b->router_scale,
+                                  b->down_scale, b->eps, reinterpret_cast<int32_t*>(base + L.idx),
+                                  reinterpret_cast<float*>(base + L.w), reinterpret_cast<int32_t*>(base + L.didx),
+                                  reinterpret_cast<float*>(base + L.dw), stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  if (int rc = moe_grouped_qgemm(&b->dense, base + L.h1, reinterpret_cast<const int32_t*>(base + L.didx),
+                                 reinterpret_cast<const float*>(base + L.dw), T, 1, base + L.b1, Q4_F32, ws, L.sub,
+                                 stream))
+    return rc;
+  if (int rc = moe_grouped_qgemm(&b->experts, base + L.h2, reinterpret_cast<const int32_t*>(base + L.idx),
+                                 reinterpret_cast<const float*>(base + L.w), T, k, base + L.b2, Q4_F32, ws, L.sub,
+                                 stream))
+    return rc;
+  if (int e = launch_block_combine(reinterpret_cast<const float*>(base + L.b1),
+                                   reinterpret_cast<const float*>(base + L.b2), T, D, b->post_ffw_norm_1,
+                                   b->post_ffw_norm_2, b->post_ffw_norm, b->eps, residual, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   return ok();
 }
 

@@ -97,6 +97,13 @@ int launch_sample_uniforms(unsigned seed_lo, unsigned seed_hi, unsigned offset, 
 // NVFP4 GEMM for M > 16 rows (q4mi_prefill.hip); uses w, panel_bytes, a, M, K,
 // N, nfull, half, gscale, out, out_dtype of the arguments
 int launch_prefill(const GemmArgs& g, void* stream);
+// MoE block norms, router normalization and combine (q4mi_block.hip)
+int launch_block_norm_in(const float* res, int T, int D, const float* w1, const float* w2, float eps, void* h1,
+                         void* h2, void* stream);
+int launch_block_router(const float* logits, int T, int E, int k, const float* scale, const float* down_scale,
+                        float eps, int32_t* idx, float* w, int32_t* didx, float* dw, void* stream);
+int launch_block_combine(const float* b1, const float* b2, int T, int D, const float* p1, const float* p2,
+                         const float* p, float eps, float* res, void* stream);
 // NVFP4 quantizer (q4mi_quant.hip); amax: one scratch word of the workspace
 int launch_quantize(const float* w, int64_t N, int64_t K, float g_in, unsigned* amax, uint8_t* packed, float* g_out,
                     void* stream);
