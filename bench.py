@@ -317,8 +317,7 @@ class MoeBlockWork:
     def step(self):
         bw = self.blocks[self.i % self.copies]
         self.i += 1
-        # the residual is updated in place; each step starts from the same input
-        self.res.copy_(self.res0)
+        # the residual is updated in place, step after step, like successive layers
         self.q4.moe_block_forward(bw, self.res, self.blk.k)
 
     def config(self):

@@ -309,7 +309,8 @@ size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k);
  * dense branch and the experts (moe_grouped_qgemm's kernels, sharing the
  * workspace), and the combine.
  * Errors: INVALID_ARG (NULL pointers, eps <= 0 or not finite, dense not a
- * one-expert layer, D mismatch, has_shared set), the errors of
+ * one-expert layer, D mismatch, has_shared set), UNSUPPORTED (T > 16,
+ * E > 256, D > 4096), the errors of
  * moe_route_topk and moe_grouped_qgemm for these shapes, ALIGNMENT,
  * WORKSPACE, HIP. */
 int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k, void* ws, size_t ws_bytes,

@@ -36,22 +36,44 @@ __device__ __forceinline__ float inv_rms(float sum_sq, int n, float eps) {
   return 1.0f / sqrtf(sum_sq / static_cast<float>(n) + eps);
 }
 
+// A row of D <= 256 * kRowRegs values lives in registers, thread t holding
+// elements t + 256 j: every load of the row is issued before the first use.
+constexpr int kRowRegs = 16;
+__device__ __forceinline__ void load_row(float (&v)[kRowRegs], const float* __restrict__ row, int D) {
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) {
+    const int i = static_cast<int>(threadIdx.x) + 256 * j;
+    v[j] = i < D ? row[i] : 0.f;
+  }
+}
+__device__ __forceinline__ float sum_sq(const float (&v)[kRowRegs]) {
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) ss = fmaf(v[j], v[j], ss);
+  return ss;
+}
+
 // h1 = RMSNorm(r; w1), h2 = RMSNorm(r; w2) as f16 (the expert GEMMs' input)
 __global__ __launch_bounds__(256) void block_norm_in_kernel(const float* __restrict__ res, int D,
                                                             const float* __restrict__ w1,
                                                             const float* __restrict__ w2, float eps,
                                                             f16* __restrict__ h1, f16* __restrict__ h2) {
   __shared__ float red[4];
-  const float* row = res + static_cast<size_t>(blockIdx.x) * D;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < D; i += 256) ss = fmaf(row[i], row[i], ss);
-  const float r = inv_rms(block_sum256(ss, red), D, eps);
+  float v[kRowRegs], a[kRowRegs], b[kRowRegs];
+  load_row(v, res + static_cast<size_t>(blockIdx.x) * D, D);
+  load_row(a, w1, D);
+  load_row(b, w2, D);
+  const float r = inv_rms(block_sum256(sum_sq(v), red), D, eps);
   f16* o1 = h1 + static_cast<size_t>(blockIdx.x) * D;
   f16* o2 = h2 + static_cast<size_t>(blockIdx.x) * D;
-  for (int i = threadIdx.x; i < D; i += 256) {
-    const float v = row[i] * r;
-    o1[i] = static_cast<f16>(v * w1[i]);
-    o2[i] = static_cast<f16>(v * w2[i]);
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) {
+    const int i = static_cast<int>(threadIdx.x) + 256 * j;
+    if (i < D) {
+      const float x = v[j] * r;
+      o1[i] = static_cast<f16>(x * a[j]);
+      o2[i] = static_cast<f16>(x * b[j]);
+    }
   }
 }
 
@@ -67,14 +89,17 @@ __global__ __launch_bounds__(64) void block_router_kernel(const float* __restric
                                                           int32_t* __restrict__ didx, float* __restrict__ dw) {
   const int t = blockIdx.x, lane = threadIdx.x;
   const float* lr = logits + static_cast<size_t>(t) * E;
-  float z[4];
-  float ss = 0.f;
+  float z[4], sc[4], ds[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 4; ++j) {  // the logits and both scales of this lane's experts, loaded together
     const int e = lane + 64 * j;
     z[j] = e < E ? lr[e] : 0.f;
-    ss = fmaf(z[j], z[j], ss);
+    sc[j] = e < E ? scale[e] : 0.f;
+    ds[j] = (e < E && down_scale) ? down_scale[e] : 1.0f;
   }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ss = fmaf(z[j], z[j], ss);
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   ss = __shfl(ss, 0);
   const float r = inv_rms(ss, E, eps);
@@ -82,7 +107,7 @@ __global__ __launch_bounds__(64) void block_router_kernel(const float* __restric
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    z[j] = e < E ? z[j] * r * scale[e] : -INFINITY;
+    z[j] = e < E ? z[j] * r * sc[j] : -INFINITY;
     m = fmaxf(m, z[j]);
   }
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -93,7 +118,7 @@ __global__ __launch_bounds__(64) void block_router_kernel(const float* __restric
   se = __shfl(se, 0);
   unsigned taken = 0u;
   for (int s = 0; s < k; ++s) {
-    float bv = -INFINITY;
+    float bv = -INFINITY, bd = 1.0f;
     int be = 0x7FFFFFFF;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -101,21 +126,23 @@ __global__ __launch_bounds__(64) void block_router_kernel(const float* __restric
       if (e < E && !(taken & (1u << j)) && (z[j] > bv || (z[j] == bv && e < be))) {
         bv = z[j];
         be = e;
+        bd = ds[j];
       }
     }
     for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
+      const float ov = __shfl_xor(bv, off), od = __shfl_xor(bd, off);
       const int oe = __shfl_xor(be, off);
       if (ov > bv || (ov == bv && oe < be)) {
         bv = ov;
         be = oe;
+        bd = od;
       }
     }
     if (be != 0x7FFFFFFF && (be & 63) == lane) taken |= 1u << (be >> 6);
     if (lane == 0) {
       const bool ok = be != 0x7FFFFFFF;
       idx[t * k + s] = ok ? be : -1;
-      w[t * k + s] = ok ? expf(bv - m) / se * (down_scale ? down_scale[be] : 1.0f) : 0.f;
+      w[t * k + s] = ok ? expf(bv - m) / se * bd : 0.f;
     }
   }
   if (lane == 0) {
@@ -125,12 +152,6 @@ __global__ __launch_bounds__(64) void block_router_kernel(const float* __restric
 }
 
 // r += RMSNorm(RMSNorm(b1; p1) + RMSNorm(b2; p2); p)
-__device__ __forceinline__ float branch_sum(const float* b1, const float* b2, const float* p1, const float* p2,
-                                            float r1, float r2, int i) {
-  const float u = (b1[i] * r1) * p1[i];
-  const float v = (b2[i] * r2) * p2[i];
-  return u + v;
-}
 __global__ __launch_bounds__(256) void block_combine_kernel(const float* __restrict__ b1,
                                                             const float* __restrict__ b2, int D,
                                                             const float* __restrict__ p1,
@@ -139,23 +160,24 @@ __global__ __launch_bounds__(256) void block_combine_kernel(const float* __restr
                                                             float* __restrict__ res) {
   __shared__ float red[4];
   const size_t o = static_cast<size_t>(blockIdx.x) * D;
-  const float* x1 = b1 + o;
-  const float* x2 = b2 + o;
-  float s1 = 0.f, s2 = 0.f;
-  for (int i = threadIdx.x; i < D; i += 256) {
-    s1 = fmaf(x1[i], x1[i], s1);
-    s2 = fmaf(x2[i], x2[i], s2);
-  }
-  const float r1 = inv_rms(block_sum256(s1, red), D, eps);
-  const float r2 = inv_rms(block_sum256(s2, red), D, eps);
-  float s3 = 0.f;
-  for (int i = threadIdx.x; i < D; i += 256) {
-    const float s = branch_sum(x1, x2, p1, p2, r1, r2, i);
-    s3 = fmaf(s, s, s3);
-  }
-  const float r3 = inv_rms(block_sum256(s3, red), D, eps);
+  float x1[kRowRegs], x2[kRowRegs], q1[kRowRegs], q2[kRowRegs], q[kRowRegs], xr[kRowRegs];
+  load_row(x1, b1 + o, D);  // every load of the kernel is issued here
+  load_row(x2, b2 + o, D);
+  load_row(q1, p1, D);
+  load_row(q2, p2, D);
+  load_row(q, p, D);
+  load_row(xr, res + o, D);
+  const float r1 = inv_rms(block_sum256(sum_sq(x1), red), D, eps);
+  const float r2 = inv_rms(block_sum256(sum_sq(x2), red), D, eps);
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) x1[j] = (x1[j] * r1) * q1[j] + (x2[j] * r2) * q2[j];  // the branches' sum
+  const float r3 = inv_rms(block_sum256(sum_sq(x1), red), D, eps);
   float* out = res + o;
-  for (int i = threadIdx.x; i < D; i += 256) out[i] += (branch_sum(x1, x2, p1, p2, r1, r2, i) * r3) * p[i];
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) {
+    const int i = static_cast<int>(threadIdx.x) + 256 * j;
+    if (i < D) out[i] = xr[j] + (x1[j] * r3) * q[j];
+  }
 }
 
 }  // namespace

@@ -606,6 +606,7 @@ int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k,
                 b->experts.D);
   if (T < 1 || T > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d outside 1..16", __func__, T);
   if (b->experts.E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", __func__, b->experts.E);
+  if (b->experts.D > 4096) return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d > 4096", __func__, b->experts.D);
   REQUIRE_ALIGNED(residual);
   if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
   REQUIRE_ALIGNED(ws);
