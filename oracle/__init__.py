@@ -22,9 +22,10 @@ Pages cited:
             FFN (GEGLU)".
 """
 from .formats import (e2m1_value, e4m3_value, unpack_nibbles, nvfp4_dequant,
-                      nvfp4_dequant_f32, bf16_value, affine_dequant, affine_dequant_f32)
+                      nvfp4_dequant_f32, bf16_value, affine_dequant, affine_dequant_f32,
+                      affine_dequant_bits, AFFINE_BITS)
 from .gemm import (gemm_ref, gemm_abs_bound, nvfp4_gemm_ref, affine_gemm_ref,
-                   affine_gemm_groupsum, argmax_ref)
+                   affine_gemm_groupsum, argmax_ref, affine_bits_gemm_ref)
 from .moe import (gelu_tanh, gelu_tanh_deriv, softmax, route_topk, moe_ref,
                   moe_ref_grouped, moe_abs_bound)
 from .sampling import (philox4, uniform_bits_to_f32, sample_uniforms, gumbel, softcap,
@@ -38,7 +39,7 @@ __all__ = [
     "nvfp4_gemm_ref", "affine_gemm_ref", "affine_gemm_groupsum", "argmax_ref",
     "gelu_tanh", "gelu_tanh_deriv", "softmax", "route_topk", "moe_ref", "moe_ref_grouped",
     "moe_abs_bound", "philox4", "uniform_bits_to_f32", "sample_uniforms", "gumbel", "softcap",
-    "sample_scores", "sample_tokens", "e4m3_encode_rne", "e2m1_encode_rne", "nvfp4_global_scale_f32",
+    "sample_scores", "sample_tokens", "e4m3_encode_rne", "e2m1_encode_rne", "nvfp4_global_scale_f32", "affine_dequant_bits", "AFFINE_BITS", "affine_bits_gemm_ref",
     "rmsnorm", "rmsnorm_bound", "route_normed", "moe_block_ref", "moe_block_bound",
     "nvfp4_quantize_f32",
 ]

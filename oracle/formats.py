@@ -100,3 +100,27 @@ def affine_dequant(codes: np.ndarray, scale_bits: np.ndarray, bias_bits: np.ndar
 def affine_dequant_f32(codes, scale_bits, bias_bits) -> np.ndarray:
     """fp32 value of each affine weight: exact q*s + b rounded once (== fmaf(q, s, b))."""
     return affine_dequant(codes, scale_bits, bias_bits).astype(np.float32)
+
+
+AFFINE_BITS = (2, 3, 4, 5, 6, 8)
+
+
+def affine_dequant_bits(codes: np.ndarray, scale_bits: np.ndarray, bias_bits: np.ndarray, bits: int) -> np.ndarray:
+    """Affine b-bit codes, one per byte [N][K] (values < 2^b), with bf16
+    scale/bias [N][K/64] -> float64 q * s + b, per 64-value group.
+
+    [README "Everything it has": MLX affine weights; the widths 2, 3, 4, 5, 6
+    and 8 bits in groups of 64].  Exact in float64 for the same reason as the
+    4-bit form (q < 2^8 times an 8-significant-bit bf16, plus a bf16)."""
+    if bits not in AFFINE_BITS:
+        raise ValueError(f"bits must be one of {AFFINE_BITS}")
+    q = np.asarray(codes)
+    if np.any(q >= (1 << bits)):
+        raise ValueError("code out of range for the bit width")
+    q = q.astype(np.float64)
+    N, K = q.shape
+    s = bf16_value(scale_bits)
+    b = bf16_value(bias_bits)
+    if s.shape != (N, K // 64) or b.shape != (N, K // 64):
+        raise ValueError("scale/bias must be [N][K/64]")
+    return q * np.repeat(s, 64, axis=1) + np.repeat(b, 64, axis=1)

@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import nvfp4_dequant, affine_dequant, unpack_nibbles, bf16_value
+from .formats import nvfp4_dequant, affine_dequant, affine_dequant_bits, unpack_nibbles, bf16_value
 
 
 def gemm_ref(a: np.ndarray, w: np.ndarray) -> np.ndarray:
@@ -86,3 +86,20 @@ def argmax_ref(y) -> np.ndarray:
     (tree_round's argmax in the issue's "Why now" names only the operation)."""
     y32 = np.asarray(y, np.float64).astype(np.float32)
     return np.argmax(y32, axis=1).astype(np.int32)   # numpy returns the first maximum
+
+
+def affine_bits_gemm_ref(codes, scale_bits, bias_bits, a_bits, bits: int, want_bound: bool = True):
+    """Affine b-bit GEMM (codes one per byte [N][K]) with bf16 activations:
+    (y float64 [M][N], sum_k |a w| or None)."""
+    a64 = bf16_value(a_bits)
+    N = codes.shape[0]
+    y = np.empty((a64.shape[0], N))
+    bnd = np.empty_like(y) if want_bound else None
+    step = 4096
+    for r0 in range(0, N, step):
+        r1 = min(N, r0 + step)
+        w = affine_dequant_bits(codes[r0:r1], scale_bits[r0:r1], bias_bits[r0:r1], bits)
+        y[:, r0:r1] = a64 @ w.T
+        if want_bound:
+            bnd[:, r0:r1] = np.abs(a64) @ np.abs(w).T
+    return y, bnd

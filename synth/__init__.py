@@ -323,6 +323,19 @@ def affine_weights(seed: int, N: int, K: int):
     return pack_nibbles(q), f32_to_bf16_bits(s), f32_to_bf16_bits(b)
 
 
+def affine_weights_bits(seed: int, N: int, K: int, bits: int):
+    """MLX-style affine b-bit weights, codes one per byte [N][K] uniform in
+    0..2^b - 1, scale bf16(|N(0, .003)| * 15 / (2^b - 1)) (the 4-bit recipe's
+    weight range at every width), bias bf16(N(0, .01)) [N][K/64]."""
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    q = _rng(seed, TAG_AFF_CODES).integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    s = np.abs(_rng(seed, TAG_AFF_SCALE).standard_normal((N, K // 64), dtype=np.float32)) \
+        * np.float32(0.003 * 15.0 / ((1 << bits) - 1))
+    b = _rng(seed, TAG_AFF_BIAS).standard_normal((N, K // 64), dtype=np.float32) * np.float32(0.01)
+    return q, f32_to_bf16_bits(s), f32_to_bf16_bits(b)
+
+
 def affine_gemm(seed: int, M: int, K: int, N: int) -> AffineGemmInputs:
     """MLX-style affine 4-bit inputs: codes U[0,15], scale bf16(|N(0,.003)|), bias bf16(N(0,.01)), a bf16 N(0,1)."""
     codes, s, b = affine_weights(seed, N, K)
