@@ -75,7 +75,8 @@ def sources_sha256(kind):
     import hashlib
     csrc = os.path.join(ROOT, "moe_w4a16_skinny_amd", "csrc")
     names = ["q4mi_tiles.h", "q4mi_internal.h"] + [{"moe": "q4mi_moe.hip", "quant": "q4mi_quant.hip",
-                                                    "prefill": "q4mi_prefill.hip"}.get(kind, "q4mi_gemm.hip")]
+                                                    "prefill": "q4mi_prefill.hip",
+                                                    "affine_bits": "q4mi_affineb.hip"}.get(kind, "q4mi_gemm.hip")]
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(csrc, n), "rb") as f:
@@ -123,6 +124,15 @@ class GemmWork:
             self.alg_bytes = N * K // 2 + N * K // 16 + 4
             self.dtype = "f16"
             self.flops = 2 * M * N * K  # the prefill rows (M > 16) make the product matrix-core bound
+        elif spec["kind"] == "affine_bits":
+            bits = spec["bits"]
+            q, sc, bi = synth.affine_weights_bits(spec["seed"], N, K, bits)
+            a = synth.act_bf16_bits(spec["seed"] + 1, M, K)
+            inp = synth.AffineGemmInputs(q, sc, bi, a)
+            packed = q4.q4_affine_bits_repack(q, sc, bi, bits)
+            self.a = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+            self.alg_bytes = N * K * bits // 8 + 2 * N * (K // 64) * 2
+            self.dtype = "bf16"
         else:
             inp = synth.affine_gemm(spec["seed"], M, K, N)
             packed = q4.q4_affine4_repack(inp.codes, inp.scale, inp.bias)
@@ -147,12 +157,17 @@ class GemmWork:
         self.amax = torch.empty(16, dtype=torch.int32, device="cuda")
         if spec["kind"] == "nvfp4":
             self.wsb = q4.raw().qgemm_nvfp4_workspace_bytes(M, K, N, int(self.want_argmax))
+        elif spec["kind"] == "affine_bits":
+            self.wsb = 0
         else:
             self.wsb = q4.raw().qgemm_affine4_workspace_bytes(M, K, N)
         self.ws = q4.workspace(max(self.wsb, 256))
         self.i = 0
         self.kind = "prefill" if M > 16 else "gemm"  # more than 16 rows run the prefill kernel
         self.kernel_names = ["qgemm_prefill_kernel" if M > 16 else "qgemm_kernel"]
+        if spec["kind"] == "affine_bits":
+            self.kind = "affine_bits"
+            self.kernel_names = ["qgemm_affineb_kernel"]
 
     def step(self):
         import ctypes as C
@@ -172,6 +187,9 @@ class GemmWork:
                                  C.c_void_p(self.out.data_ptr()), q4._dtype_code(self.out.dtype),
                                  C.c_void_p(self.amax.data_ptr()) if self.want_argmax else None,
                                  C.c_void_p(self.ws.data_ptr()), self.ws.numel(), s)
+        elif self.spec["kind"] == "affine_bits":
+            rc = lib.qgemm_affine_bits(w, C.c_void_p(self.a.data_ptr()), self.M, self.K, self.N, self.spec["bits"],
+                                       C.c_void_p(self.out.data_ptr()), q4._dtype_code(self.out.dtype), s)
         else:
             rc = lib.qgemm_affine4(w, C.c_void_p(self.a.data_ptr()), self.M, self.K, self.N,
                                    C.c_void_p(self.out.data_ptr()), q4._dtype_code(self.out.dtype),
@@ -200,6 +218,9 @@ class GemmWork:
             r1 = min(N, r0 + rows)
             if self.spec["kind"] == "nvfp4":
                 oracle.nvfp4_gemm_ref(inp.codes[r0:r1], inp.scales[r0:r1], inp.g, inp.a, want_bound=False)
+            elif self.spec["kind"] == "affine_bits":
+                oracle.affine_bits_gemm_ref(inp.codes[r0:r1], inp.scale[r0:r1], inp.bias[r0:r1], inp.a,
+                                            self.spec["bits"], want_bound=False)
             else:
                 oracle.affine_gemm_ref(inp.codes[r0:r1], inp.scale[r0:r1], inp.bias[r0:r1], inp.a,
                                        want_bound=False)

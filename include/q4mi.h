@@ -270,6 +270,33 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* MLX-style affine weights at 2, 3, 5, 6 or 8 bits [README "Everything it
+ * has": the MLX affine widths, groups of 64; the 4-bit width has the entry
+ * points above].  w = q * scale + bias per 64-value group.
+ *   codes  host u8 [N][K], one code per byte, each < 2^bits
+ *   scale_bf16, bias_bf16  host bf16 bit patterns [N][K/64]
+ * Packed layout: per 16-row panel, 128-k tiles (K padded to 128 with zero
+ * codes and zero scale/bias) of 256 * bits code bytes, lane (c, o) of the
+ * MFMA owning 4 * bits bytes that hold row c's codes at k = 32 i + 8 o + j
+ * as one little-endian bit stream (code (i, j) at bit 8 bits i + bits j),
+ * then 128 bytes of (bf16 scale | bf16 bias << 16) words, row c's two groups
+ * at 8 c.  packed_bytes = N / 16 * ceil(K / 128) * (256 bits + 128).
+ * Errors: INVALID_ARG (NULL, short buffer, a code >= 2^bits), UNSUPPORTED
+ * (bits, N % 16, K % 64). */
+size_t q4_affine_bits_packed_bytes(int64_t N, int64_t K, int bits);
+int q4_affine_bits_repack(const uint8_t* codes, const uint16_t* scale_bf16, const uint16_t* bias_bf16, int64_t N,
+                          int64_t K, int bits, void* packed, size_t packed_bytes);
+int q4_affine_bits_unpack(const void* packed, int64_t N, int64_t K, int bits, uint8_t* codes,
+                          uint16_t* scale_bf16, uint16_t* bias_bf16);
+
+/* y[m][n] = sum_k a[m][k] * (q[n][k] * s + b) for the b-bit layout above,
+ * 1 <= M <= 16, fp32 accumulation; no workspace.
+ *   w_packed device, from q4_affine_bits_repack;  a device bf16 [M][K]
+ *   out      device [M][N] of out_dtype (Q4_F32 or Q4_BF16)
+ * Errors: INVALID_ARG, UNSUPPORTED (bits, M, N % 16, K % 64), ALIGNMENT, HIP. */
+int qgemm_affine_bits(const void* w_packed, const void* a, int M, int64_t K, int64_t N, int bits, void* out,
+                      int out_dtype, void* stream);
+
 /* The whole Gemma-4 MoE block around the experts [DOC 3.2 "Per-layer (MoE)",
  * DOC 4.6 "MoE"; DOC 14 "Completed": ffn_down_exps.scale folded into the
  * routing weights].  With RMSNorm(v; w) = v / sqrt(mean(v^2) + eps) * w per

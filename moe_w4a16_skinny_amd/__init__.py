@@ -63,6 +63,10 @@ _SIGS = {
     "moe_route_topk": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_workspace_bytes": (_sz, [C.POINTER(q4_moe_desc), _i32, _i32]),
     "moe_grouped_qgemm": (_i32, [C.POINTER(q4_moe_desc), _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "q4_affine_bits_packed_bytes": (_sz, [_i64, _i64, _i32]),
+    "q4_affine_bits_repack": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz]),
+    "q4_affine_bits_unpack": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "qgemm_affine_bits": (_i32, [_vp, _vp, _i32, _i64, _i64, _i32, _vp, _i32, _vp]),
     "moe_block_workspace_bytes": (_sz, [C.POINTER(q4_moe_block_desc), _i32, _i32]),
     "moe_block_forward": (_i32, [C.POINTER(q4_moe_block_desc), _vp, _i32, _i32, _vp, _sz, _vp]),
     "q4_dequant_nvfp4": (_i32, [_vp, _f32, _i64, _i64, _vp, _vp]),
@@ -403,3 +407,35 @@ def moe_block_forward(block: MoeBlockWeights, residual, k: int):
     ws = workspace(wsb, residual.device)
     _check(_lib.moe_block_forward(C.byref(d), _tptr(residual), T, k, _tptr(ws), wsb, _stream()))
     return residual
+
+
+def q4_affine_bits_repack(codes: np.ndarray, scale_bf16: np.ndarray, bias_bf16: np.ndarray, bits: int) -> np.ndarray:
+    """codes u8 [N][K] (one per byte), scale/bias bf16 bits [N][K/64] -> packed b-bit layout."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    s = np.ascontiguousarray(scale_bf16, np.uint16)
+    b = np.ascontiguousarray(bias_bf16, np.uint16)
+    N, K = codes.shape
+    nb = _lib.q4_affine_bits_packed_bytes(N, K, bits)
+    out = np.empty(max(nb, 1), np.uint8)
+    _check(_lib.q4_affine_bits_repack(_np_ptr(codes), _np_ptr(s), _np_ptr(b), N, K, bits, _np_ptr(out), nb))
+    return out[:nb]
+
+
+def q4_affine_bits_unpack(packed: np.ndarray, N: int, K: int, bits: int):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    codes = np.zeros((N, K), np.uint8)
+    s = np.zeros((N, K // 64), np.uint16)
+    b = np.zeros((N, K // 64), np.uint16)
+    _check(_lib.q4_affine_bits_unpack(_np_ptr(packed), N, K, bits, _np_ptr(codes), _np_ptr(s), _np_ptr(b)))
+    return codes, s, b
+
+
+def qgemm_affine_bits(w_packed, a, N: int, bits: int, out=None, out_dtype=None):
+    """y = a . W^T for affine b-bit W [N][K] (bits 2, 3, 5, 6, 8) packed on the device; a bf16 [M][K]."""
+    torch = _torch()
+    M, K = a.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    _check(_lib.qgemm_affine_bits(_tptr(w_packed), _tptr(a), M, K, N, int(bits), _tptr(out), _dtype_code(out.dtype),
+                                  _stream()))
+    return out

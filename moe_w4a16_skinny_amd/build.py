@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4mi.so")
-SOURCES = ["q4mi_host.cpp", "q4mi_gemm.hip", "q4mi_moe.hip", "q4mi_quant.hip", "q4mi_prefill.hip", "q4mi_block.hip"]
+SOURCES = ["q4mi_host.cpp", "q4mi_gemm.hip", "q4mi_moe.hip", "q4mi_quant.hip", "q4mi_prefill.hip", "q4mi_block.hip", "q4mi_affineb.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -547,6 +547,124 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
   return ok();
 }
 
+// ---- affine 2/3/5/6/8-bit ------------------------------------------------
+}  // extern "C"
+namespace {
+bool affine_bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 5 || bits == 6 || bits == 8; }
+int64_t affb_tiles(int64_t K) { return (K + kTileK - 1) / kTileK; }
+int64_t affb_tile_bytes(int bits) { return 256 * int64_t(bits) + 128; }
+
+// Visit every lane chunk and scale/bias word of the b-bit layout.
+// chunk(off, n, kb, o): the lane's 4 * bits bytes for row n, k = kb + 32 i + 8 o + j
+// sb(off, n, grp): the (scale, bias) word of group grp of row n
+template <class FC, class FSB>
+void affine_bits_walk(int64_t N, int64_t K, int bits, FC chunk, FSB sb) {
+  const int64_t nt = affb_tiles(K), tb = affb_tile_bytes(bits), pb = nt * tb;
+  for (int64_t p = 0; p < N / 16; ++p)
+    for (int64_t t = 0; t < nt; ++t) {
+      const int64_t base = p * pb + t * tb;
+      for (int lane = 0; lane < 64; ++lane)
+        chunk(base + lane * 4 * bits, p * 16 + (lane & 15), t * kTileK, lane >> 4);
+      for (int c = 0; c < 16; ++c)
+        for (int gi = 0; gi < 2; ++gi) sb(base + 256 * bits + (c * 2 + gi) * 4, p * 16 + c, t * 2 + gi);
+    }
+}
+}  // namespace
+extern "C" {
+
+size_t q4_affine_bits_packed_bytes(int64_t N, int64_t K, int bits) {
+  if (!affine_bits_ok(bits) || N <= 0 || K <= 0 || N % 16 || K % 64) return 0;
+  return size_t(N / 16) * size_t(affb_tiles(K) * affb_tile_bytes(bits));
+}
+
+int q4_affine_bits_repack(const uint8_t* codes, const uint16_t* scale_bf16, const uint16_t* bias_bf16, int64_t N,
+                          int64_t K, int bits, void* packed, size_t packed_bytes) {
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scale_bf16);
+  REQUIRE_PTR(bias_bf16);
+  REQUIRE_PTR(packed);
+  if (!affine_bits_ok(bits)) return fail(Q4_ERR_UNSUPPORTED, "%s: bits=%d not in {2, 3, 5, 6, 8}", __func__, bits);
+  if (int rc = check_nk(__func__, N, K, 64)) return rc;
+  const size_t need = q4_affine_bits_packed_bytes(N, K, bits);
+  if (packed_bytes < need) return fail(Q4_ERR_INVALID_ARG, "%s: packed_bytes=%zu < %zu", __func__, packed_bytes, need);
+  for (int64_t i = 0; i < N * K; ++i)
+    if (codes[i] >> bits) return fail(Q4_ERR_INVALID_ARG, "%s: code %d at %lld exceeds %d bits", __func__, codes[i],
+                                      (long long)i, bits);
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  const int64_t G = K / 64;
+  affine_bits_walk(
+      N, K, bits,
+      [&](int64_t off, int64_t n, int64_t kb, int o) {
+        uint8_t* dst = out + off;
+        std::memset(dst, 0, size_t(4 * bits));
+        for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < 8; ++j) {
+            const int64_t k = kb + 32 * i + 8 * o + j;
+            const unsigned q = k < K ? codes[n * K + k] : 0u;
+            const int bit = 8 * bits * i + bits * j;
+            for (int b = 0; b < bits; ++b)
+              if (q >> b & 1u) dst[(bit + b) >> 3] |= uint8_t(1u << ((bit + b) & 7));
+          }
+      },
+      [&](int64_t off, int64_t n, int64_t grp) {
+        const uint16_t sv = grp < G ? scale_bf16[n * G + grp] : 0, bv = grp < G ? bias_bf16[n * G + grp] : 0;
+        std::memcpy(out + off, &sv, 2);
+        std::memcpy(out + off + 2, &bv, 2);
+      });
+  return ok();
+}
+
+int q4_affine_bits_unpack(const void* packed, int64_t N, int64_t K, int bits, uint8_t* codes, uint16_t* scale_bf16,
+                          uint16_t* bias_bf16) {
+  REQUIRE_PTR(packed);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scale_bf16);
+  REQUIRE_PTR(bias_bf16);
+  if (!affine_bits_ok(bits)) return fail(Q4_ERR_UNSUPPORTED, "%s: bits=%d not in {2, 3, 5, 6, 8}", __func__, bits);
+  if (int rc = check_nk(__func__, N, K, 64)) return rc;
+  const uint8_t* in = static_cast<const uint8_t*>(packed);
+  const int64_t G = K / 64;
+  affine_bits_walk(
+      N, K, bits,
+      [&](int64_t off, int64_t n, int64_t kb, int o) {
+        const uint8_t* src = in + off;
+        for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < 8; ++j) {
+            const int64_t k = kb + 32 * i + 8 * o + j;
+            if (k >= K) continue;
+            const int bit = 8 * bits * i + bits * j;
+            unsigned q = 0;
+            for (int b = 0; b < bits; ++b) q |= unsigned(src[(bit + b) >> 3] >> ((bit + b) & 7) & 1u) << b;
+            codes[n * K + k] = uint8_t(q);
+          }
+      },
+      [&](int64_t off, int64_t n, int64_t grp) {
+        if (grp >= G) return;
+        std::memcpy(&scale_bf16[n * G + grp], in + off, 2);
+        std::memcpy(&bias_bf16[n * G + grp], in + off + 2, 2);
+      });
+  return ok();
+}
+
+int qgemm_affine_bits(const void* w_packed, const void* a, int M, int64_t K, int64_t N, int bits, void* out,
+                      int out_dtype, void* stream) {
+  REQUIRE_PTR(w_packed);
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(out);
+  if (!affine_bits_ok(bits)) return fail(Q4_ERR_UNSUPPORTED, "%s: bits=%d not in {2, 3, 5, 6, 8}", __func__, bits);
+  if (M < 1 || M > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: M=%d outside 1..16", __func__, M);
+  if (int rc = check_nk(__func__, N, K, 64)) return rc;
+  if (out_dtype != Q4_F32 && out_dtype != Q4_BF16)
+    return fail(Q4_ERR_INVALID_ARG, "%s: out_dtype=%d is not Q4_F32 or Q4_BF16", __func__, out_dtype);
+  REQUIRE_ALIGNED(w_packed);
+  REQUIRE_ALIGNED(a);
+  REQUIRE_ALIGNED(out);
+  if (int e = launch_affine_bits(bits, static_cast<const uint8_t*>(w_packed), N, K, static_cast<const uint16_t*>(a), M,
+                                 out, out_dtype, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
+}
+
 // ---- MoE block -----------------------------------------------------------
 // Workspace: [0, sub) is shared by the router and the two grouped calls (run
 // one after another on the stream), then the block's own buffers.

@@ -104,6 +104,9 @@ int launch_block_router(const float* logits, int T, int E, int k, const float* s
                         float eps, int32_t* idx, float* w, int32_t* didx, float* dw, void* stream);
 int launch_block_combine(const float* b1, const float* b2, int T, int D, const float* p1, const float* p2,
                          const float* p, float eps, float* res, void* stream);
+// affine 2/3/5/6/8-bit skinny GEMM (q4mi_affineb.hip)
+int launch_affine_bits(int bits, const uint8_t* w, int64_t N, int64_t K, const uint16_t* a, int M, void* out,
+                       int out_dtype, void* stream);
 // NVFP4 quantizer (q4mi_quant.hip); amax: one scratch word of the workspace
 int launch_quantize(const float* w, int64_t N, int64_t K, float g_in, unsigned* amax, uint8_t* packed, float* g_out,
                     void* stream);

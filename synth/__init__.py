@@ -403,6 +403,9 @@ WORKLOADS = {
     "nvfp4_prefill_m2048_k4096_n8192": dict(kind="nvfp4", seed=107, M=2048, K=4096, N=8192, out="f32"),
     # the tied embedding in fp32, N(0, 0.02), for the device quantizer
     "nvfp4_quantize_n262144_k2816": dict(kind="quant", seed=103, N=262144, K=2816, std=0.02),
+    # the other MLX affine widths at the affine workload's shape
+    "affine2_m16_k5120_n15360": dict(kind="affine_bits", bits=2, seed=109, M=16, K=5120, N=15360, out="f32"),
+    "affine8_m16_k5120_n15360": dict(kind="affine_bits", bits=8, seed=110, M=16, K=5120, N=15360, out="f32"),
     "affine4_m1_k5120_n15360": dict(kind="affine", seed=105, M=1, K=5120, N=15360, out="f32"),
     "affine4_m16_k5120_n15360": dict(kind="affine", seed=105, M=16, K=5120, N=15360, out="f32"),
 }

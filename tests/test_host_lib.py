@@ -218,3 +218,46 @@ def test_quantize_refusals_without_gpu():
     for call, code, needle in cases:
         assert call() == code, needle
         assert needle in _err(code), (needle, _err(code))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 5, 6, 8])
+@pytest.mark.parametrize("N,K", [(16, 64), (32, 192), (48, 640)])
+def test_affine_bits_repack_round_trip_and_placement(bits, N, K):
+    import synth
+    q, s, b = synth.affine_weights_bits(11 + bits, N, K, bits)
+    packed = q4.q4_affine_bits_repack(q, s, b, bits)
+    nt = -(-K // 128)
+    assert packed.size == N // 16 * nt * (256 * bits + 128) == q4.raw().q4_affine_bits_packed_bytes(N, K, bits)
+    q2, s2, b2 = q4.q4_affine_bits_unpack(packed, N, K, bits)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s) and np.array_equal(b2, b)
+    # placement as documented: lane (c, o) of tile t holds 4 * bits bytes, code (i, j)
+    # (k = 128 t + 32 i + 8 o + j) at bit 8 bits i + bits j; then (scale | bias << 16) words
+    rng = np.random.default_rng(bits)
+    tb = 256 * bits + 128
+    for _ in range(200):
+        n, k = int(rng.integers(N)), int(rng.integers(K))
+        p, c, t = n // 16, n % 16, k // 128
+        i, o, j = (k % 128) // 32, (k % 32) // 8, k % 8
+        lane = 16 * o + c
+        base = (p * nt + t) * tb + lane * 4 * bits
+        bit = 8 * bits * i + bits * j
+        val = sum(((int(packed[base + (bit + x) // 8]) >> ((bit + x) % 8)) & 1) << x for x in range(bits))
+        assert val == q[n, k]
+        g = k // 64
+        off = (p * nt + t) * tb + 256 * bits + (c * 2 + g % 2) * 4
+        assert int(packed[off]) | int(packed[off + 1]) << 8 == s[n, g]
+        assert int(packed[off + 2]) | int(packed[off + 3]) << 8 == b[n, g]
+
+
+def test_affine_bits_refusals_without_gpu():
+    lib = q4.raw()
+    buf = (C.c_uint8 * 4096)()
+    p = C.c_void_p((C.addressof(buf) + 15) & ~15)
+    assert lib.q4_affine_bits_packed_bytes(16, 64, 4) == 0
+    assert lib.qgemm_affine_bits(p, p, 1, 64, 16, 4, p, q4.Q4_F32, None) == q4.Q4_ERR_UNSUPPORTED
+    assert lib.qgemm_affine_bits(p, p, 17, 64, 16, 2, p, q4.Q4_F32, None) == q4.Q4_ERR_UNSUPPORTED
+    assert lib.qgemm_affine_bits(p, p, 1, 96, 16, 2, p, q4.Q4_F32, None) == q4.Q4_ERR_UNSUPPORTED
+    assert lib.qgemm_affine_bits(p, p, 1, 64, 16, 2, p, q4.Q4_F16, None) == q4.Q4_ERR_INVALID_ARG
+    codes = np.full((16, 64), 4, np.uint8)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_affine_bits_repack(codes, np.zeros((16, 1), np.uint16), np.zeros((16, 1), np.uint16), 2)
