@@ -346,6 +346,9 @@ static int gemm_common(int fmt, const char* fn, const void* w_packed, float gsca
     g.offset = sp->offset;
   }
   if (prefill) {
+    // one workgroup per 64 x 128 block (or a smaller measured shape): keep the grid within int range
+    if ((int64_t(M) + 15) / 16 * ((N + 127) / 128) > (int64_t(1) << 30))
+      return fail(Q4_ERR_UNSUPPORTED, "%s: M=%d x N=%lld too large for one launch", fn, M, (long long)N);
     if (int e = launch_prefill(g, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
     return ok();
   }
