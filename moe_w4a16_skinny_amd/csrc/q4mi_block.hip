@@ -78,9 +78,8 @@ __global__ __launch_bounds__(256) void block_norm_in_kernel(const float* __restr
 }
 
 // One wave per token: z = RMSNorm(logits) * scale over the E <= 256 logits
-// (lane l holds experts l, l + 64, l + 128, l + 192), softmax, then k rounds
-// of a wave-wide arg-max (larger z first, ties to the lower index, NaN never
-// chosen); w = p * down_scale.  Also writes the dense branch's one-expert
+// (lane l holds experts l, l + 64, l + 128, l + 192), softmax, top-k (larger
+// z first, ties to the lower index, k <= 16); w = p * down_scale.  Also writes the dense branch's one-expert
 // routing (expert 0, weight 1).
 __global__ __launch_bounds__(64) void block_router_kernel(const float* __restrict__ logits, int E, int k,
                                                           const float* __restrict__ scale,
@@ -116,34 +115,58 @@ __global__ __launch_bounds__(64) void block_router_kernel(const float* __restric
   for (int j = 0; j < 4; ++j) se += (lane + 64 * j < E) ? expf(z[j] - m) : 0.f;
   for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
   se = __shfl(se, 0);
-  unsigned taken = 0u;
-  for (int s = 0; s < k; ++s) {
-    float bv = -INFINITY, bd = 1.0f;
-    int be = 0x7FFFFFFF;
+  // Top-k without a round per pick: find the k-th largest ordered key V by
+  // a bitwise search whose counts are wave ballots, take every key above V
+  // and the lowest-index keys equal to V, park the k picks in LDS, and let
+  // lane r < k place pick r at its rank (larger z first, ties to the lower
+  // index).  NaN scores (key 0) rank lowest.
+  __shared__ unsigned skey[16];
+  __shared__ int sidx[16];
+  __shared__ float sw[16];
+  unsigned key[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !(taken & (1u << j)) && (z[j] > bv || (z[j] == bv && e < be))) {
-        bv = z[j];
-        be = e;
-        bd = ds[j];
-      }
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    const float v = z[j] == 0.f ? 0.f : z[j];  // -0 and +0 are equal
+    const unsigned b = __float_as_uint(v);
+    key[j] = (e < E && v == v) ? ((b & 0x80000000u) ? ~b : (b | 0x80000000u)) : 0u;
+  }
+  unsigned V = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned cand = V | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+    if (cnt >= k) V = cand;
+  }
+  int above = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) above += __popcll(__ballot(key[j] > V));
+  const int need = k - above;  // keys equal to V to take, lowest index first
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int eq_base = 0, sel_base = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const unsigned long long eq = __ballot(key[j] == V);
+    const bool pick = key[j] > V || (key[j] == V && eq_base + __popcll(eq & below) < need);
+    const unsigned long long sel = __ballot(pick);
+    if (pick) {
+      const int slot = sel_base + __popcll(sel & below);
+      skey[slot] = key[j];
+      sidx[slot] = lane + 64 * j;
+      sw[slot] = expf(z[j] - m) / se * ds[j];
     }
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off), od = __shfl_xor(bd, off);
-      const int oe = __shfl_xor(be, off);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-        bd = od;
-      }
-    }
-    if (be != 0x7FFFFFFF && (be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == 0) {
-      const bool ok = be != 0x7FFFFFFF;
-      idx[t * k + s] = ok ? be : -1;
-      w[t * k + s] = ok ? expf(bv - m) / se * bd : 0.f;
-    }
+    eq_base += __popcll(eq);
+    sel_base += __popcll(sel);
+  }
+  __syncthreads();
+  if (lane < k) {
+    const unsigned mk = skey[lane];
+    const int me = sidx[lane];
+    int rank = 0;
+    for (int q = 0; q < k; ++q) rank += (skey[q] > mk || (skey[q] == mk && sidx[q] < me)) ? 1 : 0;
+    idx[t * k + rank] = me;
+    w[t * k + rank] = sw[lane];
   }
   if (lane == 0) {
     didx[t] = 0;
