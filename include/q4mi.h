@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define Q4MI_ABI_VERSION 2
+#define Q4MI_ABI_VERSION 3
 
 enum {
   Q4_OK = 0,

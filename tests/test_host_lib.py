@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q4.EXPORTED)
-    assert q4.abi_version() == 2
+    assert q4.abi_version() == 3
 
 
 @pytest.mark.parametrize("N,K", [(16, 128), (32, 64), (16, 704), (48, 2816), (16, 80), (32, 176), (16, 16)])
