@@ -261,3 +261,34 @@ def test_affine_bits_refusals_without_gpu():
     codes = np.full((16, 64), 4, np.uint8)
     with pytest.raises(q4.Q4Error):
         q4.q4_affine_bits_repack(codes, np.zeros((16, 1), np.uint16), np.zeros((16, 1), np.uint16), 2)
+
+
+def test_moe_block_refusals_without_gpu():
+    lib = q4.raw()
+    buf = (C.c_uint8 * 8192)()
+    al = (C.addressof(buf) + 255) & ~255
+    p = C.c_void_p(al)
+    exp = q4.q4_moe_desc(8, 0, 256, 64, p, p, p, p, p, p)
+    dense = q4.q4_moe_desc(1, 0, 256, 128, p, p, p, p, p, p)
+    d = q4.q4_moe_block_desc(exp, dense, p, p, None, p, p, p, p, p, 1e-6)
+    wsb = lib.moe_block_workspace_bytes(C.byref(d), 4, 2)
+    assert wsb > 32768
+
+    def call(desc, T=4, k=2, ws=p, nb=wsb):
+        return lib.moe_block_forward(C.byref(desc), p, T, k, ws, nb, None)
+
+    bad_eps = q4.q4_moe_block_desc(exp, dense, p, p, None, p, p, p, p, p, 0.0)
+    assert call(bad_eps) == q4.Q4_ERR_INVALID_ARG and "eps" in _err(0)
+    shared = q4.q4_moe_desc(8, 1, 256, 64, p, p, p, p, p, p)
+    assert call(q4.q4_moe_block_desc(shared, dense, p, p, None, p, p, p, p, p, 1e-6)) == q4.Q4_ERR_INVALID_ARG
+    two = q4.q4_moe_desc(2, 0, 256, 128, p, p, p, p, p, p)
+    assert call(q4.q4_moe_block_desc(exp, two, p, p, None, p, p, p, p, p, 1e-6)) == q4.Q4_ERR_INVALID_ARG
+    other_d = q4.q4_moe_desc(1, 0, 512, 128, p, p, p, p, p, p)
+    assert call(q4.q4_moe_block_desc(exp, other_d, p, p, None, p, p, p, p, p, 1e-6)) == q4.Q4_ERR_INVALID_ARG
+    assert call(q4.q4_moe_block_desc(exp, dense, p, None, None, p, p, p, p, p, 1e-6)) == q4.Q4_ERR_INVALID_ARG
+    assert call(d, T=17) == q4.Q4_ERR_UNSUPPORTED
+    assert call(d, ws=None) == q4.Q4_ERR_WORKSPACE
+    assert call(d, nb=wsb - 1) == q4.Q4_ERR_WORKSPACE
+    big = q4.q4_moe_desc(8, 0, 8192, 64, p, p, p, p, p, p)
+    bigd = q4.q4_moe_desc(1, 0, 8192, 128, p, p, p, p, p, p)
+    assert call(q4.q4_moe_block_desc(big, bigd, p, p, None, p, p, p, p, p, 1e-6)) == q4.Q4_ERR_UNSUPPORTED
