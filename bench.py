@@ -294,7 +294,7 @@ class MoeWork:
 
 class MoeBlockWork:
     """One step = moe_block_forward: input norms, router matmul, router norm and
-    top-k, dense branch, experts, combine (7 launches) on the residual."""
+    top-k, dense branch, experts, combine (10 launches) on the residual."""
 
     def __init__(self, name, spec, hot):
         import numpy as np

@@ -331,7 +331,7 @@ size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k);
  *   ws       device workspace of ws_bytes >= moe_block_workspace_bytes; its
  *            first 32 KiB of counters start and end at zero, as for the
  *            other entry points
- * The block runs 7 launches on `stream`: the two input norms, the router
+ * The block runs 10 launches on `stream`: the two input norms, the router
  * matmul (moe_route_topk's kernel), the router normalization and top-k, the
  * dense branch and the experts (moe_grouped_qgemm's kernels, sharing the
  * workspace), and the combine.
