@@ -21,6 +21,9 @@ roofline     = algorithmic bytes of the dominant launch / its mean duration (the
                the counted HBM bytes per launch from the committed counter summary
                (profiles/traffic.json) when it was taken on the current kernel
                sources, else null
+               stream_ceiling = q4_stream_read of the same number of bytes (16-byte
+               non-temporal loads and nothing else, rotated like the weights, the
+               fastest of a few launch shapes): the measured floor for those bytes
 cpu_baseline = the float64 CPU oracle on a bounded sample of the same workload, on
                this host's cores
 """
@@ -58,6 +61,7 @@ def parse():
     ap.add_argument("--copy-kernel", type=int, default=0,
                     help="instead of the path, time a device copy of this many MiB (counter calibration)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the stream-read ceiling measurement")
     return ap.parse_args()
 
 
@@ -435,6 +439,57 @@ class CopyWork:
         return {"workload": f"device_copy_{self.nbytes >> 20}MiB"}
 
 
+def stream_ceiling(nbytes, steps):
+    """The stream-read ceiling for `nbytes`: q4_stream_read over rotated copies
+    (>= 2 GiB in total, as for the weights), each launch shape timed as a HIP
+    graph of `steps` launches; the fastest shape is the ceiling."""
+    import ctypes as C
+
+    import torch
+
+    import moe_w4a16_skinny_amd as q4
+    lib = q4.raw()
+    n = -(-nbytes // 16) * 16
+    stride = -(-n // 4096) * 4096
+    copies = max(2, -(-ROTATE_BYTES // stride))
+    buf = torch.zeros(copies * stride, dtype=torch.uint8, device="cuda")
+    out = torch.empty(65536, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    n16 = n // 16
+    shapes = [(mode, grid, depth) for mode in (0, 1) for depth in (2, 4, 8) for grid in (256, 512, 1024, 2048)]
+    # and the grids in which every lane issues exactly one or two batches
+    shapes += [(0, max(1, min(65536, -(-n16 // (256 * depth * nb)))), depth) for depth in (2, 4, 8) for nb in (1, 2)]
+    for mode, grid, depth in shapes:
+        def step(i):
+            rc = lib.q4_stream_read(C.c_void_p(buf.data_ptr() + (i % copies) * stride), n, grid, mode, depth,
+                                    C.c_void_p(out.data_ptr()), q4._stream())
+            if rc != 0:
+                q4._check(rc)
+        for i in range(3):
+            step(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        if best is None or us < best["mean_launch_us"]:
+            best = {"bytes": n, "mean_launch_us": round(us, 3), "GB/s": round(n / us / 1e3, 1),
+                    "frac_of_peak": round(n / us / 1e3 / HBM_PEAK_GBS, 4), "grid": grid, "depth": depth,
+                    "mode": "grid-stride" if mode == 0 else "chunk per workgroup",
+                    "kernel": "stream_read_kernel (q4_stream_read)"}
+        del g
+    del buf
+    return best
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -538,6 +593,10 @@ def main():
             "empty_kernel_interval_us": round(launch_interval * 1e6, 3),
         },
     }
+    if not args.copy_kernel and not args.no_ceiling and rec["roofline"]["bound"] == "hbm":
+        ceil = stream_ceiling(work.alg_bytes, min(K, 100))
+        rec["roofline"]["stream_ceiling"] = ceil
+        rec["roofline"]["frac_of_ceiling"] = round(achieved / ceil["GB/s"], 4)
     if not args.no_cpu_baseline and not args.copy_kernel:
         gbs, sample = work.cpu_oracle_sample(args.cpu_seconds)
         rec["cpu_baseline"] = {"value": round(gbs, 4), "unit": "GB/s", "cores": threads_used(),

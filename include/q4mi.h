@@ -41,7 +41,8 @@
  *     of the largest queried size can therefore serve every entry point, as
  *     long as the calls that share it are ordered on one stream (calls that
  *     overlap in time on a shared workspace race).
- *   - Entries are re-entrant.
+ *   - Entries are re-entrant: any number of host threads may call them at
+ *     once (each with its own workspace, or ordered on one stream).
  */
 #ifndef Q4MI_H
 #define Q4MI_H
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define Q4MI_ABI_VERSION 3
+#define Q4MI_ABI_VERSION 4
 
 enum {
   Q4_OK = 0,
@@ -327,21 +328,28 @@ typedef struct {
 size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k);
 
 /* One MoE block on the residual stream, in place.
- *   residual device fp32 [T][D], updated r <- r + update
- *   ws       device workspace of ws_bytes >= moe_block_workspace_bytes; its
- *            first 32 KiB of counters start and end at zero, as for the
- *            other entry points
+ *   residual     device fp32 [T][D], updated r <- r + update
+ *   topk_idx_out device int32 [T][k] receiving the experts the block chose
+ *                (decreasing z, ties to the lower index), or NULL
+ *   topk_w_out   device fp32 [T][k] receiving their weights
+ *                softmax(z)[idx] * down_scale[idx], or NULL; with these, a
+ *                caller sees the routing the outputs were computed with
+ *                (several are valid where scores tie within rounding)
+ *   ws           device workspace of ws_bytes >= moe_block_workspace_bytes;
+ *                its first 32 KiB of counters start and end at zero, as for
+ *                the other entry points
  * The block runs 10 launches on `stream`: the two input norms, the router
  * matmul (moe_route_topk's kernel), the router normalization and top-k, the
  * dense branch and the experts (moe_grouped_qgemm's kernels, sharing the
  * workspace), and the combine.
  * Errors: INVALID_ARG (NULL pointers, eps <= 0 or not finite, dense not a
- * one-expert layer, D mismatch, has_shared set), UNSUPPORTED (T > 16,
- * E > 256, D > 4096), the errors of
- * moe_route_topk and moe_grouped_qgemm for these shapes, ALIGNMENT,
- * WORKSPACE, HIP. */
-int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k, void* ws, size_t ws_bytes,
-                      void* stream);
+ * one-expert layer, D mismatch, has_shared set, T or k < 1), UNSUPPORTED
+ * (T > 16, E > 256, D > 4096), the errors of moe_route_topk and
+ * moe_grouped_qgemm for these shapes (k > min(E, 16), D % 64, F % 64, ...),
+ * ALIGNMENT, WORKSPACE, HIP.  Every refusal happens before the first
+ * launch. */
+int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k, int32_t* topk_idx_out,
+                      float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Test exports: the same device dequantization the GEMMs use, written out.
@@ -357,6 +365,23 @@ int q4_dequant_nvfp4(const void* w_packed, float global_scale, int64_t N, int64_
 
 /* out[n][k] (device fp32 [N][K]) = fmaf(q, scale, bias) from the packed matrix. */
 int q4_dequant_affine4(const void* w_packed, int64_t N, int64_t K, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement export.  [README "Why it's NVIDIA-only": the kernels are tuned
+ * against the bandwidth the memory really delivers.]  The stream-read
+ * ceiling: reads `bytes` of device memory at `src` with the loads the
+ * weight-streaming kernels issue (16-byte non-temporal loads, each wave
+ * instruction covering 1 KiB) and nothing else, so that its duration is the
+ * floor for streaming that many bytes.
+ *   src    device, 16-byte aligned, `bytes` readable (a positive multiple of 16)
+ *   grid   workgroups of 256 threads, 1..65536
+ *   mode   0: grid-stride (consecutive waves read consecutive KiB);
+ *          1: workgroup b reads the b-th of `grid` contiguous chunks
+ *   depth  loads per lane per batch (1, 2, 4 or 8); each lane keeps two
+ *          batches in flight
+ *   out    device u32[grid]: the XOR of each workgroup's words
+ * Errors: INVALID_ARG (NULL, bytes, grid, mode, depth), ALIGNMENT, HIP. */
+int q4_stream_read(const void* src, size_t bytes, int grid, int mode, int depth, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -68,9 +68,10 @@ _SIGS = {
     "q4_affine_bits_unpack": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "qgemm_affine_bits": (_i32, [_vp, _vp, _i32, _i64, _i64, _i32, _vp, _i32, _vp]),
     "moe_block_workspace_bytes": (_sz, [C.POINTER(q4_moe_block_desc), _i32, _i32]),
-    "moe_block_forward": (_i32, [C.POINTER(q4_moe_block_desc), _vp, _i32, _i32, _vp, _sz, _vp]),
+    "moe_block_forward": (_i32, [C.POINTER(q4_moe_block_desc), _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "q4_dequant_nvfp4": (_i32, [_vp, _f32, _i64, _i64, _vp, _vp]),
     "q4_dequant_affine4": (_i32, [_vp, _i64, _i64, _vp, _vp]),
+    "q4_stream_read": (_i32, [_vp, _sz, _i32, _i32, _i32, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -396,8 +397,9 @@ def moe_block_pack(blk, eps: float = 1e-6, device="cuda") -> MoeBlockWeights:
                            f(blk.down_scale) if blk.down_scale is not None else None, norms, eps)
 
 
-def moe_block_forward(block: MoeBlockWeights, residual, k: int):
-    """One MoE block on the residual stream (fp32 [T][D] device tensor), in place; returns it."""
+def moe_block_forward(block: MoeBlockWeights, residual, k: int, want_routing: bool = False):
+    """One MoE block on the residual stream (fp32 [T][D] device tensor), in place; returns it,
+    or (residual, topk_idx int32 [T][k], topk_w fp32 [T][k]) with want_routing."""
     torch = _torch()
     if residual.dtype != torch.float32 or not residual.is_contiguous():
         raise ValueError("residual must be a contiguous fp32 [T][D] tensor")
@@ -405,8 +407,13 @@ def moe_block_forward(block: MoeBlockWeights, residual, k: int):
     d = block.desc()
     wsb = _lib.moe_block_workspace_bytes(C.byref(d), T, k)
     ws = workspace(wsb, residual.device)
-    _check(_lib.moe_block_forward(C.byref(d), _tptr(residual), T, k, _tptr(ws), wsb, _stream()))
-    return residual
+    idx = w = None
+    if want_routing:
+        idx = torch.empty((T, max(k, 1)), dtype=torch.int32, device=residual.device)
+        w = torch.empty((T, max(k, 1)), dtype=torch.float32, device=residual.device)
+    _check(_lib.moe_block_forward(C.byref(d), _tptr(residual), T, k, _tptr(idx), _tptr(w), _tptr(ws), wsb,
+                                  _stream()))
+    return (residual, idx, w) if want_routing else residual
 
 
 def q4_affine_bits_repack(codes: np.ndarray, scale_bf16: np.ndarray, bias_bf16: np.ndarray, bits: int) -> np.ndarray:

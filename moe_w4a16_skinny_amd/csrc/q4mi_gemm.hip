@@ -464,16 +464,8 @@ __global__ __launch_bounds__(64) void dequant_kernel(const uint8_t* __restrict__
 template <int FMT, int P, int W, int D, bool RING, bool SAMPLE>
 int launch_cfg(const GemmParams& kp, hipStream_t s) {
   const size_t lds = gemm_lds_bytes(kp.g.M, kp.KR, kp.KW, kp.PB, RING, W, D);
-  static size_t lds_allowed = 48 * 1024;  // per instantiation: raise the dynamic LDS limit on demand
-  if (lds > lds_allowed) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qgemm_kernel<FMT, P, W, D, RING, SAMPLE>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) {
-      (void)hipGetLastError();  // do not leave the error for the next call
-      return static_cast<int>(e);
-    }
-    lds_allowed = lds;
-  }
+  if (int e = ensure_dynamic_lds(reinterpret_cast<const void*>(&qgemm_kernel<FMT, P, W, D, RING, SAMPLE>), lds))
+    return e;
   hipLaunchKernelGGL((qgemm_kernel<FMT, P, W, D, RING, SAMPLE>), dim3(kp.nblocks * kp.KS), dim3(64 * W), lds, s, kp);
   return static_cast<int>(hipGetLastError());
 }

@@ -1,15 +1,50 @@
 // Host side of libq4mi: argument validation, offline repack/unpack, workspace
 // queries, and the extern "C" entry points that enqueue the HIP kernels.
+#include <hip/hip_runtime.h>
+
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "q4mi.h"
 #include "q4mi_internal.h"
 
 using namespace q4mi;
+
+namespace q4mi {
+
+int ensure_dynamic_lds(const void* fn, size_t bytes) {
+  if (bytes <= 48 * 1024) return 0;  // within the default limit
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return static_cast<int>(e);
+  struct Set {
+    const void* fn;
+    int dev;
+    size_t bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Set> done;
+  std::lock_guard<std::mutex> lock(mu);
+  Set* cur = nullptr;
+  for (Set& d : done)
+    if (d.fn == fn && d.dev == dev) cur = &d;
+  if (cur && cur->bytes >= bytes) return 0;
+  if (hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes))) {
+    (void)hipGetLastError();  // do not leave the error for the next call
+    return static_cast<int>(e);
+  }
+  if (cur)
+    cur->bytes = bytes;
+  else
+    done.push_back(Set{fn, dev, bytes});
+  return 0;
+}
+
+}  // namespace q4mi
 
 namespace {
 
@@ -387,6 +422,20 @@ int qgemm_affine4(const void* w_packed, const void* a, int M, int64_t K, int64_t
   return gemm_common(kAffine, __func__, w_packed, 1.0f, a, M, K, N, out, out_dtype, nullptr, ws, ws_bytes, stream);
 }
 
+int q4_stream_read(const void* src, size_t bytes, int grid, int mode, int depth, uint32_t* out, void* stream) {
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(out);
+  if (bytes == 0 || bytes % 16) return fail(Q4_ERR_INVALID_ARG, "%s: bytes=%zu is not a positive multiple of 16", __func__, bytes);
+  if (grid < 1 || grid > 65536) return fail(Q4_ERR_INVALID_ARG, "%s: grid=%d outside 1..65536", __func__, grid);
+  if (mode != 0 && mode != 1) return fail(Q4_ERR_INVALID_ARG, "%s: mode=%d is not 0 or 1", __func__, mode);
+  if (depth != 1 && depth != 2 && depth != 4 && depth != 8)
+    return fail(Q4_ERR_INVALID_ARG, "%s: depth=%d is not 1, 2, 4 or 8", __func__, depth);
+  REQUIRE_ALIGNED(src);
+  if (int e = launch_stream_read(src, bytes, grid, mode, depth, out, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  return ok();
+}
+
 int q4_dequant_nvfp4(const void* w_packed, float global_scale, int64_t N, int64_t K, float* out, void* stream) {
   REQUIRE_PTR(w_packed);
   REQUIRE_PTR(out);
@@ -417,29 +466,34 @@ size_t moe_route_workspace_bytes(int T, int D, int E) {
   return kWsCounterBytes + size_t(route_splits(D)) * size_t(T) * size_t(E) * sizeof(float);
 }
 
-int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k, int renormalize, float* logits,
-                   int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
-  REQUIRE_PTR(x);
-  REQUIRE_PTR(w_router);
-  REQUIRE_PTR(topk_idx);
-  REQUIRE_PTR(topk_w);
+}  // extern "C"
+
+// Every condition moe_route_topk refuses, checked without enqueueing anything.
+static int route_check(const char* fn, const void* x, const float* w_router, int T, int D, int E, int k,
+                       const float* logits, const int32_t* topk_idx, const float* topk_w, const void* ws,
+                       size_t ws_bytes) {
+  if (!x || !w_router || !topk_idx || !topk_w)
+    return fail(Q4_ERR_INVALID_ARG, "%s: x, w_router, topk_idx and topk_w must not be NULL", fn);
   if (T < 1 || D < 1 || E < 1 || k < 1)
-    return fail(Q4_ERR_INVALID_ARG, "%s: T=%d D=%d E=%d k=%d must be positive", __func__, T, D, E, k);
-  if (T > 64) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d > 64", __func__, T);
-  if (E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", __func__, E);
-  if (k > E || k > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d must be <= E=%d and <= 16", __func__, k, E);
-  if (D % 8) return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d is not a multiple of 8", __func__, D);
+    return fail(Q4_ERR_INVALID_ARG, "%s: T=%d D=%d E=%d k=%d must be positive", fn, T, D, E, k);
+  if (T > 64) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d > 64", fn, T);
+  if (E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", fn, E);
+  if (k > E || k > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d must be <= E=%d and <= 16", fn, k, E);
+  if (D % 8) return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d is not a multiple of 8", fn, D);
   if (route_rows(D) > kRouteMaxRows)
-    return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d > %d", __func__, D, kRouteMaxSplits * kRouteMaxRows);
-  REQUIRE_ALIGNED(x);
-  REQUIRE_ALIGNED(w_router);
-  REQUIRE_ALIGNED(topk_idx);
-  REQUIRE_ALIGNED(topk_w);
-  if (logits) REQUIRE_ALIGNED(logits);
-  if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
-  REQUIRE_ALIGNED(ws);
+    return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d > %d", fn, D, kRouteMaxSplits * kRouteMaxRows);
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      (logits && !aligned16(logits)))
+    return fail(Q4_ERR_ALIGNMENT, "%s: x, w_router, topk_idx, topk_w and logits must be 16-byte aligned", fn);
+  if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", fn);
+  if (!aligned16(ws)) return fail(Q4_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
   if (ws_bytes < moe_route_workspace_bytes(T, D, E))
-    return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, moe_route_workspace_bytes(T, D, E));
+    return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", fn, ws_bytes, moe_route_workspace_bytes(T, D, E));
+  return Q4_OK;
+}
+
+static int route_enqueue(const char* fn, const void* x, const float* w_router, int T, int D, int E, int k,
+                         int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws, void* stream) {
   RouteArgs r{};
   r.x = static_cast<const uint16_t*>(x);
   r.wr = w_router;
@@ -455,7 +509,17 @@ int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, in
   r.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
   r.nsplit = route_splits(D);
   r.rows = route_rows(D);
-  if (int e = launch_route(r, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  if (int e = launch_route(r, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
+  return Q4_OK;
+}
+
+extern "C" {
+
+int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, int k, int renormalize, float* logits,
+                   int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = route_check(__func__, x, w_router, T, D, E, k, logits, topk_idx, topk_w, ws, ws_bytes)) return rc;
+  if (int rc = route_enqueue(__func__, x, w_router, T, D, E, k, renormalize, logits, topk_idx, topk_w, ws, stream))
+    return rc;
   return ok();
 }
 
@@ -484,42 +548,42 @@ size_t moe_workspace_bytes(const q4_moe_desc* w, int T, int k) {
   return moe_ws_layout(w, T, k, &h, &o, &r, &g);
 }
 
-int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_idx, const float* topk_w, int T,
-                      int k, void* y, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
-  REQUIRE_PTR(w);
-  REQUIRE_PTR(x);
-  REQUIRE_PTR(topk_idx);
-  REQUIRE_PTR(topk_w);
-  REQUIRE_PTR(y);
-  REQUIRE_PTR(w->gate_packed);
-  REQUIRE_PTR(w->up_packed);
-  REQUIRE_PTR(w->down_packed);
-  REQUIRE_PTR(w->g_gate);
-  REQUIRE_PTR(w->g_up);
-  REQUIRE_PTR(w->g_down);
+}  // extern "C"
+
+// Every condition moe_grouped_qgemm refuses, checked without enqueueing anything.
+static int moe_check(const char* fn, const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
+                     const float* topk_w, int T, int k, const void* y, int out_dtype, const void* ws,
+                     size_t ws_bytes) {
+  if (!w) return fail(Q4_ERR_INVALID_ARG, "%s: w is NULL", fn);
+  if (!x || !topk_idx || !topk_w || !y)
+    return fail(Q4_ERR_INVALID_ARG, "%s: x, topk_idx, topk_w and y must not be NULL", fn);
+  if (!w->gate_packed || !w->up_packed || !w->down_packed || !w->g_gate || !w->g_up || !w->g_down)
+    return fail(Q4_ERR_INVALID_ARG, "%s: a weight or global-scale pointer of the descriptor is NULL", fn);
   if (w->E < 1 || w->D < 1 || w->F < 1 || (w->has_shared != 0 && w->has_shared != 1))
-    return fail(Q4_ERR_INVALID_ARG, "%s: bad descriptor (E=%d D=%d F=%d has_shared=%d)", __func__, w->E, w->D, w->F,
+    return fail(Q4_ERR_INVALID_ARG, "%s: bad descriptor (E=%d D=%d F=%d has_shared=%d)", fn, w->E, w->D, w->F,
                 w->has_shared);
-  if (T < 1 || T > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d outside 1..16", __func__, T);
-  if (k < 1 || k > w->E || k > 64) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d outside 1..min(E=%d, 64)", __func__, k, w->E);
+  if (T < 1 || T > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d outside 1..16", fn, T);
+  if (k < 1 || k > w->E || k > 64) return fail(Q4_ERR_UNSUPPORTED, "%s: k=%d outside 1..min(E=%d, 64)", fn, k, w->E);
   if (w->D % 64 || w->F % 64)
-    return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d and F=%d must be multiples of 64", __func__, w->D, w->F);
-  if (w->E > 1024) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 1024", __func__, w->E);
+    return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d and F=%d must be multiples of 64", fn, w->D, w->F);
+  if (w->E > 1024) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 1024", fn, w->E);
   if (out_dtype != Q4_F32 && out_dtype != Q4_F16)
-    return fail(Q4_ERR_INVALID_ARG, "%s: out_dtype=%d is not Q4_F32 or Q4_F16", __func__, out_dtype);
-  REQUIRE_ALIGNED(x);
-  REQUIRE_ALIGNED(topk_idx);
-  REQUIRE_ALIGNED(topk_w);
-  REQUIRE_ALIGNED(y);
-  REQUIRE_ALIGNED(w->gate_packed);
-  REQUIRE_ALIGNED(w->up_packed);
-  REQUIRE_ALIGNED(w->down_packed);
-  if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
-  REQUIRE_ALIGNED(ws);
-  size_t h_off, o_off;
-  size_t r_off = 0, g_off = 0;
+    return fail(Q4_ERR_INVALID_ARG, "%s: out_dtype=%d is not Q4_F32 or Q4_F16", fn, out_dtype);
+  if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(y) || !aligned16(w->gate_packed) ||
+      !aligned16(w->up_packed) || !aligned16(w->down_packed))
+    return fail(Q4_ERR_ALIGNMENT, "%s: x, topk_idx, topk_w, y and the packed weights must be 16-byte aligned", fn);
+  if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", fn);
+  if (!aligned16(ws)) return fail(Q4_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
+  size_t h_off, o_off, r_off, g_off;
   const size_t need = moe_ws_layout(w, T, k, &h_off, &o_off, &r_off, &g_off);
-  if (ws_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, need);
+  if (ws_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", fn, ws_bytes, need);
+  return Q4_OK;
+}
+
+static int moe_enqueue(const char* fn, const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
+                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws, void* stream) {
+  size_t h_off, o_off, r_off, g_off;
+  (void)moe_ws_layout(w, T, k, &h_off, &o_off, &r_off, &g_off);
   MoeArgs m{};
   m.E = w->E;
   m.has_shared = w->has_shared;
@@ -546,7 +610,16 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
   m.o = reinterpret_cast<float*>(static_cast<char*>(ws) + o_off);
   m.rowof = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + r_off);
   m.grp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + g_off);
-  if (int e = launch_moe(m, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  if (int e = launch_moe(m, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
+  return Q4_OK;
+}
+
+extern "C" {
+
+int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_idx, const float* topk_w, int T,
+                      int k, void* y, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = moe_check(__func__, w, x, topk_idx, topk_w, T, k, y, out_dtype, ws, ws_bytes)) return rc;
+  if (int rc = moe_enqueue(__func__, w, x, topk_idx, topk_w, T, k, y, out_dtype, ws, stream)) return rc;
   return ok();
 }
 
@@ -702,12 +775,16 @@ static BlockWs block_ws(const q4_moe_block_desc* b, int T, int k) {
 }
 
 size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k) {
-  if (!b || T < 1 || k < 1 || b->experts.D < 1 || b->experts.E < 1) return 0;
+  if (!b || T < 1 || T > 64 || k < 1 || k > 64 || b->experts.D < 1 || b->experts.E < 1 || b->experts.F < 1 ||
+      b->dense.F < 1)
+    return 0;
   return block_ws(b, T, k).total;
 }
 
-int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k, void* ws, size_t ws_bytes,
-                      void* stream) {
+int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k, int32_t* topk_idx_out,
+                      float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  // every refusal, of this entry and of the calls it makes below, comes
+  // before the first launch: on error nothing is enqueued
   REQUIRE_PTR(b);
   REQUIRE_PTR(residual);
   REQUIRE_PTR(b->w_router);
@@ -725,39 +802,48 @@ int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k,
   if (b->dense.E != 1 || b->dense.has_shared != 0 || b->dense.D != b->experts.D)
     return fail(Q4_ERR_INVALID_ARG, "%s: dense must be a one-expert layer (E=1, has_shared=0) of D=%d", __func__,
                 b->experts.D);
-  if (T < 1 || T > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d outside 1..16", __func__, T);
+  if (T < 1 || k < 1) return fail(Q4_ERR_INVALID_ARG, "%s: T=%d and k=%d must be positive", __func__, T, k);
+  if (T > 16) return fail(Q4_ERR_UNSUPPORTED, "%s: T=%d outside 1..16", __func__, T);
   if (b->experts.E > 256) return fail(Q4_ERR_UNSUPPORTED, "%s: E=%d > 256", __func__, b->experts.E);
   if (b->experts.D > 4096) return fail(Q4_ERR_UNSUPPORTED, "%s: D=%d > 4096", __func__, b->experts.D);
   REQUIRE_ALIGNED(residual);
+  if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
+    return fail(Q4_ERR_ALIGNMENT, "%s: topk_idx_out and topk_w_out must be 16-byte aligned", __func__);
   if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", __func__);
   REQUIRE_ALIGNED(ws);
   const BlockWs L = block_ws(b, T, k);
   if (ws_bytes < L.total) return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, L.total);
   char* base = static_cast<char*>(ws);
   const int D = b->experts.D, E = b->experts.E;
+  int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(base + L.idx);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + L.w);
+  const void* h1 = base + L.h1;
+  const void* h2 = base + L.h2;
+  float* logits = reinterpret_cast<float*>(base + L.logits);
+  const int32_t* didx = reinterpret_cast<const int32_t*>(base + L.didx);
+  const float* dw = reinterpret_cast<const float*>(base + L.dw);
+  float* b1 = reinterpret_cast<float*>(base + L.b1);
+  float* b2 = reinterpret_cast<float*>(base + L.b2);
+  if (int rc = route_check(__func__, h2, b->w_router, T, D, E, k, logits, reinterpret_cast<int32_t*>(base + L.ridx),
+                           reinterpret_cast<float*>(base + L.rw), ws, L.sub))
+    return rc;
+  if (int rc = moe_check(__func__, &b->dense, h1, didx, dw, T, 1, b1, Q4_F32, ws, L.sub)) return rc;
+  if (int rc = moe_check(__func__, &b->experts, h2, idx, w, T, k, b2, Q4_F32, ws, L.sub)) return rc;
   if (int e = launch_block_norm_in(residual, T, D, b->ffn_norm, b->pre_ffw_norm_2, b->eps, base + L.h1, base + L.h2,
                                    stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
-  if (int rc = moe_route_topk(base + L.h2, b->w_router, T, D, E, k, 0, reinterpret_cast<float*>(base + L.logits),
-                              reinterpret_cast<int32_t*>(base + L.ridx), reinterpret_cast<float*>(base + L.rw), ws,
-                              L.sub, stream))
+  if (int rc = route_enqueue(__func__, h2, b->w_router, T, D, E, k, 0, logits,
+                             reinterpret_cast<int32_t*>(base + L.ridx), reinterpret_cast<float*>(base + L.rw), ws,
+                             stream))
     return rc;
-  if (int e = launch_block_router(reinterpret_cast<const float*>(base + L.logits), T, E, k, b->router_scale,
-                                  b->down_scale, b->eps, reinterpret_cast<int32_t*>(base + L.idx),
-                                  reinterpret_cast<float*>(base + L.w), reinterpret_cast<int32_t*>(base + L.didx),
-                                  reinterpret_cast<float*>(base + L.dw), stream))
+  if (int e = launch_block_router(logits, T, E, k, b->router_scale, b->down_scale, b->eps, idx, w,
+                                  reinterpret_cast<int32_t*>(base + L.didx), reinterpret_cast<float*>(base + L.dw),
+                                  stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
-  if (int rc = moe_grouped_qgemm(&b->dense, base + L.h1, reinterpret_cast<const int32_t*>(base + L.didx),
-                                 reinterpret_cast<const float*>(base + L.dw), T, 1, base + L.b1, Q4_F32, ws, L.sub,
-                                 stream))
-    return rc;
-  if (int rc = moe_grouped_qgemm(&b->experts, base + L.h2, reinterpret_cast<const int32_t*>(base + L.idx),
-                                 reinterpret_cast<const float*>(base + L.w), T, k, base + L.b2, Q4_F32, ws, L.sub,
-                                 stream))
-    return rc;
-  if (int e = launch_block_combine(reinterpret_cast<const float*>(base + L.b1),
-                                   reinterpret_cast<const float*>(base + L.b2), T, D, b->post_ffw_norm_1,
-                                   b->post_ffw_norm_2, b->post_ffw_norm, b->eps, residual, stream))
+  if (int rc = moe_enqueue(__func__, &b->dense, h1, didx, dw, T, 1, b1, Q4_F32, ws, stream)) return rc;
+  if (int rc = moe_enqueue(__func__, &b->experts, h2, idx, w, T, k, b2, Q4_F32, ws, stream)) return rc;
+  if (int e = launch_block_combine(b1, b2, T, D, b->post_ffw_norm_1, b->post_ffw_norm_2, b->post_ffw_norm, b->eps,
+                                   residual, stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   return ok();
 }

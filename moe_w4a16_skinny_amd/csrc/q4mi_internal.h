@@ -86,6 +86,12 @@ struct GemmCfg {
   int RING;  // 1: each wave moves its own tiles' activations into an LDS ring (one group per wave, K % 64 == 0)
 };
 
+// Let kernel `fn` use `bytes` of dynamic LDS on the current device: raises the
+// function's limit when this is more than was set before on that device, and
+// never lowers it, so concurrent callers with different needs cannot undo
+// each other.  Thread-safe; returns hipError_t as int.
+int ensure_dynamic_lds(const void* fn, size_t bytes);
+
 // kernel launchers (q4mi_gemm.hip); return hipError_t as int
 GemmCfg choose_gemm_cfg(int fmt, int M, int64_t K, int64_t N);
 size_t gemm_workspace(int fmt, int M, int64_t K, int64_t N);
@@ -107,6 +113,8 @@ int launch_block_combine(const float* b1, const float* b2, int T, int D, const f
 // affine 2/3/5/6/8-bit skinny GEMM (q4mi_affineb.hip)
 int launch_affine_bits(int bits, const uint8_t* w, int64_t N, int64_t K, const uint16_t* a, int M, void* out,
                        int out_dtype, void* stream);
+// stream-read ceiling (q4mi_ceiling.hip): bytes % 16 == 0, out[grid], depth in {1, 2, 4, 8}
+int launch_stream_read(const void* src, size_t bytes, int grid, int mode, int depth, unsigned* out, void* stream);
 // NVFP4 quantizer (q4mi_quant.hip); amax: one scratch word of the workspace
 int launch_quantize(const float* w, int64_t N, int64_t K, float g_in, unsigned* amax, uint8_t* packed, float* g_out,
                     void* stream);

@@ -760,16 +760,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
 int launch_route(const RouteArgs& r, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t need = route_lds_bytes(r.D);
-  static size_t lds_allowed = 48 * 1024;
-  if (need > lds_allowed) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(need));
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      return static_cast<int>(e);
-    }
-    lds_allowed = need;
-  }
+  if (int e = ensure_dynamic_lds(reinterpret_cast<const void*>(&route_kernel), need)) return e;
   hipLaunchKernelGGL(route_kernel, dim3(route_eblocks(r.E) * r.nsplit), dim3(kRouteThreads), need, s, r);
   return static_cast<int>(hipGetLastError());
 }
@@ -792,23 +783,8 @@ int launch_moe(const MoeArgs& m, void* stream) {
   const int dn_ngw = std::min((nexp * ngp + dn_nw - 1) / dn_nw, dn_cap);
   const size_t dn_lds = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
   if (gu_ngw < 1 || dn_ngw < 1) return static_cast<int>(hipErrorInvalidConfiguration);
-  static size_t gu_allowed = 48 * 1024, dn_allowed = 48 * 1024;
-  if (gu_lds > gu_allowed) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(gu_lds)) != hipSuccess) {
-      (void)hipGetLastError();
-      return static_cast<int>(hipErrorInvalidConfiguration);
-    }
-    gu_allowed = gu_lds;
-  }
-  if (dn_lds > dn_allowed) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dn_lds)) != hipSuccess) {
-      (void)hipGetLastError();
-      return static_cast<int>(hipErrorInvalidConfiguration);
-    }
-    dn_allowed = dn_lds;
-  }
+  if (int e = ensure_dynamic_lds(reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4>), gu_lds)) return e;
+  if (int e = ensure_dynamic_lds(reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4>), dn_lds)) return e;
   hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m, gu_ngw);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
   hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw);

@@ -27,10 +27,11 @@ from .formats import (e2m1_value, e4m3_value, unpack_nibbles, nvfp4_dequant,
 from .gemm import (gemm_ref, gemm_abs_bound, nvfp4_gemm_ref, affine_gemm_ref,
                    affine_gemm_groupsum, argmax_ref, affine_bits_gemm_ref)
 from .moe import (gelu_tanh, gelu_tanh_deriv, softmax, route_topk, moe_ref,
-                  moe_ref_grouped, moe_abs_bound)
+                  moe_ref_grouped, moe_abs_bound, a16)
 from .sampling import (philox4, uniform_bits_to_f32, sample_uniforms, gumbel, softcap,
                        sample_scores, sample_tokens)
-from .block import rmsnorm, rmsnorm_bound, route_normed, moe_block_ref, moe_block_bound
+from .block import (rmsnorm, rmsnorm_bound, route_normed, route_normed_bound, routing_weight_bound,
+                    moe_block_ref, moe_block_bound)
 from .quantize import e4m3_encode_rne, e2m1_encode_rne, nvfp4_global_scale_f32, nvfp4_quantize_f32
 
 __all__ = [
@@ -38,8 +39,9 @@ __all__ = [
     "bf16_value", "affine_dequant", "affine_dequant_f32", "gemm_ref", "gemm_abs_bound",
     "nvfp4_gemm_ref", "affine_gemm_ref", "affine_gemm_groupsum", "argmax_ref",
     "gelu_tanh", "gelu_tanh_deriv", "softmax", "route_topk", "moe_ref", "moe_ref_grouped",
-    "moe_abs_bound", "philox4", "uniform_bits_to_f32", "sample_uniforms", "gumbel", "softcap",
+    "moe_abs_bound", "a16", "philox4", "uniform_bits_to_f32", "sample_uniforms", "gumbel", "softcap",
     "sample_scores", "sample_tokens", "e4m3_encode_rne", "e2m1_encode_rne", "nvfp4_global_scale_f32", "affine_dequant_bits", "AFFINE_BITS", "affine_bits_gemm_ref",
-    "rmsnorm", "rmsnorm_bound", "route_normed", "moe_block_ref", "moe_block_bound",
+    "rmsnorm", "rmsnorm_bound", "route_normed", "route_normed_bound", "routing_weight_bound", "moe_block_ref",
+    "moe_block_bound",
     "nvfp4_quantize_f32",
 ]

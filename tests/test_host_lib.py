@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q4.EXPORTED)
-    assert q4.abi_version() == 3
+    assert q4.abi_version() == 4
 
 
 @pytest.mark.parametrize("N,K", [(16, 128), (32, 64), (16, 704), (48, 2816), (16, 80), (32, 176), (16, 16)])
@@ -274,8 +274,8 @@ def test_moe_block_refusals_without_gpu():
     wsb = lib.moe_block_workspace_bytes(C.byref(d), 4, 2)
     assert wsb > 32768
 
-    def call(desc, T=4, k=2, ws=p, nb=wsb):
-        return lib.moe_block_forward(C.byref(desc), p, T, k, ws, nb, None)
+    def call(desc, T=4, k=2, ws=p, nb=wsb, idx=None, w=None):
+        return lib.moe_block_forward(C.byref(desc), p, T, k, idx, w, ws, nb, None)
 
     bad_eps = q4.q4_moe_block_desc(exp, dense, p, p, None, p, p, p, p, p, 0.0)
     assert call(bad_eps) == q4.Q4_ERR_INVALID_ARG and "eps" in _err(0)
@@ -292,3 +292,65 @@ def test_moe_block_refusals_without_gpu():
     big = q4.q4_moe_desc(8, 0, 8192, 64, p, p, p, p, p, p)
     bigd = q4.q4_moe_desc(1, 0, 8192, 128, p, p, p, p, p, p)
     assert call(q4.q4_moe_block_desc(big, bigd, p, p, None, p, p, p, p, p, 1e-6)) == q4.Q4_ERR_UNSUPPORTED
+
+
+def test_moe_block_refuses_downstream_shapes_before_any_launch():
+    # conditions that only the router or the grouped MoE check: the block must
+    # refuse them before its first launch (without a GPU, a launch would
+    # surface as Q4_ERR_HIP instead)
+    lib = q4.raw()
+    buf = (C.c_uint8 * 8192)()
+    p = C.c_void_p((C.addressof(buf) + 255) & ~255)
+    odd = C.c_void_p(p.value + 4)
+
+    def blk(E=8, D=256, F=64, Fd=128):
+        return q4.q4_moe_block_desc(q4.q4_moe_desc(E, 0, D, F, p, p, p, p, p, p),
+                                    q4.q4_moe_desc(1, 0, D, Fd, p, p, p, p, p, p), p, p, None, p, p, p, p, p, 1e-6)
+
+    def call(desc, T=4, k=2, idx=None, w=None):
+        return lib.moe_block_forward(C.byref(desc), p, T, k, idx, w, p, 1 << 30, None)
+
+    cases = [
+        (lambda: call(blk(E=32), k=17), q4.Q4_ERR_UNSUPPORTED, "k=17"),
+        (lambda: call(blk(E=8), k=9), q4.Q4_ERR_UNSUPPORTED, "k=9"),
+        (lambda: call(blk(), k=0), q4.Q4_ERR_INVALID_ARG, "k=0"),
+        (lambda: call(blk(), k=-3), q4.Q4_ERR_INVALID_ARG, "k=-3"),
+        (lambda: call(blk(), T=0), q4.Q4_ERR_INVALID_ARG, "T=0"),
+        (lambda: call(blk(D=2824)), q4.Q4_ERR_UNSUPPORTED, "D=2824"),
+        (lambda: call(blk(D=260)), q4.Q4_ERR_UNSUPPORTED, "D=260"),
+        (lambda: call(blk(F=700)), q4.Q4_ERR_UNSUPPORTED, "F=700"),
+        (lambda: call(blk(Fd=100)), q4.Q4_ERR_UNSUPPORTED, "F=100"),
+        (lambda: call(blk(E=300)), q4.Q4_ERR_UNSUPPORTED, "E=300"),
+        (lambda: call(blk(), idx=odd), q4.Q4_ERR_ALIGNMENT, "topk_idx_out"),
+    ]
+    for fn, code, needle in cases:
+        assert fn() == code, needle
+        assert needle in _err(code), (needle, _err(code))
+    assert lib.moe_block_workspace_bytes(C.byref(blk()), 4, -3) == 0
+    nulls = q4.q4_moe_block_desc(q4.q4_moe_desc(8, 0, 256, 64, None, p, p, p, p, p),
+                                 q4.q4_moe_desc(1, 0, 256, 128, p, p, p, p, p, p), p, p, None, p, p, p, p, p, 1e-6)
+    assert call(nulls) == q4.Q4_ERR_INVALID_ARG
+
+
+def test_dynamic_lds_limit_setup_is_thread_safe():
+    # launchers on many host threads at once: every call must either be
+    # refused on the host or fail at its launch for lack of a GPU, never
+    # with another thread's error (this host has no device, so each launch
+    # reports Q4_ERR_HIP; what is checked is that the calls run concurrently
+    # without corrupting the library's state)
+    import threading
+    lib = q4.raw()
+    buf = (C.c_uint8 * 65536)()
+    p = C.c_void_p((C.addressof(buf) + 255) & ~255)
+    out = []
+
+    def worker(M):
+        for _ in range(50):
+            out.append(lib.qgemm_affine4(p, p, M, 5120, 15360, p, q4.Q4_F32, p, 1 << 30, None))
+
+    th = [threading.Thread(target=worker, args=(m,)) for m in (1, 4, 16, 8)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert len(out) == 200 and set(out) <= {q4.Q4_ERR_HIP, q4.Q4_OK}

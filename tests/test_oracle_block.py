@@ -1,8 +1,10 @@
 """Pins of the MoE-block oracle (oracle/block.py) to things other than itself."""
 import numpy as np
+import pytest
 
 import oracle
 import synth
+from perturb import perturbed_block
 
 
 def test_rmsnorm_closed_forms():
@@ -30,9 +32,21 @@ def test_rmsnorm_bound_dominates_perturbations():
     B = 1e-4 * np.abs(rng.standard_normal((4, 128)))
     bnd = oracle.rmsnorm_bound(v, w, B)
     y = oracle.rmsnorm(v, w)
+    worst = 0.0
     for s in range(20):
         dv = B * rng.choice([-1.0, 1.0], size=B.shape) * rng.uniform(0, 1, B.shape)
-        assert np.all(np.abs(oracle.rmsnorm(v + dv, w) - y) <= bnd * 1.01 + 1e-15)
+        dev = np.abs(oracle.rmsnorm(v + dv, w) - y)
+        assert np.all(dev <= bnd)
+        worst = max(worst, float(np.max(dev / bnd)))
+    # the largest permitted change of one element: dv = +-B everywhere, signed with v there
+    for i in range(3):
+        dv = B * np.where(np.arange(128) == i, 1.0, -np.sign(v) * np.sign(v[:, i:i + 1]))
+        dev = np.abs(oracle.rmsnorm(v + dv, w) - y)
+        assert np.all(dev <= bnd)
+        worst = max(worst, float(np.max(dev[:, i] / bnd[:, i])))
+    assert worst > 0.5
+    # a perturbation as large as the row itself: no finite bound
+    assert np.all(np.isinf(oracle.rmsnorm_bound(v, w, 2 * np.abs(v))))
 
 
 def test_router_normalization_is_scale_invariant():
@@ -82,3 +96,80 @@ def test_block_output_is_residual_plus_unit_rms_update():
     out = oracle.moe_block_ref(blk, blk.residual)
     c = out - blk.residual
     assert np.allclose(np.sqrt(np.mean(c * c, axis=1)), 1.0, atol=1e-4)
+
+
+@pytest.mark.parametrize("T,D,E,F,Fd,k", [(3, 128, 8, 64, 64, 2), (2, 256, 6, 64, 128, 3)])
+def test_block_bound_dominates_contract_limit_errors(T, D, E, F, Fd, k):
+    blk = synth.moe_block(60 + D, T=T, D=D, E=E, F=F, F_dense=Fd, k=k)
+    rng = np.random.default_rng(D)
+    worst = 0.0
+    for target in (None, None, 3, 17, D - 1):
+        out, ref, parts = perturbed_block(blk, rng, target=target)
+        bnd = oracle.moe_block_bound(blk, blk.residual, parts)
+        assert np.all(np.isfinite(bnd))
+        dev = np.abs(out - ref)
+        assert np.all(dev <= bnd), f"dev/bound {np.max(dev / bnd):.3f}"
+        worst = max(worst, float(np.max(dev / bnd)))
+    assert worst >= 1 / 20, f"bound {1 / worst:.1f}x the largest deviation"
+
+
+def test_block_bound_fails_without_the_h_error_term(monkeypatch):
+    blk = synth.moe_block(64, T=3, D=128, E=8, F=64, F_dense=64, k=2)
+    rng = np.random.default_rng(5)
+    out, ref, parts = perturbed_block(blk, rng, target=7)
+    full = oracle.moe_block_bound(blk, blk.residual, parts)
+
+    def h_error_rounding_only(g, u, rg, ru, act_rel):
+        return (act_rel + oracle.moe.F16_REL) * np.abs(oracle.gelu_tanh(g) * u) + oracle.moe.F16_ABS
+
+    monkeypatch.setattr(oracle.moe, "_h_error", h_error_rounding_only)
+    cut = oracle.moe_block_bound(blk, blk.residual, parts)
+    assert np.all(cut < full)
+    assert np.any(np.abs(out - ref) > cut)
+
+
+def test_block_at_a_given_routing():
+    # evaluated at its own routing the block is unchanged; at another one the
+    # expert branch follows that routing and the dense branch does not move
+    blk = synth.moe_block(65, T=3, D=128, E=8, F=64, F_dense=64, k=2)
+    out, parts = oracle.moe_block_ref(blk, blk.residual, want_parts=True)
+    same, p2 = oracle.moe_block_ref(blk, blk.residual, want_parts=True, routing=(parts["idx"], parts["w"]))
+    assert np.array_equal(out, same)
+    idx = parts["idx"][:, ::-1].copy()
+    w = parts["w"][:, ::-1].copy() * 0.5
+    _, p3 = oracle.moe_block_ref(blk, blk.residual, want_parts=True, routing=(idx, w))
+    assert np.array_equal(p3["b1"], parts["b1"]) and np.array_equal(p3["idx"], idx)
+    assert np.allclose(p3["b2"], 0.5 * parts["b2"], rtol=1e-12, atol=1e-15)
+
+
+def test_router_score_bound_dominates_f16_inputs_and_fp32_sums():
+    # the device's scores come from the f16 h2 and fp32 accumulation: z from
+    # h2 rounded to f16 (and its neighbours one f16 step away), with fp32
+    # products summed in fp32 four at a time, must lie within route_normed_bound
+    blk = synth.moe_block(66, T=4, D=512, E=16, F=64, F_dense=64, k=4)
+    res = np.asarray(blk.residual, np.float64)
+    h2 = oracle.rmsnorm(res, blk.pre_ffw_norm_2)
+    z, _, _ = oracle.route_normed(h2, blk.w_router, blk.router_scale, blk.down_scale, 4)
+    zb = oracle.route_normed_bound(blk, h2)
+    wr32 = np.asarray(blk.w_router, np.float32)
+    rng = np.random.default_rng(2)
+    for trial in range(3):
+        h16 = h2.astype(np.float16)
+        if trial:
+            up = np.nextafter(h16, np.float16(np.inf) * np.sign(rng.standard_normal(h16.shape)).astype(np.float16))
+            h16 = np.where(rng.uniform(size=h16.shape) < 0.5, up, h16)
+        acc = np.zeros((4, 16), np.float32)
+        for d0 in range(0, 512, 4):
+            acc = (acc + (h16[:, d0:d0 + 4].astype(np.float32) @ wr32[d0:d0 + 4])).astype(np.float32)
+        zd = oracle.rmsnorm(acc.astype(np.float64), blk.router_scale)
+        assert np.all(np.abs(zd - z) <= zb)
+
+
+def test_a16_block_within_the_rounding_only_bound():
+    # rounding h1, h2 and h to f16 at a fixed routing moves the block by at
+    # most the bound with no GEMM error (gemm_rel = 0) and exact norms
+    blk = synth.moe_block(67, T=3, D=128, E=8, F=64, F_dense=64, k=2)
+    out, parts = oracle.moe_block_ref(blk, blk.residual, want_parts=True)
+    o16 = oracle.moe_block_ref(blk, blk.residual, routing=(parts["idx"], parts["w"]), a16_inputs=True)
+    bnd = oracle.moe_block_bound(blk, blk.residual, parts, gemm_rel=0.0, f32_rel=0.0)
+    assert np.all(np.isfinite(bnd)) and np.all(np.abs(o16 - out) <= bnd) and np.max(np.abs(o16 - out)) > 0

@@ -11,6 +11,7 @@ import torch.nn.functional as F
 import oracle
 import synth
 from conftest import read_golden
+from perturb import perturbed_layer as _perturbed_layer
 
 E2 = torch.tensor([float(v) for _, v in read_golden("e2m1_table.txt")], dtype=torch.float64)
 E4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
@@ -142,9 +143,90 @@ def test_moe_single_expert_is_dense_gated_ffn():
     assert np.max(np.abs(y - ref)) < 1e-13
 
 
-def test_moe_bound_positive_and_linear_in_rel():
+# ---------------------------------------------------------------- composed bound
+
+def test_gelu_second_derivative_is_bounded_by_its_value_at_zero():
+    # the curvature constant of the bound: sup |gelu''| = sqrt(2/pi), at u = 0
+    u = np.linspace(-40.0, 40.0, 800001)
+    h = 1e-4
+    d2 = (oracle.gelu_tanh_deriv(u + h) - oracle.gelu_tanh_deriv(u - h)) / (2 * h)
+    assert np.max(np.abs(d2)) <= oracle.moe.GELU_D2_MAX * (1 + 1e-6)
+    assert abs(d2[400000] - math.sqrt(2 / math.pi)) < 1e-6
+
+
+def _check_layer_bound(moe, idx, w, rng):
+    """every perturbation at the contract's limit stays within moe_abs_bound,
+    and an aligned one reaches it; returns the worst deviation / bound"""
+    y = oracle.moe_ref(moe, idx, w)
+    bnd = oracle.moe_abs_bound(moe, idx, w)
+    worst = 0.0
+    for _ in range(3):
+        dev = np.abs(_perturbed_layer(moe, idx, w, rng) - y)
+        assert np.all(dev <= bnd), f"random signs: dev/bound {np.max(dev / bnd):.4f}"
+        worst = max(worst, float(np.max(dev / bnd)))
+    for t_n in range(3):
+        n = int(rng.integers(moe.x.shape[1]))
+        dev = np.abs(_perturbed_layer(moe, idx, w, rng, target=n) - y)
+        assert np.all(dev <= bnd), f"aligned at {n}: dev/bound {np.max(dev / bnd):.4f}"
+        # the aligned element of the token whose experts were aligned for it
+        ratio = dev[:, n] / bnd[:, n]
+        worst = max(worst, float(ratio.max()))
+        assert ratio.min() >= 0.9, f"aligned error reaches only {ratio.min():.3f} of the bound"
+    return worst
+
+
+@pytest.mark.parametrize("T,D,E,F,k,shared", [(3, 64, 4, 32, 2, True), (2, 256, 6, 128, 3, False),
+                                               (2, 704, 8, 64, 2, True)])
+def test_moe_bound_dominates_contract_limit_errors_and_is_reached(T, D, E, F, k, shared):
+    moe = _tiny_moe(seed=30 + D, T=T, D=D, E=E, F=F, k=k, shared=shared)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    worst = _check_layer_bound(moe, idx, w, np.random.default_rng(D))
+    assert worst >= 1 / 20  # not vacuous: a permitted error pattern comes close to it
+
+
+def test_moe_bound_fails_without_the_h_error_term(monkeypatch):
+    # a planted mistake: the bound without the gate/up errors propagated into
+    # h (only h's own rounding kept) must be exceeded by the aligned pattern
+    moe = _tiny_moe(seed=44, T=2, D=256, E=4, F=64, k=2, shared=True)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    full = oracle.moe.moe_abs_bound(moe, idx, w)
+
+    def h_error_rounding_only(g, u, rg, ru, act_rel):
+        h = np.abs(oracle.gelu_tanh(g) * u)
+        return (act_rel + oracle.moe.F16_REL) * h + oracle.moe.F16_ABS
+
+    monkeypatch.setattr(oracle.moe, "_h_error", h_error_rounding_only)
+    assert np.all(oracle.moe.moe_abs_bound(moe, idx, w) < full)
+    with pytest.raises(AssertionError):
+        _check_layer_bound(moe, idx, w, np.random.default_rng(1))
+
+
+def test_moe_bound_grows_with_the_gemm_criterion():
     moe = _tiny_moe()
     _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
-    b1 = oracle.moe_abs_bound(moe, idx, w, 1e-3, 0)
-    b2 = oracle.moe_abs_bound(moe, idx, w, 2e-3, 0)
-    assert np.all(b1 > 0) and np.allclose(b2, 2 * b1)
+    b1 = oracle.moe_abs_bound(moe, idx, w, 1e-3)
+    b2 = oracle.moe_abs_bound(moe, idx, w, 2e-3)
+    assert np.all(b1 > 0) and np.all(b2 > 1.9 * b1 - oracle.moe.F16_ABS * 1e3)
+
+
+def test_a16_is_round_to_nearest_even_f16():
+    # the 16-bit activation of W4A16: torch's fp16 conversion (RNE) on normal,
+    # subnormal, tie and overflowing values
+    v = np.concatenate([np.random.default_rng(4).standard_normal(10000) * 3,
+                        [1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -24 * 1.5, 2.0 ** -25, 65504.0, 65520.0, -0.0]])
+    got = oracle.a16(v)
+    ref = torch.from_numpy(v).to(torch.float16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref, equal_nan=True)
+    assert got[-7] == 1.0 and got[-6] == 1 + 2.0 ** -9 and np.isinf(got[-2])
+
+
+def test_a16_h_moves_the_layer_within_its_rounding_bound():
+    # the layer with h as an f16 activation differs from the exact one by at
+    # most the bound's share for h's rounding (no GEMM error, no fp32 error)
+    moe = _tiny_moe(seed=12, T=3, D=256, E=6, F=128, k=2)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    d = np.abs(oracle.moe_ref(moe, idx, w, a16_h=True) - oracle.moe_ref(moe, idx, w))
+    b = oracle.moe_abs_bound(moe, idx, w, gemm_rel=0.0, act_rel=0.0)
+    assert np.all(d <= b) and np.max(d) > 0
+    yg, _ = oracle.moe_ref_grouped(moe, idx, w, a16_h=True)
+    assert np.max(np.abs(yg - oracle.moe_ref(moe, idx, w, a16_h=True))) < 1e-13
