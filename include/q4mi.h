@@ -271,6 +271,22 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* moe_grouped_qgemm without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, with
+ * their scratch (h, the per-pair outputs, the expert grouping) in an 8 MiB
+ * array that the library keeps on each GPU it runs on until the process
+ * ends.  The call allocates nothing; the caller passes the inputs and y as
+ * for moe_grouped_qgemm.  All calls on one GPU share that GPU's array, so
+ * calls that overlap in time on one GPU (other streams, other threads)
+ * race; calls ordered on one stream do not.  The array needs no clearing:
+ * every call writes all the scratch it reads.
+ * Errors: those of moe_grouped_qgemm (no WORKSPACE), and UNSUPPORTED when
+ * moe_workspace_bytes(w, T, k) exceeds 8 MiB (T = 16, k = 16 fit up to
+ * D = F = 4096). */
+int moe_grouped_qgemm_noalloc(const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
+                              const float* topk_w, int T, int k, void* y, int out_dtype, void* stream);
+
 /* MLX-style affine weights at 2, 3, 5, 6 or 8 bits [README "Everything it
  * has": the MLX affine widths, groups of 64; the 4-bit width has the entry
  * points above].  w = q * scale + bias per 64-value group.

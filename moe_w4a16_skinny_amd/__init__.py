@@ -63,6 +63,7 @@ _SIGS = {
     "moe_route_topk": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_workspace_bytes": (_sz, [C.POINTER(q4_moe_desc), _i32, _i32]),
     "moe_grouped_qgemm": (_i32, [C.POINTER(q4_moe_desc), _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "moe_grouped_qgemm_noalloc": (_i32, [C.POINTER(q4_moe_desc), _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp]),
     "q4_affine_bits_packed_bytes": (_sz, [_i64, _i64, _i32]),
     "q4_affine_bits_repack": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz]),
     "q4_affine_bits_unpack": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
@@ -348,6 +349,17 @@ def moe_grouped_qgemm(weights: MoeWeights, x, topk_idx, topk_w, out=None, out_dt
     ws = workspace(wsb, x.device)
     _check(_lib.moe_grouped_qgemm(C.byref(d), _tptr(x), _tptr(topk_idx), _tptr(topk_w), T, k, _tptr(out),
                                   _dtype_code(out.dtype), _tptr(ws), wsb, _stream()))
+    return out
+
+
+def moe_grouped_qgemm_noalloc(weights: MoeWeights, x, topk_idx, topk_w, out):
+    """moe_grouped_qgemm with the library's per-device scratch array instead of
+    a workspace (no allocation in the call; `out` must be given)."""
+    T, D = x.shape
+    k = topk_idx.shape[1]
+    d = weights.desc()
+    _check(_lib.moe_grouped_qgemm_noalloc(C.byref(d), _tptr(x), _tptr(topk_idx), _tptr(topk_w), T, k, _tptr(out),
+                                          _dtype_code(out.dtype), _stream()))
     return out
 
 

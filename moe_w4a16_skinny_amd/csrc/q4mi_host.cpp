@@ -550,10 +550,10 @@ size_t moe_workspace_bytes(const q4_moe_desc* w, int T, int k) {
 
 }  // extern "C"
 
-// Every condition moe_grouped_qgemm refuses, checked without enqueueing anything.
-static int moe_check(const char* fn, const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
-                     const float* topk_w, int T, int k, const void* y, int out_dtype, const void* ws,
-                     size_t ws_bytes) {
+// Every condition moe_grouped_qgemm refuses except those on its workspace,
+// checked without enqueueing anything.
+static int moe_check_shape(const char* fn, const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
+                           const float* topk_w, int T, int k, const void* y, int out_dtype) {
   if (!w) return fail(Q4_ERR_INVALID_ARG, "%s: w is NULL", fn);
   if (!x || !topk_idx || !topk_w || !y)
     return fail(Q4_ERR_INVALID_ARG, "%s: x, topk_idx, topk_w and y must not be NULL", fn);
@@ -572,6 +572,14 @@ static int moe_check(const char* fn, const q4_moe_desc* w, const void* x, const 
   if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(y) || !aligned16(w->gate_packed) ||
       !aligned16(w->up_packed) || !aligned16(w->down_packed))
     return fail(Q4_ERR_ALIGNMENT, "%s: x, topk_idx, topk_w, y and the packed weights must be 16-byte aligned", fn);
+  return Q4_OK;
+}
+
+// ... and with them
+static int moe_check(const char* fn, const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
+                     const float* topk_w, int T, int k, const void* y, int out_dtype, const void* ws,
+                     size_t ws_bytes) {
+  if (int rc = moe_check_shape(fn, w, x, topk_idx, topk_w, T, k, y, out_dtype)) return rc;
   if (!ws) return fail(Q4_ERR_WORKSPACE, "%s: ws is NULL", fn);
   if (!aligned16(ws)) return fail(Q4_ERR_ALIGNMENT, "%s: ws is not 16-byte aligned", fn);
   size_t h_off, o_off, r_off, g_off;
@@ -620,6 +628,21 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
                       int k, void* y, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
   if (int rc = moe_check(__func__, w, x, topk_idx, topk_w, T, k, y, out_dtype, ws, ws_bytes)) return rc;
   if (int rc = moe_enqueue(__func__, w, x, topk_idx, topk_w, T, k, y, out_dtype, ws, stream)) return rc;
+  return ok();
+}
+
+int moe_grouped_qgemm_noalloc(const q4_moe_desc* w, const void* x, const int32_t* topk_idx, const float* topk_w,
+                              int T, int k, void* y, int out_dtype, void* stream) {
+  if (int rc = moe_check_shape(__func__, w, x, topk_idx, topk_w, T, k, y, out_dtype)) return rc;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (int e = moe_noalloc_scratch(&scratch, &scratch_bytes))
+    return fail(Q4_ERR_HIP, "%s: the scratch array's device address is not available (hip error %d)", __func__, e);
+  const size_t need = moe_workspace_bytes(w, T, k);
+  if (need > scratch_bytes)
+    return fail(Q4_ERR_UNSUPPORTED, "%s: this shape needs %zu bytes of scratch, more than the %zu of the "
+                "library's per-device array (use moe_grouped_qgemm with a workspace)", __func__, need, scratch_bytes);
+  if (int rc = moe_enqueue(__func__, w, x, topk_idx, topk_w, T, k, y, out_dtype, scratch, stream)) return rc;
   return ok();
 }
 

@@ -184,5 +184,10 @@ inline size_t moe_grp_words(int E, int T, int k) {
   return 4 + 3 * (static_cast<size_t>(E) + 1) + static_cast<size_t>(T) * (k + 1);
 }
 int launch_moe(const MoeArgs& m, void* stream);
+// The per-device scratch array of moe_grouped_qgemm_noalloc (q4mi_moe.hip):
+// its device address on the current device (looked up once per device) and
+// its size.  Returns hipError_t as int.
+constexpr int kMaxDevices = 64;
+int moe_noalloc_scratch(void** ptr, size_t* bytes);
 
 }  // namespace q4mi

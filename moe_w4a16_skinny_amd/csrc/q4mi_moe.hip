@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "q4mi_tiles.h"
 
@@ -755,7 +756,34 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
     static_cast<_Float16*>(m.y)[static_cast<size_t>(t) * m.D + n] = (_Float16)acc;
 }
 
+// Scratch of moe_grouped_qgemm_noalloc: one array per device, in the code
+// object, so that the entry point needs no allocation.  Host code never uses
+// its name as an address (on the host it is only a stand-in): the device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kMoeScratchBytes = size_t(8) << 20;
+__device__ __align__(256) unsigned char scratch[kMoeScratchBytes];
+
 }  // namespace
+
+int moe_noalloc_scratch(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) {
+      (void)hipGetLastError();
+      return static_cast<int>(e);
+    }
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kMoeScratchBytes;
+  return 0;
+}
 
 int launch_route(const RouteArgs& r, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
