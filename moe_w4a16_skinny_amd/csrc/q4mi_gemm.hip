@@ -212,7 +212,6 @@ __global__ __launch_bounds__(64 * W) void qgemm_kernel(GemmParams kp) {
       panel = panel < kp.npanels ? panel : kp.npanels - 1;  // in-bounds load, result dropped
       gp.panel[p] = g.w + static_cast<size_t>(panel) * static_cast<size_t>(g.panel_bytes);
     }
-    gp.arow = nullptr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) gp.ar[j] = ar[j];
   };

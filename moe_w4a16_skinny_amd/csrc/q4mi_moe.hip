@@ -590,7 +590,11 @@ __device__ __forceinline__ int items_of_wave(int nitems, int gw, int NW) {
 // Item (active expert a, panel pair j): gate panel j and up panel j of the
 // expert streamed together over K = D (P = 2), h = gelu_tanh(g_gate acc_g) *
 // (g_up acc_u) for the expert's rows, written as f16 to the scratch row.
-template <int W, int DP>
+// AM = kAStagedRows: the workgroup first stages all of x [T][D] in LDS
+// (with its first weight loads in flight), and each item's tokens are read
+// from there, so the stream issues only weight loads; AM = kAGlobal (when x
+// does not fit beside the stash): lanes load their token's activations.
+template <int W, int DP, int AM>
 __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW) {
   __shared__ MoeGroups G;
   build_groups(m, G);
@@ -611,6 +615,9 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   const bool half = has_half_tile(m.D);
 
   const DivBy by_npp(static_cast<unsigned>(npp));
+  const __amdgpu_buffer_rsrc_t xr = act_rsrc(m.x, static_cast<unsigned>(m.T) * static_cast<unsigned>(m.D) * 2u);
+  const int ntx = nfull + (half ? 1 : 0);
+  const unsigned xrs = static_cast<unsigned>(stage_row_stride(ntx));  // staged row stride (bytes)
   auto item = [&](int gi, int& e, int& jp) {
     int it = gw + (c0 + gi) * NW;
     it = it < nitems ? it : nitems - 1;  // past the wave's items: in-bounds, never computed
@@ -625,17 +632,34 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
     gp.panel[0] = m.gate + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jp) * m.gate_panel_bytes;
     gp.panel[1] = m.up + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jp) * m.gate_panel_bytes;
     const int me = min(G.cnt[e], 16);
-    gp.arow = m.x + static_cast<size_t>(G.tok[G.base[e] + min(c, me - 1)]) * m.D;
+    if constexpr (AM == kAStagedRows) {
+      gp.alds = static_cast<unsigned>(G.tok[G.base[e] + min(c, me - 1)]) * xrs;
+    } else {
+      gp.arsrc = xr;
+      gp.aoff = c < me ? static_cast<unsigned>(G.tok[G.base[e] + c]) * static_cast<unsigned>(m.D) * 2u : kDeadLane;
+    }
   };
-  extern __shared__ f32x4 gu_out[];  // [W][NGW][2 panels][64 lanes]
-  f32x4* wout = gu_out + static_cast<size_t>(w) * NGW * 2 * 64;
-  auto pre = [] {};
+  // dynamic LDS: [staged x (kAStagedRows)] then the stash [W][NGW][2 panels][64 lanes]
+  extern __shared__ f32x4 gu_dyn[];
+  char* const dyn = reinterpret_cast<char*>(gu_dyn);
+  const size_t xbytes = AM == kAStagedRows ? (static_cast<size_t>(stage_bytes(m.T, ntx)) + 15) / 16 * 16 : 0;
+  f32x4* wout = reinterpret_cast<f32x4*>(dyn + xbytes) + static_cast<size_t>(w) * NGW * 2 * 64;
+  const ALds al{dyn + 16 * o};
+  const StageGeom sg = stage_geom(m.x, m.T, m.D, 0, ntx);
+  // the first chunk's stream stages x (every wave enters it, possibly with no
+  // item, so all reach the staging barrier); it is a separate instance so
+  // that the staging and its wait are unconditional and the compiler's
+  // waits in the later streams know the staging has landed
+  auto stage_pre_issue = [&] {
+    if constexpr (AM == kAStagedRows) stage_issue(sg, reinterpret_cast<u32x4*>(gu_dyn));
+  };
+  auto stage_pre = [&] {
+    if constexpr (AM == kAStagedRows) stage_wait<DP * 2 * 2>();  // the prologue's D tiles of 2 panels: codes + scales
+  };
+  auto none = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[2][2]) { stash<2>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[2][2]) { stash_add<2>(wout, gi, acc); };
-  for (; c0 < ntot; c0 += NGW) {
-    ng = min(NGW, ntot - c0);
-    stream_groups<kNvfp4, 2, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.D,
-                                          group, pre, pre, epi, epi_add);
+  auto finish = [&]() {
     for (int gi = 0; gi < ng; ++gi) {
       int e, jp;
       item(gi, e, jp);
@@ -651,6 +675,18 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
         }
       }
     }
+    c0 += NGW;
+  };
+  if (nitems == 0) return;  // no item at all: nothing to stage or compute
+  ng = min(NGW, ntot);
+  stream_groups<kNvfp4, 2, DP, AM>(ng, ntx, 0, half ? nfull : -1, al, ARing{}, m.D, group, stage_pre_issue, stage_pre,
+                                   epi, epi_add);
+  finish();
+  while (c0 < ntot) {
+    ng = min(NGW, ntot - c0);
+    stream_groups<kNvfp4, 2, DP, AM>(ng, ntx, 0, half ? nfull : -1, al, ARing{}, m.D, group, none, none, epi,
+                                     epi_add);
+    finish();
   }
 }
 
@@ -676,6 +712,8 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   const bool half = has_half_tile(m.F);
 
   const DivBy by_ngp(static_cast<unsigned>(ngp));
+  const unsigned nrows_h = static_cast<unsigned>(m.T * m.k + (m.has_shared ? m.T : 0));
+  const __amdgpu_buffer_rsrc_t hr = act_rsrc(m.h, nrows_h * static_cast<unsigned>(m.F) * 2u);
   auto item = [&](int gi, int& e, int& q) {
     int it = gw + (c0 + gi) * NW;
     it = it < nitems ? it : nitems - 1;
@@ -693,7 +731,8 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
       gp.panel[p] = m.down + static_cast<size_t>(e) * m.down_stride + static_cast<size_t>(pi) * m.down_panel_bytes;
     }
     const int me = min(G.cnt[e], 16);
-    gp.arow = m.h + static_cast<size_t>(G.base[e] + min(c, me - 1)) * m.F;
+    gp.arsrc = hr;
+    gp.aoff = c < me ? static_cast<unsigned>(G.base[e] + c) * static_cast<unsigned>(m.F) * 2u : kDeadLane;
   };
   extern __shared__ f32x4 dn_out[];  // [W][NGW][P][64]
   f32x4* wout = dn_out + static_cast<size_t>(w) * NGW * P * 64;
@@ -804,16 +843,35 @@ int launch_moe(const MoeArgs& m, void* stream) {
   constexpr size_t kStashLds = 96 * 1024;
   const int npp = m.F / 16;
   const int gu_cap = static_cast<int>(kStashLds / (size_t(GU_W) * 2 * 64 * 16));
-  const int gu_ngw = std::min((nexp * npp + gu_nw - 1) / gu_nw, gu_cap);
-  const size_t gu_lds = static_cast<size_t>(GU_W) * gu_ngw * 2 * 64 * 16;
+  const int gu_need = (nexp * npp + gu_nw - 1) / gu_nw;  // stash slots a wave would use for all its items
+  int gu_ngw = std::min(gu_need, gu_cap);
+  size_t gu_lds = static_cast<size_t>(GU_W) * gu_ngw * 2 * 64 * 16;
+  // gate/up stages x in LDS when it fits beside the grouping table and a
+  // stash of at least one item per wave (a wave with more items than slots
+  // streams them in chunks)
+  const int ntx = static_cast<int>(full_tiles(m.D) + (has_half_tile(m.D) ? 1 : 0));
+  const size_t xbytes = (static_cast<size_t>(stage_bytes(m.T, ntx)) + 15) / 16 * 16;
+  const size_t lds_total = 160 * 1024;
+  const size_t slot = static_cast<size_t>(GU_W) * 2 * 64 * 16;
+  const size_t room = lds_total > sizeof(MoeGroups) + xbytes ? lds_total - sizeof(MoeGroups) - xbytes : 0;
+  const bool gu_staged = room >= slot;
+  if (gu_staged) {
+    gu_ngw = std::min(gu_need, static_cast<int>(room / slot));
+    gu_lds = xbytes + static_cast<size_t>(gu_ngw) * slot;
+  }
   const int ngp = (m.D / 16 + DN_P - 1) / DN_P;
   const int dn_cap = static_cast<int>(kStashLds / (size_t(DN_W) * DN_P * 64 * 16));
   const int dn_ngw = std::min((nexp * ngp + dn_nw - 1) / dn_nw, dn_cap);
   const size_t dn_lds = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
   if (gu_ngw < 1 || dn_ngw < 1) return static_cast<int>(hipErrorInvalidConfiguration);
-  if (int e = ensure_dynamic_lds(reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4>), gu_lds)) return e;
+  const void* gu_fn = gu_staged ? reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4, kAStagedRows>)
+                                : reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4, kAGlobal>);
+  if (int e = ensure_dynamic_lds(gu_fn, gu_lds)) return e;
   if (int e = ensure_dynamic_lds(reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4>), dn_lds)) return e;
-  hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m, gu_ngw);
+  if (gu_staged)
+    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAStagedRows>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m, gu_ngw);
+  else
+    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAGlobal>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m, gu_ngw);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
   hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);

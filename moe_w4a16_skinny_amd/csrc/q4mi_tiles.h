@@ -211,13 +211,19 @@ __device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4
 //    tile's own loads.
 //  * kAGlobal: lane (c, o) loads a[row c][k0 .. k0 + 8) straight into
 //    registers from its row pointer.
-enum AMode { kAStaged = 0, kARing = 1, kAGlobal = 2 };
+//  * kAStagedRows: the workgroup staged whole rows of an activation matrix
+//    in LDS (all its k-range, row stride stage_row_stride); each group names
+//    the staged row every lane reads (GroupPtrs::alds), which is recorded with
+//    the tile's loads, so the activations cost no memory instruction in the
+//    stream.
+enum AMode { kAStaged = 0, kARing = 1, kAGlobal = 2, kAStagedRows = 3 };
 
 template <int FMT, int P, int AM>
 struct StreamStage {
   u32x4 c[P];
   typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type s[P];
   u32x4 a[AM == kAGlobal ? 4 : 1];
+  unsigned arow;  // kAStagedRows: LDS byte offset of this lane's staged row for this tile
 };
 
 // Ring slots of kARing: slot d holds one tile of 16 rows x 128 k (f16/bf16)
@@ -361,14 +367,30 @@ __device__ __forceinline__ void stage_wait() {
 // Where group g's data lives: the packed base of each of its P panels and,
 // for the activations (valid rows for every lane: rows past the real ones
 // only feed output rows that are never stored)
-//  * kAGlobal: arow, this lane's row (c = lane & 15);
+//  * kAGlobal: arsrc and aoff, this lane's row (c = lane & 15);
 //  * kARing: ar[j], the row this lane moves for row group j plus
 //    ring_chunk(j).
+// kAGlobal: the activations are read through a buffer resource over the
+// whole activation matrix; a lane whose row holds no token gets an offset
+// past the resource's end, so its loads return zeros without touching
+// memory, and every load stays one unconditional instruction (the
+// compiler's wait counting stays exact).
+constexpr unsigned kDeadLane = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 act_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
 template <int P>
 struct GroupPtrs {
   const uint8_t* panel[P];
-  const uint16_t* arow;
   const uint16_t* ar[4];
+  __amdgpu_buffer_rsrc_t arsrc;  // kAGlobal: the activation matrix
+  unsigned aoff;                 // kAGlobal: byte offset of this lane's row, or kDeadLane
+  unsigned alds;                 // kAStagedRows: LDS byte offset of this lane's staged row
 };
 
 // Stream ng groups of P panels over the tiles [kt0, kt0 + KRg) of each group
@@ -390,6 +412,7 @@ template <int FMT, int P, int D, int AM, class Group, class PreIssue, class Pre,
 __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, ALds al, ARing ring, int K,
                                               Group group, PreIssue pre_issue, Pre pre, Epi epi, EpiAdd epi_add) {
   constexpr bool ALDS = AM == kAStaged;
+  constexpr bool STAGED = AM == kAStaged || AM == kAStagedRows;  // activations complete in LDS before the math
   const int lane = threadIdx.x & 63;
   const int o = lane >> 4;
   const int c = lane & 15;
@@ -406,9 +429,11 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   // tile's first weight load also covers its activations.
   auto load_a = [&](St& st, const GroupPtrs<P>& gp, int tg, int d) {
     if constexpr (AM == kAGlobal) {
-      const int kb = tg * kTileK;
+      const unsigned kb = static_cast<unsigned>(tg * kTileK + 8 * o) * 2u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(gp.arow + kb + 32 * i + 8 * o);
+      for (int i = 0; i < 4; ++i) st.a[i] = act_load16(gp.arsrc, gp.aoff + kb + 64u * i);
+    } else if constexpr (AM == kAStagedRows) {
+      st.arow = gp.alds;
     } else if constexpr (AM == kARing) {
       const int kb = tg * kTileK;
 #pragma unroll
@@ -423,9 +448,10 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k0 = kb + 32 * i + 8 * o;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(gp.arow + (k0 < K ? k0 : 0));
-        st.a[i] = k0 < K ? v : u32x4{0u, 0u, 0u, 0u};
+        st.a[i] = act_load16(gp.arsrc, k0 < K ? gp.aoff + static_cast<unsigned>(k0) * 2u : kDeadLane);
       }
+    } else if constexpr (AM == kAStagedRows) {
+      st.arow = gp.alds;  // the staged k-padding is zero
     } else if constexpr (AM == kARing) {
       const int kb = half_t * kTileK;
 #pragma unroll
@@ -491,6 +517,10 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
       const char* pa = al.base + t * 256;
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(pa + i * 64);
+    } else if constexpr (AM == kAStagedRows) {
+      const char* pa = al.base + x.arow + t * 256;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(pa + i * 64);
     } else if constexpr (AM == kARing) {
       unsigned off = static_cast<unsigned>(d * kRingSlot);
       asm volatile("" : "+v"(off) : "v"(x.c[0].x));
@@ -527,7 +557,7 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   // read past the end of rows shorter than a tile.  pre() must then not rely
   // on the prologue's loads (it does not in these modes).
   pre_issue();
-  if (ALDS || KRf > 0) {
+  if (STAGED || KRf > 0) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       load_next(st[d], d);
