@@ -29,6 +29,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "q4mi_tiles.h"
 
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
 // activation rows are the expert's contiguous h rows; o[row][n] = w_pair *
 // g_down * acc in fp32.
 template <int P, int W, int DP>
-__global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
+__global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, int stage_room) {
   __shared__ MoeDownTable G;
   fetch_groups(m, G);
   const int lane = threadIdx.x & 63;
@@ -705,45 +706,42 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
   const int npan = m.D / 16;
   const int ngp = (npan + P - 1) / P;  // panel groups per expert
   const int nitems = G.nact * ngp;
-  const int gw = blockIdx.x + gridDim.x * w, NW = gridDim.x * W;
-  const int ntot = items_of_wave(nitems, gw, NW);  // in chunks of at most NGW, as in gate/up
+  // the workgroup's items: a contiguous range (one or two experts' panel
+  // groups), dealt round-robin to its waves
+  const int i0 = static_cast<int>((static_cast<long long>(blockIdx.x) * nitems) / gridDim.x);
+  const int i1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * nitems) / gridDim.x);
+  if (i1 <= i0) return;  // no item for this workgroup (uniform)
+  const int ntot = i1 - i0 > w ? (i1 - i0 - w + W - 1) / W : 0;  // in chunks of at most NGW, as in gate/up
   int c0 = 0, ng = 0;
   const int nfull = static_cast<int>(full_tiles(m.F));
   const bool half = has_half_tile(m.F);
+  const int ntf = nfull + (half ? 1 : 0);
 
   const DivBy by_ngp(static_cast<unsigned>(ngp));
   const unsigned nrows_h = static_cast<unsigned>(m.T * m.k + (m.has_shared ? m.T : 0));
   const __amdgpu_buffer_rsrc_t hr = act_rsrc(m.h, nrows_h * static_cast<unsigned>(m.F) * 2u);
   auto item = [&](int gi, int& e, int& q) {
-    int it = gw + (c0 + gi) * NW;
-    it = it < nitems ? it : nitems - 1;
+    int it = i0 + w + (c0 + gi) * W;
+    it = it < i1 ? it : i1 - 1;  // past the wave's items: in-bounds, never computed
     const int a = by_ngp(it);
     q = it - a * ngp;
     e = G.act[a];
   };
-  auto group = [&](int gi, GroupPtrs<P>& gp) {
-    prio_by_items_left(ntot - c0 - gi);
-    int e, q;
-    item(gi, e, q);
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int pi = min(q * P + p, npan - 1);
-      gp.panel[p] = m.down + static_cast<size_t>(e) * m.down_stride + static_cast<size_t>(pi) * m.down_panel_bytes;
-    }
-    const int me = min(G.cnt[e], 16);
-    gp.arsrc = hr;
-    gp.aoff = c < me ? static_cast<unsigned>(G.base[e] + c) * static_cast<unsigned>(m.F) * 2u : kDeadLane;
-  };
-  extern __shared__ f32x4 dn_out[];  // [W][NGW][P][64]
-  f32x4* wout = dn_out + static_cast<size_t>(w) * NGW * P * 64;
-  auto pre = [] {};
+  // the h rows of the experts the range spans are contiguous: stage them in
+  // LDS if they fit, so the stream issues only weight loads
+  const int e_lo = G.act[by_ngp(i0)], e_hi = G.act[by_ngp(i1 - 1)];
+  const int rlo = G.base[e_lo], rhi = G.base[e_hi] + G.cnt[e_hi];
+  const unsigned hrs = static_cast<unsigned>(stage_row_stride(ntf));
+  const bool staged = static_cast<long long>(stage_bytes(rhi - rlo, ntf)) <= stage_room;
+  extern __shared__ f32x4 dn_dyn[];  // [W][NGW][P][64] stash, then the staged rows
+  f32x4* wout = dn_dyn + static_cast<size_t>(w) * NGW * P * 64;
+  char* const stage = reinterpret_cast<char*>(dn_dyn + static_cast<size_t>(W) * NGW * P * 64);
+  const ALds al{stage + 16 * o};
+  const StageGeom sg = stage_geom(m.h + static_cast<size_t>(rlo) * m.F, rhi - rlo, m.F, 0, ntf);
   auto epi = [&](int gi, f32x4 (&acc)[P][2]) { stash<P>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
   const int nrow = m.T * m.k + m.T;
-  for (; c0 < ntot; c0 += NGW) {
-    ng = min(NGW, ntot - c0);
-    stream_groups<kNvfp4, P, DP, kAGlobal>(ng, nfull + (half ? 1 : 0), 0, half ? nfull : -1, ALds{}, ARing{}, m.F,
-                                          group, pre, pre, epi, epi_add);
+  auto finish = [&]() {
     for (int gi = 0; gi < ng; ++gi) {
       int e, q;
       item(gi, e, q);
@@ -763,7 +761,51 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW) {
         }
       }
     }
-  }
+    c0 += NGW;
+  };
+  // the two ways of reaching the activations; as in gate/up, the first
+  // chunk's stream (entered by every wave) stages the rows
+  auto run = [&](auto mode) {
+    constexpr int AM = decltype(mode)::value;
+    auto group = [&](int gi, GroupPtrs<P>& gp) {
+      prio_by_items_left(ntot - c0 - gi);
+      int e, q;
+      item(gi, e, q);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int pi = min(q * P + p, npan - 1);
+        gp.panel[p] = m.down + static_cast<size_t>(e) * m.down_stride + static_cast<size_t>(pi) * m.down_panel_bytes;
+      }
+      const int me = min(G.cnt[e], 16);
+      if constexpr (AM == kAStagedRows) {
+        gp.alds = static_cast<unsigned>(G.base[e] + min(c, me - 1) - rlo) * hrs;
+      } else {
+        gp.arsrc = hr;
+        gp.aoff = c < me ? static_cast<unsigned>(G.base[e] + c) * static_cast<unsigned>(m.F) * 2u : kDeadLane;
+      }
+    };
+    auto stage_pre_issue = [&] {
+      if constexpr (AM == kAStagedRows) stage_issue(sg, reinterpret_cast<u32x4*>(stage));
+    };
+    auto stage_pre = [&] {
+      if constexpr (AM == kAStagedRows) stage_wait<DP * P * 2>();  // the prologue's D tiles of P panels
+    };
+    auto none = [] {};
+    ng = min(NGW, ntot);
+    stream_groups<kNvfp4, P, DP, AM>(ng, ntf, 0, half ? nfull : -1, al, ARing{}, m.F, group, stage_pre_issue,
+                                     stage_pre, epi, epi_add);
+    finish();
+    while (c0 < ntot) {
+      ng = min(NGW, ntot - c0);
+      stream_groups<kNvfp4, P, DP, AM>(ng, ntf, 0, half ? nfull : -1, al, ARing{}, m.F, group, none, none, epi,
+                                       epi_add);
+      finish();
+    }
+  };
+  if (staged)
+    run(std::integral_constant<int, kAStagedRows>{});
+  else
+    run(std::integral_constant<int, kAGlobal>{});
 }
 
 // ------------------------------------------------------------------ combine
@@ -862,7 +904,12 @@ int launch_moe(const MoeArgs& m, void* stream) {
   const int ngp = (m.D / 16 + DN_P - 1) / DN_P;
   const int dn_cap = static_cast<int>(kStashLds / (size_t(DN_W) * DN_P * 64 * 16));
   const int dn_ngw = std::min((nexp * ngp + dn_nw - 1) / dn_nw, dn_cap);
-  const size_t dn_lds = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
+  // the rest of the CU's LDS holds a workgroup's staged h rows (a workgroup
+  // whose rows do not fit reads them from global memory)
+  const size_t dn_stash = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
+  const size_t dn_fixed = sizeof(MoeDownTable) + 512;  // the table and the kernel's other static LDS
+  const size_t dn_room = 160 * 1024 > dn_fixed + dn_stash ? 160 * 1024 - dn_fixed - dn_stash : 0;
+  const size_t dn_lds = dn_stash + dn_room;
   if (gu_ngw < 1 || dn_ngw < 1) return static_cast<int>(hipErrorInvalidConfiguration);
   const void* gu_fn = gu_staged ? reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4, kAStagedRows>)
                                 : reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4, kAGlobal>);
@@ -873,7 +920,8 @@ int launch_moe(const MoeArgs& m, void* stream) {
   else
     hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAGlobal>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m, gu_ngw);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
-  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw);
+  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw,
+                     static_cast<int>(dn_room));
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
   hipLaunchKernelGGL(moe_combine_kernel, dim3(m.T, (m.D + 255) / 256), dim3(256), 0, s, m);
   return static_cast<int>(hipGetLastError());

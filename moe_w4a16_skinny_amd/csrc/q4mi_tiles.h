@@ -477,8 +477,7 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
         st.s[p] = ld_nt8(tb + kTileCodeBytes + c * 8);
     }
   };
-  auto load_half = [&](St& st, const GroupPtrs<P>& gp, int d) {
-    load_a_half(st, gp, d);
+  auto load_half_w = [&](St& st, const GroupPtrs<P>& gp) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const uint8_t* tb = gp.panel[p] + static_cast<size_t>(half_t) * kTileBytes;
@@ -489,6 +488,10 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
       else
         st.s[p] = u32x2{ld_nt4(tb + kHalfCodeBytes + c * 4), 0u};  // 2nd group s = b = 0 adds 0
     }
+  };
+  auto load_half = [&](St& st, const GroupPtrs<P>& gp, int d) {
+    load_a_half(st, gp, d);
+    load_half_w(st, gp);
   };
 
   f32x4 acc[P][2];
@@ -556,6 +559,30 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   // or none), the prologue is skipped: its full-tile activation loads would
   // read past the end of rows shorter than a tile.  pre() must then not rely
   // on the prologue's loads (it does not in these modes).
+  // The half tiles' weights of the first D groups are loaded before anything
+  // else (not in the ring mode, whose half-tile activations move with its
+  // own slots): the data is there when the half-tile math comes after the
+  // stream, instead of one more memory round trip then.  Being older than
+  // every load of the stream, these loads leave the stream's waits exact.
+  const bool pre_half = has_half && AM != kARing;
+  struct HalfW {
+    u32x2 c[P];
+    typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type s[P];
+  } hpre[D];
+  if (pre_half) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      GroupPtrs<P> hp;
+      group(d, hp);
+      St tmp;
+      load_half_w(tmp, hp);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        hpre[d].c[p] = u32x2{tmp.c[p].x, tmp.c[p].y};
+        hpre[d].s[p] = tmp.s[p];
+      }
+    }
+  }
   pre_issue();
   if (STAGED || KRf > 0) {
 #pragma unroll
@@ -590,7 +617,8 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
     for (int gg = 0; gg < ng; ++gg) epi(gg, acc);
   }
 
-  // half tiles: loads of up to D groups in flight, then their math
+  // half tiles: loads of up to D groups in flight (the first D groups'
+  // weights are already in hpre), then their math
   if (has_half) {
     for (int g0 = 0; g0 < ng; g0 += D) {
 #pragma unroll
@@ -598,7 +626,16 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
         if (g0 + d < ng) {
           GroupPtrs<P> hp;
           group(g0 + d, hp);
-          load_half(st[d], hp, d);
+          if (pre_half && g0 == 0) {
+            load_a_half(st[d], hp, d);
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+              st[d].c[p] = u32x4{hpre[d].c[p].x, hpre[d].c[p].y, 0u, 0u};
+              st[d].s[p] = hpre[d].s[p];
+            }
+          } else {
+            load_half(st[d], hp, d);
+          }
         }
       }
 #pragma unroll
