@@ -335,8 +335,8 @@ class MoeBlockWork:
         per = lambda f: 2 * (f * D // 2 + f * D // 16 + 4) + (D * f // 2 + D * f // 16 + 4)
         self.alg_bytes = D * blk.E * 4 + per(Fd) + self.active * per(F) + 2 * T * D * 4
         self.kind = "moe_block"
-        self.kernel_names = ["block step: block_norm_in + route + block_router + 2 x (moe_gate_up + moe_down + "
-                             "moe_combine) + block_combine"]
+        self.kernel_names = ["block step: block_norm_in + route (logits) + block_router + 2 x (moe_gate_up + "
+                             "moe_down) + block_combine"]
         self.dtype = "f16"
 
     def step(self):
@@ -460,6 +460,9 @@ def stream_ceiling(nbytes, steps):
     shapes = [(mode, grid, depth) for mode in (0, 1) for depth in (2, 4, 8) for grid in (256, 512, 1024, 2048)]
     # and the grids in which every lane issues exactly one or two batches
     shapes += [(0, max(1, min(65536, -(-n16 // (256 * depth * nb)))), depth) for depth in (2, 4, 8) for nb in (1, 2)]
+    # one batch per lane, 512-thread workgroups (the GEMMs' shape), where a
+    # workgroup's chunk is at most 32 loads per lane
+    shapes += [(2, grid, 0) for grid in (256, 512, 768, 1024) if -(-n16 // grid) <= 512 * 32]
     for mode, grid, depth in shapes:
         def step(i):
             rc = lib.q4_stream_read(C.c_void_p(buf.data_ptr() + (i % copies) * stride), n, grid, mode, depth,
@@ -483,7 +486,7 @@ def stream_ceiling(nbytes, steps):
         if best is None or us < best["mean_launch_us"]:
             best = {"bytes": n, "mean_launch_us": round(us, 3), "GB/s": round(n / us / 1e3, 1),
                     "frac_of_peak": round(n / us / 1e3 / HBM_PEAK_GBS, 4), "grid": grid, "depth": depth,
-                    "mode": "grid-stride" if mode == 0 else "chunk per workgroup",
+                    "mode": ["grid-stride", "chunk per workgroup", "one batch per lane"][mode],
                     "kernel": "stream_read_kernel (q4_stream_read)"}
         del g
     del buf

@@ -354,10 +354,11 @@ size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k);
  *   ws           device workspace of ws_bytes >= moe_block_workspace_bytes;
  *                its first 32 KiB of counters start and end at zero, as for
  *                the other entry points
- * The block runs 10 launches on `stream`: the two input norms, the router
- * matmul (moe_route_topk's kernel), the router normalization and top-k, the
- * dense branch and the experts (moe_grouped_qgemm's kernels, sharing the
- * workspace), and the combine.
+ * The block runs 8 launches on `stream`: the two input norms, the router
+ * matmul (moe_route_topk's kernel, logits only), the router normalization
+ * and top-k, the dense branch and the experts (moe_grouped_qgemm's gate/up
+ * and down kernels, each layer in its own part of the workspace), and the
+ * combine, which sums each token's expert outputs itself.
  * Errors: INVALID_ARG (NULL pointers, eps <= 0 or not finite, dense not a
  * one-expert layer, D mismatch, has_shared set, T or k < 1), UNSUPPORTED
  * (T > 16, E > 256, D > 4096), the errors of moe_route_topk and
@@ -392,9 +393,12 @@ int q4_dequant_affine4(const void* w_packed, int64_t N, int64_t K, float* out, v
  *   src    device, 16-byte aligned, `bytes` readable (a positive multiple of 16)
  *   grid   workgroups of 256 threads, 1..65536
  *   mode   0: grid-stride (consecutive waves read consecutive KiB);
- *          1: workgroup b reads the b-th of `grid` contiguous chunks
- *   depth  loads per lane per batch (1, 2, 4 or 8); each lane keeps two
- *          batches in flight
+ *          1: workgroup b reads the b-th of `grid` contiguous chunks;
+ *          2: one batch per lane: 512-thread workgroups, workgroup b
+ *             reading the b-th of `grid` contiguous chunks (at most 256 KiB
+ *             each), every lane issuing all its loads at once
+ *   depth  loads per lane per batch in modes 0 and 1 (1, 2, 4 or 8), each
+ *          lane keeping two batches in flight; ignored in mode 2
  *   out    device u32[grid]: the XOR of each workgroup's words
  * Errors: INVALID_ARG (NULL, bytes, grid, mode, depth), ALIGNMENT, HIP. */
 int q4_stream_read(const void* src, size_t bytes, int grid, int mode, int depth, uint32_t* out, void* stream);

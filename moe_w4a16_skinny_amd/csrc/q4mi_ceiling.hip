@@ -15,6 +15,14 @@ using namespace dev;
 
 constexpr int kCeilThreads = 256;
 
+// XOR over the wave (one LDS atomic per wave afterwards, not one per lane:
+// atomics on one LDS word serialize)
+__device__ __forceinline__ unsigned wave_xor(unsigned x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off);
+  return x;
+}
+
 // Lane work: words i0, i0 + stride, ... below end, in batches of U loads,
 // the next batch issued before the previous one is consumed (two batches in
 // flight per lane).
@@ -61,9 +69,37 @@ __global__ __launch_bounds__(kCeilThreads) void stream_read_kernel(const uint8_t
   }
   for (; i < end; i += stride) acc ^= ld_nt16(src + i * 16);
   __syncthreads();
-  atomicXor(&sx, acc.x ^ acc.y ^ acc.z ^ acc.w);
+  const unsigned x = wave_xor(acc.x ^ acc.y ^ acc.z ^ acc.w);
+  if ((tid & 63) == 0) atomicXor(&sx, x);
   __syncthreads();
   if (tid == 0) out[blockIdx.x] = sx;
+}
+
+// MODE 2 (one batch): 512-thread workgroups; workgroup b reads the b-th of
+// `grid` contiguous chunks (whole KiB per wave instruction), every lane
+// issuing all its loads (at most kOnceMax) before the first is used, as a
+// GEMM wave issues its tiles.
+constexpr int kOnceMax = 32;
+__global__ __launch_bounds__(512) void stream_read_once_kernel(const uint8_t* __restrict__ src, size_t n16,
+                                                              size_t per, unsigned* __restrict__ out) {
+  __shared__ unsigned sx;
+  const size_t b0 = static_cast<size_t>(blockIdx.x) * per;
+  const size_t end = b0 + per < n16 ? b0 + per : n16;
+  if (threadIdx.x == 0) sx = 0u;
+  u32x4 v[kOnceMax];
+#pragma unroll
+  for (int u = 0; u < kOnceMax; ++u) {
+    const size_t i = b0 + static_cast<size_t>(u) * 512 + threadIdx.x;
+    v[u] = i < end ? ld_nt16(src + i * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+  u32x4 acc = v[0];
+#pragma unroll
+  for (int u = 1; u < kOnceMax; ++u) acc ^= v[u];
+  __syncthreads();
+  const unsigned x = wave_xor(acc.x ^ acc.y ^ acc.z ^ acc.w);
+  if ((threadIdx.x & 63) == 0) atomicXor(&sx, x);
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = sx;
 }
 
 template <int MODE, int U>
@@ -74,10 +110,16 @@ int launch_u(const uint8_t* p, size_t bytes, int grid, unsigned* out, hipStream_
 
 }  // namespace
 
-// depth: loads per batch (1, 2, 4 or 8; the host checks)
+// depth: loads per batch (1, 2, 4 or 8; the host checks); mode 2 ignores it
 int launch_stream_read(const void* src, size_t bytes, int grid, int mode, int depth, unsigned* out, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* p = static_cast<const uint8_t*>(src);
+  if (mode == 2) {
+    const size_t n16 = bytes / 16;
+    const size_t per = (n16 + grid - 1) / grid;
+    hipLaunchKernelGGL(stream_read_once_kernel, dim3(grid), dim3(512), 0, s, p, n16, per, out);
+    return static_cast<int>(hipGetLastError());
+  }
   if (mode == 0) {
     switch (depth) {
       case 1: return launch_u<0, 1>(p, bytes, grid, out, s);

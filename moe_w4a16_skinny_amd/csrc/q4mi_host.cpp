@@ -427,9 +427,11 @@ int q4_stream_read(const void* src, size_t bytes, int grid, int mode, int depth,
   REQUIRE_PTR(out);
   if (bytes == 0 || bytes % 16) return fail(Q4_ERR_INVALID_ARG, "%s: bytes=%zu is not a positive multiple of 16", __func__, bytes);
   if (grid < 1 || grid > 65536) return fail(Q4_ERR_INVALID_ARG, "%s: grid=%d outside 1..65536", __func__, grid);
-  if (mode != 0 && mode != 1) return fail(Q4_ERR_INVALID_ARG, "%s: mode=%d is not 0 or 1", __func__, mode);
-  if (depth != 1 && depth != 2 && depth != 4 && depth != 8)
+  if (mode < 0 || mode > 2) return fail(Q4_ERR_INVALID_ARG, "%s: mode=%d is not 0, 1 or 2", __func__, mode);
+  if (mode < 2 && depth != 1 && depth != 2 && depth != 4 && depth != 8)
     return fail(Q4_ERR_INVALID_ARG, "%s: depth=%d is not 1, 2, 4 or 8", __func__, depth);
+  if (mode == 2 && (bytes / 16 + size_t(grid) - 1) / size_t(grid) > size_t(512) * 32)
+    return fail(Q4_ERR_INVALID_ARG, "%s: mode 2 reads at most 256 KiB per workgroup (grid=%d)", __func__, grid);
   REQUIRE_ALIGNED(src);
   if (int e = launch_stream_read(src, bytes, grid, mode, depth, out, stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
@@ -493,8 +495,10 @@ static int route_check(const char* fn, const void* x, const float* w_router, int
 }
 
 static int route_enqueue(const char* fn, const void* x, const float* w_router, int T, int D, int E, int k,
-                         int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws, void* stream) {
+                         int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws, void* stream,
+                         bool topk = true) {
   RouteArgs r{};
+  r.topk = topk ? 1 : 0;
   r.x = static_cast<const uint16_t*>(x);
   r.wr = w_router;
   r.T = T;
@@ -525,13 +529,13 @@ int moe_route_topk(const void* x, const float* w_router, int T, int D, int E, in
 
 // ---- grouped MoE ---------------------------------------------------------
 
-// scratch after the counter region: h [npairs][F] f16, o [npairs][D] fp32,
+// scratch after the counter region: h [npairs][F] f16, o [T][k + 1][D] fp32,
 // rowof [T k] int32, the grouping table (moe_grp_words int32)
 static size_t moe_ws_layout(const q4_moe_desc* w, int T, int k, size_t* h_off, size_t* o_off, size_t* r_off,
                             size_t* g_off) {
   const size_t npairs = size_t(T) * size_t(k) + (w->has_shared ? size_t(T) : 0);
   const size_t hbytes = (npairs * size_t(w->F) * 2 + 255) / 256 * 256;
-  const size_t obytes = (npairs * size_t(w->D) * 4 + 255) / 256 * 256;
+  const size_t obytes = (size_t(T) * (size_t(k) + 1) * size_t(w->D) * 4 + 255) / 256 * 256;
   const size_t rbytes = (size_t(T) * size_t(k) * 4 + 255) / 256 * 256;
   const size_t gbytes = (moe_grp_words(w->E, T, k) * 4 + 255) / 256 * 256;
   *h_off = kWsCounterBytes;
@@ -589,7 +593,8 @@ static int moe_check(const char* fn, const q4_moe_desc* w, const void* x, const 
 }
 
 static int moe_enqueue(const char* fn, const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
-                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws, void* stream) {
+                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws, void* stream,
+                       bool combine = true) {
   size_t h_off, o_off, r_off, g_off;
   (void)moe_ws_layout(w, T, k, &h_off, &o_off, &r_off, &g_off);
   MoeArgs m{};
@@ -618,6 +623,7 @@ static int moe_enqueue(const char* fn, const q4_moe_desc* w, const void* x, cons
   m.o = reinterpret_cast<float*>(static_cast<char*>(ws) + o_off);
   m.rowof = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + r_off);
   m.grp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + g_off);
+  m.combine = combine ? 1 : 0;
   if (int e = launch_moe(m, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
   return Q4_OK;
 }
@@ -767,32 +773,35 @@ int qgemm_affine_bits(const void* w_packed, const void* a, int M, int64_t K, int
 // ---- MoE block -----------------------------------------------------------
 // Workspace: [0, sub) is shared by the router and the two grouped calls (run
 // one after another on the stream), then the block's own buffers.
+// The block's workspace: the experts' grouped-MoE workspace (sub2, which the
+// router uses before them; at offset 0, so the router's arrival counter is in
+// the buffer's counter region), the dense layer's (sub1: the grouped-MoE
+// kernels use no counters, only scratch above the counter region, which needs
+// no zero-fill), then the normed inputs, the logits and the routings.  The
+// two expert layers' outputs stay in their own workspaces until the block's
+// combine reads them.
 struct BlockWs {
-  size_t sub, h1, h2, logits, idx, w, ridx, rw, didx, dw, b1, b2, total;
+  size_t sub2, sub1, h1, h2, logits, idx, w, didx, dw, total;
 };
 static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 static BlockWs block_ws(const q4_moe_block_desc* b, int T, int k) {
   BlockWs L{};
   const int D = b->experts.D, E = b->experts.E;
-  L.sub = up256(std::max(std::max(moe_route_workspace_bytes(T, D, E), moe_workspace_bytes(&b->experts, T, k)),
-                         moe_workspace_bytes(&b->dense, T, 1)));
-  size_t o = L.sub;
+  size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o += up256(bytes);
     return at;
   };
+  L.sub2 = take(std::max(moe_route_workspace_bytes(T, D, E), moe_workspace_bytes(&b->experts, T, k)));
+  L.sub1 = take(moe_workspace_bytes(&b->dense, T, 1));
   L.h1 = take(size_t(T) * D * 2);
   L.h2 = take(size_t(T) * D * 2);
   L.logits = take(size_t(T) * E * 4);
   L.idx = take(size_t(T) * k * 4);
   L.w = take(size_t(T) * k * 4);
-  L.ridx = take(size_t(T) * k * 4);
-  L.rw = take(size_t(T) * k * 4);
   L.didx = take(size_t(T) * 4);
   L.dw = take(size_t(T) * 4);
-  L.b1 = take(size_t(T) * D * 4);
-  L.b2 = take(size_t(T) * D * 4);
   L.total = o;
   return L;
 }
@@ -843,30 +852,34 @@ int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k,
   const void* h1 = base + L.h1;
   const void* h2 = base + L.h2;
   float* logits = reinterpret_cast<float*>(base + L.logits);
-  const int32_t* didx = reinterpret_cast<const int32_t*>(base + L.didx);
-  const float* dw = reinterpret_cast<const float*>(base + L.dw);
-  float* b1 = reinterpret_cast<float*>(base + L.b1);
-  float* b2 = reinterpret_cast<float*>(base + L.b2);
-  if (int rc = route_check(__func__, h2, b->w_router, T, D, E, k, logits, reinterpret_cast<int32_t*>(base + L.ridx),
-                           reinterpret_cast<float*>(base + L.rw), ws, L.sub))
-    return rc;
-  if (int rc = moe_check(__func__, &b->dense, h1, didx, dw, T, 1, b1, Q4_F32, ws, L.sub)) return rc;
-  if (int rc = moe_check(__func__, &b->experts, h2, idx, w, T, k, b2, Q4_F32, ws, L.sub)) return rc;
+  int32_t* didx = reinterpret_cast<int32_t*>(base + L.didx);
+  float* dw = reinterpret_cast<float*>(base + L.dw);
+  void* ws1 = base + L.sub1;
+  void* ws2 = base + L.sub2;
+  const size_t ws2_bytes = L.sub1 - L.sub2, ws1_bytes = L.h1 - L.sub1;
+  // the expert layers leave their per-slot outputs in their workspaces (no
+  // combine launch of their own); y is required by the checks, never written
+  size_t h_off, o1_off, r1_off, g_off, o2_off, r2_off;
+  (void)moe_ws_layout(&b->dense, T, 1, &h_off, &o1_off, &r1_off, &g_off);
+  (void)moe_ws_layout(&b->experts, T, k, &h_off, &o2_off, &r2_off, &g_off);
+  const float* o1 = reinterpret_cast<const float*>(static_cast<char*>(ws1) + o1_off);
+  const float* o2 = reinterpret_cast<const float*>(static_cast<char*>(ws2) + o2_off);
+  const int32_t* rowof2 = reinterpret_cast<const int32_t*>(static_cast<char*>(ws2) + r2_off);
+  // the router computes the logits only; the block's own router kernel
+  // normalizes them and takes the top-k (idx and w are not written by it)
+  if (int rc = route_check(__func__, h2, b->w_router, T, D, E, k, logits, idx, w, ws2, ws2_bytes)) return rc;
+  if (int rc = moe_check(__func__, &b->dense, h1, didx, dw, T, 1, residual, Q4_F32, ws1, ws1_bytes)) return rc;
+  if (int rc = moe_check(__func__, &b->experts, h2, idx, w, T, k, residual, Q4_F32, ws2, ws2_bytes)) return rc;
   if (int e = launch_block_norm_in(residual, T, D, b->ffn_norm, b->pre_ffw_norm_2, b->eps, base + L.h1, base + L.h2,
                                    stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
-  if (int rc = route_enqueue(__func__, h2, b->w_router, T, D, E, k, 0, logits,
-                             reinterpret_cast<int32_t*>(base + L.ridx), reinterpret_cast<float*>(base + L.rw), ws,
-                             stream))
-    return rc;
-  if (int e = launch_block_router(logits, T, E, k, b->router_scale, b->down_scale, b->eps, idx, w,
-                                  reinterpret_cast<int32_t*>(base + L.didx), reinterpret_cast<float*>(base + L.dw),
-                                  stream))
+  if (int rc = route_enqueue(__func__, h2, b->w_router, T, D, E, k, 0, logits, idx, w, ws2, stream, false)) return rc;
+  if (int e = launch_block_router(logits, T, E, k, b->router_scale, b->down_scale, b->eps, idx, w, didx, dw, stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
-  if (int rc = moe_enqueue(__func__, &b->dense, h1, didx, dw, T, 1, b1, Q4_F32, ws, stream)) return rc;
-  if (int rc = moe_enqueue(__func__, &b->experts, h2, idx, w, T, k, b2, Q4_F32, ws, stream)) return rc;
-  if (int e = launch_block_combine(b1, b2, T, D, b->post_ffw_norm_1, b->post_ffw_norm_2, b->post_ffw_norm, b->eps,
-                                   residual, stream))
+  if (int rc = moe_enqueue(__func__, &b->dense, h1, didx, dw, T, 1, residual, Q4_F32, ws1, stream, false)) return rc;
+  if (int rc = moe_enqueue(__func__, &b->experts, h2, idx, w, T, k, residual, Q4_F32, ws2, stream, false)) return rc;
+  if (int e = launch_block_combine(o1, o2, rowof2, k, T, D, b->post_ffw_norm_1, b->post_ffw_norm_2, b->post_ffw_norm,
+                                   b->eps, residual, stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   return ok();
 }

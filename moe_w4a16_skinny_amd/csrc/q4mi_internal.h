@@ -108,8 +108,10 @@ int launch_block_norm_in(const float* res, int T, int D, const float* w1, const 
                          void* h2, void* stream);
 int launch_block_router(const float* logits, int T, int E, int k, const float* scale, const float* down_scale,
                         float eps, int32_t* idx, float* w, int32_t* didx, float* dw, void* stream);
-int launch_block_combine(const float* b1, const float* b2, int T, int D, const float* p1, const float* p2,
-                         const float* p, float eps, float* res, void* stream);
+// o1: the dense branch's outputs [T][2][D] (slot 0), o2 and rowof2 the
+// experts' [T][k + 1][D] and [T][k] (grouped-MoE scratch layout)
+int launch_block_combine(const float* o1, const float* o2, const int32_t* rowof2, int k, int T, int D,
+                         const float* p1, const float* p2, const float* p, float eps, float* res, void* stream);
 // affine 2/3/5/6/8-bit skinny GEMM (q4mi_affineb.hip)
 int launch_affine_bits(int bits, const uint8_t* w, int64_t N, int64_t K, const uint16_t* a, int M, void* out,
                        int out_dtype, void* stream);
@@ -151,6 +153,7 @@ struct RouteArgs {
   float* logits;        // nullable [T][E]
   int32_t* idx;         // [T][k]
   float* w;             // [T][k]
+  int topk;             // 0: logits only (no top-k; idx and w unused)
   float* partial;       // workspace [splits][T][E]
   unsigned* counter;    // workspace counter
   int nsplit;           // splits of D
@@ -173,10 +176,11 @@ struct MoeArgs {
   const float* tw;         // [T][k]
   void* y;
   int out_dtype;
-  uint16_t* h;             // workspace f16 [npairs][F]
-  float* o;                // workspace fp32 [npairs][D]
+  uint16_t* h;             // workspace f16 [npairs][F], expert-sorted rows
+  float* o;                // workspace fp32 [T][k + 1][D]: token t's slot s output (slot k: shared expert)
   int32_t* rowof;          // workspace [T * k]: pair -> scratch row (-1: none)
   int32_t* grp;            // workspace: the expert grouping, written by gate/up, read by down
+  int combine;             // 1: a third launch sums each token's slots into y
 };
 // the grouping table in the workspace (int32 words): nact, then act, cnt and
 // base [E + 1] each, then tok and slot as int16 [T k + T] each

@@ -310,10 +310,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
     }
   }
   __syncthreads();
-  if (E <= 128)
-    route_topk_rows<8>(r, lg);
-  else
-    route_topk_rows<16>(r, lg);
+  if (r.topk) {
+    if (E <= 128)
+      route_topk_rows<8>(r, lg);
+    else
+      route_topk_rows<16>(r, lg);
+  }
   if (tid == 0) atomicExch(r.counter, 0u);
 }
 
@@ -595,7 +597,11 @@ __device__ __forceinline__ int items_of_wave(int nitems, int gw, int NW) {
 // (with its first weight loads in flight), and each item's tokens are read
 // from there, so the stream issues only weight loads; AM = kAGlobal (when x
 // does not fit beside the stash): lanes load their token's activations.
-template <int W, int DP, int AM>
+// KS: a layer with few items (one expert: the block's dense branch) gives
+// each item to a whole workgroup, its W waves streaming W consecutive
+// ranges of the K tiles; the waves' partial sums meet in LDS and are added
+// in wave order before the epilogue.  Otherwise an item is one wave's.
+template <int W, int DP, int AM, bool KS>
 __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW) {
   __shared__ MoeGroups G;
   build_groups(m, G);
@@ -608,12 +614,18 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   const int o = lane >> 4, c = lane & 15;
   const int npp = m.F / 16;
   const int nitems = G.nact * npp;
-  const int gw = blockIdx.x + gridDim.x * w, NW = gridDim.x * W;
+  // the item dealer: a wave (gw of NW), or with KS the whole workgroup
+  const int gw = KS ? static_cast<int>(blockIdx.x) : blockIdx.x + gridDim.x * w;
+  const int NW = KS ? static_cast<int>(gridDim.x) : gridDim.x * W;
   // a wave's items go in chunks of at most NGW (its stash slots)
   const int ntot = items_of_wave(nitems, gw, NW);
+  if (KS && ntot == 0) return;  // the whole workgroup idle
   int c0 = 0, ng = 0;  // current chunk: items c0 .. c0 + ng
   const int nfull = static_cast<int>(full_tiles(m.D));
   const bool half = has_half_tile(m.D);
+  const int ntx0 = nfull + (half ? 1 : 0);
+  const int kt0 = KS ? (w * ntx0) / W : 0;  // this wave's K tiles [kt0, kt0 + krg)
+  const int krg = KS ? ((w + 1) * ntx0) / W - kt0 : ntx0;
 
   const DivBy by_npp(static_cast<unsigned>(npp));
   const __amdgpu_buffer_rsrc_t xr = act_rsrc(m.x, static_cast<unsigned>(m.T) * static_cast<unsigned>(m.D) * 2u);
@@ -634,7 +646,7 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
     gp.panel[1] = m.up + static_cast<size_t>(e) * m.gate_stride + static_cast<size_t>(jp) * m.gate_panel_bytes;
     const int me = min(G.cnt[e], 16);
     if constexpr (AM == kAStagedRows) {
-      gp.alds = static_cast<unsigned>(G.tok[G.base[e] + min(c, me - 1)]) * xrs;
+      gp.alds = static_cast<unsigned>(G.tok[G.base[e] + min(c, me - 1)]) * xrs + static_cast<unsigned>(kt0) * 256u;
     } else {
       gp.arsrc = xr;
       gp.aoff = c < me ? static_cast<unsigned>(G.tok[G.base[e] + c]) * static_cast<unsigned>(m.D) * 2u : kDeadLane;
@@ -660,13 +672,23 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   auto none = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[2][2]) { stash<2>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[2][2]) { stash_add<2>(wout, gi, acc); };
+  f32x4* const stash0 = reinterpret_cast<f32x4*>(dyn + xbytes);
   auto finish = [&]() {
-    for (int gi = 0; gi < ng; ++gi) {
+    if constexpr (KS) __syncthreads();  // every wave's partial sums parked
+    for (int gi = KS ? w : 0; gi < ng; gi += KS ? W : 1) {
       int e, jp;
       item(gi, e, jp);
       const int me = min(G.cnt[e], 16), base = G.base[e];
       const float gg = G.gs0[e], gu = G.gs1[e];
-      const f32x4 rg = wout[(gi * 2 + 0) * 64 + lane], ru = wout[(gi * 2 + 1) * 64 + lane];
+      f32x4 rg = wout[(gi * 2 + 0) * 64 + lane], ru = wout[(gi * 2 + 1) * 64 + lane];
+      if constexpr (KS) {
+        rg = ru = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < W; ++v) {  // the waves' K ranges, in order
+          const f32x4* sv = stash0 + static_cast<size_t>(v) * NGW * 2 * 64;
+          rg += sv[(gi * 2 + 0) * 64 + lane];
+          ru += sv[(gi * 2 + 1) * 64 + lane];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * o + r;
@@ -676,16 +698,17 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
         }
       }
     }
+    if constexpr (KS) __syncthreads();  // the stash is free for the next chunk
     c0 += NGW;
   };
   if (nitems == 0) return;  // no item at all: nothing to stage or compute
   ng = min(NGW, ntot);
-  stream_groups<kNvfp4, 2, DP, AM>(ng, ntx, 0, half ? nfull : -1, al, ARing{}, m.D, group, stage_pre_issue, stage_pre,
-                                   epi, epi_add);
+  stream_groups<kNvfp4, 2, DP, AM>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.D, group, stage_pre_issue,
+                                   stage_pre, epi, epi_add);
   finish();
   while (c0 < ntot) {
     ng = min(NGW, ntot - c0);
-    stream_groups<kNvfp4, 2, DP, AM>(ng, ntx, 0, half ? nfull : -1, al, ARing{}, m.D, group, none, none, epi,
+    stream_groups<kNvfp4, 2, DP, AM>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.D, group, none, none, epi,
                                      epi_add);
     finish();
   }
@@ -695,8 +718,9 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
 
 // Item (active expert a, group q of P panels of W_down, N = D): K = F, the
 // activation rows are the expert's contiguous h rows; o[row][n] = w_pair *
-// g_down * acc in fp32.
-template <int P, int W, int DP>
+// g_down * acc in fp32.  KS: every item of the workgroup's range is streamed
+// by all W waves, each over its own range of the K tiles, as in gate/up.
+template <int P, int W, int DP, bool KS>
 __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, int stage_room) {
   __shared__ MoeDownTable G;
   fetch_groups(m, G);
@@ -711,17 +735,20 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, in
   const int i0 = static_cast<int>((static_cast<long long>(blockIdx.x) * nitems) / gridDim.x);
   const int i1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * nitems) / gridDim.x);
   if (i1 <= i0) return;  // no item for this workgroup (uniform)
-  const int ntot = i1 - i0 > w ? (i1 - i0 - w + W - 1) / W : 0;  // in chunks of at most NGW, as in gate/up
+  // items of this wave (all of the range with KS), in chunks of at most NGW, as in gate/up
+  const int ntot = KS ? i1 - i0 : (i1 - i0 > w ? (i1 - i0 - w + W - 1) / W : 0);
   int c0 = 0, ng = 0;
   const int nfull = static_cast<int>(full_tiles(m.F));
   const bool half = has_half_tile(m.F);
   const int ntf = nfull + (half ? 1 : 0);
+  const int kt0 = KS ? (w * ntf) / W : 0;  // this wave's K tiles [kt0, kt0 + krg)
+  const int krg = KS ? ((w + 1) * ntf) / W - kt0 : ntf;
 
   const DivBy by_ngp(static_cast<unsigned>(ngp));
   const unsigned nrows_h = static_cast<unsigned>(m.T * m.k + (m.has_shared ? m.T : 0));
   const __amdgpu_buffer_rsrc_t hr = act_rsrc(m.h, nrows_h * static_cast<unsigned>(m.F) * 2u);
   auto item = [&](int gi, int& e, int& q) {
-    int it = i0 + w + (c0 + gi) * W;
+    int it = KS ? i0 + c0 + gi : i0 + w + (c0 + gi) * W;
     it = it < i1 ? it : i1 - 1;  // past the wave's items: in-bounds, never computed
     const int a = by_ngp(it);
     q = it - a * ngp;
@@ -742,7 +769,8 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, in
   auto epi_add = [&](int gi, f32x4 (&acc)[P][2]) { stash_add<P>(wout, gi, acc); };
   const int nrow = m.T * m.k + m.T;
   auto finish = [&]() {
-    for (int gi = 0; gi < ng; ++gi) {
+    if constexpr (KS) __syncthreads();  // every wave's partial sums parked
+    for (int gi = KS ? w : 0; gi < ng; gi += KS ? W : 1) {
       int e, q;
       item(gi, e, q);
       const int me = min(G.cnt[e], 16), base = G.base[e];
@@ -753,14 +781,23 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, in
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int pi = q * P + p;
-        const f32x4 v = wout[(gi * P + p) * 64 + lane];
+        f32x4 v = wout[(gi * P + p) * 64 + lane];
+        if constexpr (KS) {
+          v = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int u = 0; u < W; ++u) v += dn_dyn[(static_cast<size_t>(u) * NGW + gi) * P * 64 + p * 64 + lane];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 4 * o + r;
-          if (pi < npan && row < me) m.o[static_cast<size_t>(base + row) * m.D + pi * 16 + c] = wp[r] * (gd * v[r]);
+          if (pi < npan && row < me) {
+            const int sl = G.slot[base + row];  // the row's (token, slot); -1: the shared expert, slot k
+            const size_t orow = static_cast<size_t>(G.tok[base + row]) * (m.k + 1) + (sl < 0 ? m.k : sl);
+            m.o[orow * m.D + pi * 16 + c] = wp[r] * (gd * v[r]);
+          }
         }
       }
     }
+    if constexpr (KS) __syncthreads();  // the stash is free for the next chunk
     c0 += NGW;
   };
   // the two ways of reaching the activations; as in gate/up, the first
@@ -778,7 +815,7 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, in
       }
       const int me = min(G.cnt[e], 16);
       if constexpr (AM == kAStagedRows) {
-        gp.alds = static_cast<unsigned>(G.base[e] + min(c, me - 1) - rlo) * hrs;
+        gp.alds = static_cast<unsigned>(G.base[e] + min(c, me - 1) - rlo) * hrs + static_cast<unsigned>(kt0) * 256u;
       } else {
         gp.arsrc = hr;
         gp.aoff = c < me ? static_cast<unsigned>(G.base[e] + c) * static_cast<unsigned>(m.F) * 2u : kDeadLane;
@@ -792,12 +829,12 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, in
     };
     auto none = [] {};
     ng = min(NGW, ntot);
-    stream_groups<kNvfp4, P, DP, AM>(ng, ntf, 0, half ? nfull : -1, al, ARing{}, m.F, group, stage_pre_issue,
+    stream_groups<kNvfp4, P, DP, AM>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group, stage_pre_issue,
                                      stage_pre, epi, epi_add);
     finish();
     while (c0 < ntot) {
       ng = min(NGW, ntot - c0);
-      stream_groups<kNvfp4, P, DP, AM>(ng, ntf, 0, half ? nfull : -1, al, ARing{}, m.F, group, none, none, epi,
+      stream_groups<kNvfp4, P, DP, AM>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group, none, none, epi,
                                        epi_add);
       finish();
     }
@@ -810,31 +847,37 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, in
 
 // ------------------------------------------------------------------ combine
 
-// y[t][n] = sum_{s<k} o[pos(t, s)][n] (+ o[T k + t][n] for the shared expert),
-// slots in order.  pos(t, s) = (valid pairs routed to lower experts) + (rank of
-// the pair among its expert's pairs), the row gate_up/down used for it.
+// y[t][n] = sum_{s<k} o[t][s][n] (+ o[t][k][n] for the shared expert), slots
+// in order; a slot whose pair has no row (an index outside 0..E-1, or past an
+// expert's 16th) adds nothing.  Four columns per thread; the row map and the
+// outputs are loaded together (the output rows are at fixed places).
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs m) {
   const int t = blockIdx.x;
-  const int n = blockIdx.y * 256 + threadIdx.x;
+  const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (n >= m.D) return;
-  const int nall = m.T * m.k;
-  float acc = 0.f;
-  for (int s0 = 0; s0 < m.k; s0 += 16) {  // 16 slots' rows in flight, summed in slot order
-    float v[16];
+  const float* ot = m.o + static_cast<size_t>(t) * (m.k + 1) * m.D + n;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < m.k; s0 += 8) {  // 8 slots' rows in flight, summed in slot order
+    f32x4 v[8];
+    int pos[8];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int s = s0 + u;
-      const int pos = s < m.k ? m.rowof[t * m.k + s] : -1;
-      v[u] = pos >= 0 ? m.o[static_cast<size_t>(pos) * m.D + n] : 0.f;
+    for (int u = 0; u < 8; ++u) {
+      const int sl = min(s0 + u, m.k - 1);
+      pos[u] = s0 + u < m.k ? m.rowof[t * m.k + sl] : -1;
+      v[u] = *reinterpret_cast<const f32x4*>(ot + static_cast<size_t>(sl) * m.D);
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc += v[u];
+    for (int u = 0; u < 8; ++u)
+      if (pos[u] >= 0) acc += v[u];
   }
-  if (m.has_shared) acc += m.o[static_cast<size_t>(nall + t) * m.D + n];
-  if (m.out_dtype == Q4_F32)
-    static_cast<float*>(m.y)[static_cast<size_t>(t) * m.D + n] = acc;
-  else
-    static_cast<_Float16*>(m.y)[static_cast<size_t>(t) * m.D + n] = (_Float16)acc;
+  if (m.has_shared) acc += *reinterpret_cast<const f32x4*>(ot + static_cast<size_t>(m.k) * m.D);
+  if (m.out_dtype == Q4_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(m.y) + static_cast<size_t>(t) * m.D + n) = acc;
+  } else {
+    const f16x2 h0 = {(f16)acc[0], (f16)acc[1]}, h1 = {(f16)acc[2], (f16)acc[3]};
+    *reinterpret_cast<u32x2*>(static_cast<f16*>(m.y) + static_cast<size_t>(t) * m.D + n) =
+        u32x2{__builtin_bit_cast(unsigned, h0), __builtin_bit_cast(unsigned, h1)};
+  }
 }
 
 // Scratch of moe_grouped_qgemm_noalloc: one array per device, in the code
@@ -874,36 +917,50 @@ int launch_route(const RouteArgs& r, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
+template <int W, bool KS>
+const void* gate_up_fn(bool staged) {
+  return staged ? reinterpret_cast<const void*>(&moe_gate_up_kernel<W, 4, kAStagedRows, KS>)
+                : reinterpret_cast<const void*>(&moe_gate_up_kernel<W, 4, kAGlobal, KS>);
+}
+
 int launch_moe(const MoeArgs& m, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int nexp = m.E + m.has_shared;
   constexpr int GU_W = 8, DN_P = 2, DN_W = 8, kWG = 256;  // one 8-wave workgroup per CU
   const int gu_nw = kWG * GU_W, dn_nw = kWG * DN_W;  // waves in the grid
+  // experts that can be active: at most one per routed pair, plus the shared one
+  const int nact_max = std::min(m.E, m.T * m.k) + m.has_shared;
+  const int npp = m.F / 16;
+  const int ngp = (m.D / 16 + DN_P - 1) / DN_P;
+  const int ntx = static_cast<int>(full_tiles(m.D) + (has_half_tile(m.D) ? 1 : 0));
+  const int ntf = static_cast<int>(full_tiles(m.F) + (has_half_tile(m.F) ? 1 : 0));
+  // K split over a workgroup's waves when the layer has too few items to give
+  // every CU's waves one each (at least one K tile per wave)
+  const bool gu_ks = nact_max * npp <= 2 * kWG && ntx >= GU_W;
+  const bool dn_ks = nact_max * ngp <= 2 * kWG && ntf >= DN_W;
   // stash slots per wave (items parked until the wave's stream ends): as many
   // as a wave has items at most, up to what 96 KiB of LDS holds; a wave with
   // more items streams them in chunks of that many
   constexpr size_t kStashLds = 96 * 1024;
-  const int npp = m.F / 16;
   const int gu_cap = static_cast<int>(kStashLds / (size_t(GU_W) * 2 * 64 * 16));
-  const int gu_need = (nexp * npp + gu_nw - 1) / gu_nw;  // stash slots a wave would use for all its items
+  const int gu_need = gu_ks ? (nact_max * npp + kWG - 1) / kWG : (nact_max * npp + gu_nw - 1) / gu_nw;
   int gu_ngw = std::min(gu_need, gu_cap);
   size_t gu_lds = static_cast<size_t>(GU_W) * gu_ngw * 2 * 64 * 16;
   // gate/up stages x in LDS when it fits beside the grouping table and a
   // stash of at least one item per wave (a wave with more items than slots
-  // streams them in chunks)
-  const int ntx = static_cast<int>(full_tiles(m.D) + (has_half_tile(m.D) ? 1 : 0));
+  // streams them in chunks); with the K split each wave reads only its range
+  // of x, from global memory
   const size_t xbytes = (static_cast<size_t>(stage_bytes(m.T, ntx)) + 15) / 16 * 16;
   const size_t lds_total = 160 * 1024;
   const size_t slot = static_cast<size_t>(GU_W) * 2 * 64 * 16;
   const size_t room = lds_total > sizeof(MoeGroups) + xbytes ? lds_total - sizeof(MoeGroups) - xbytes : 0;
-  const bool gu_staged = room >= slot;
+  const bool gu_staged = !gu_ks && room >= slot;
   if (gu_staged) {
     gu_ngw = std::min(gu_need, static_cast<int>(room / slot));
     gu_lds = xbytes + static_cast<size_t>(gu_ngw) * slot;
   }
-  const int ngp = (m.D / 16 + DN_P - 1) / DN_P;
   const int dn_cap = static_cast<int>(kStashLds / (size_t(DN_W) * DN_P * 64 * 16));
-  const int dn_ngw = std::min((nexp * ngp + dn_nw - 1) / dn_nw, dn_cap);
+  const int dn_need = dn_ks ? (nact_max * ngp + kWG - 1) / kWG : (nact_max * ngp + dn_nw - 1) / dn_nw;
+  const int dn_ngw = std::min(dn_need, dn_cap);
   // the rest of the CU's LDS holds a workgroup's staged h rows (a workgroup
   // whose rows do not fit reads them from global memory)
   const size_t dn_stash = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
@@ -911,19 +968,30 @@ int launch_moe(const MoeArgs& m, void* stream) {
   const size_t dn_room = 160 * 1024 > dn_fixed + dn_stash ? 160 * 1024 - dn_fixed - dn_stash : 0;
   const size_t dn_lds = dn_stash + dn_room;
   if (gu_ngw < 1 || dn_ngw < 1) return static_cast<int>(hipErrorInvalidConfiguration);
-  const void* gu_fn = gu_staged ? reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4, kAStagedRows>)
-                                : reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4, kAGlobal>);
+  const void* gu_fn = gu_ks ? gate_up_fn<GU_W, true>(gu_staged) : gate_up_fn<GU_W, false>(gu_staged);
+  const void* dn_fn = dn_ks ? reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4, true>)
+                            : reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4, false>);
   if (int e = ensure_dynamic_lds(gu_fn, gu_lds)) return e;
-  if (int e = ensure_dynamic_lds(reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4>), dn_lds)) return e;
-  if (gu_staged)
-    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAStagedRows>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m, gu_ngw);
+  if (int e = ensure_dynamic_lds(dn_fn, dn_lds)) return e;
+  if (gu_ks)
+    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAGlobal, true>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m,
+                       gu_ngw);
+  else if (gu_staged)
+    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAStagedRows, false>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m,
+                       gu_ngw);
   else
-    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAGlobal>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m, gu_ngw);
+    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAGlobal, false>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m,
+                       gu_ngw);
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
-  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw,
-                     static_cast<int>(dn_room));
+  if (dn_ks)
+    hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4, true>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw,
+                       static_cast<int>(dn_room));
+  else
+    hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4, false>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw,
+                       static_cast<int>(dn_room));
   if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(m.T, (m.D + 255) / 256), dim3(256), 0, s, m);
+  if (!m.combine) return 0;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(m.T, (m.D / 4 + 255) / 256), dim3(256), 0, s, m);
   return static_cast<int>(hipGetLastError());
 }
 

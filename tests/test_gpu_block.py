@@ -165,3 +165,34 @@ def test_block_refusals():
         m.moe_block_forward(bw, res.double(), 2)
     torch.cuda.synchronize()
     assert torch.equal(res, before), "a refused call changed the residual"
+
+
+def test_block_scratch_needs_no_zero_fill():
+    # Only the workspace's first 32 KiB (counters) must start at zero; the
+    # scratch above them may hold anything (here: NaN bit patterns and junk
+    # left from other calls), and the result is the same as on a zeroed one.
+    import ctypes as C
+    m = q4()
+    blk = synth.moe_block(81, T=6, D=512, E=16, F=128, F_dense=192, k=4)
+    bw = m.moe_block_pack(blk)
+    d = bw.desc()
+    lib = m.raw()
+    T, k = blk.T, blk.k
+    wsb = lib.moe_block_workspace_bytes(C.byref(d), T, k)
+    outs = []
+    for fill in (0, 0xFF, 0x7F):
+        ws = torch.full((wsb,), fill, dtype=torch.uint8, device="cuda")
+        ws[:32768].zero_()
+        res = torch.from_numpy(np.ascontiguousarray(blk.residual)).cuda()
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        vp = C.c_void_p
+        rc = lib.moe_block_forward(C.byref(d), vp(res.data_ptr()), T, k, vp(idx.data_ptr()), vp(w.data_ptr()),
+                                   vp(ws.data_ptr()), C.c_size_t(wsb), vp(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0, lib.q4_last_error().decode() if hasattr(lib, "q4_last_error") else rc
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[:32768]).item() == 0, "counters not left at zero"
+        outs.append((res.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b), "result depends on the scratch's prior contents"

@@ -201,6 +201,20 @@ def test_moe_small_layers(T, D, E, F, k, shared):
     check_moe(moe, mw, idx, w, what=f"T={T} D={D} E={E} F={F} k={k} shared={shared}")
 
 
+@pytest.mark.parametrize("T,D,E,F,k,shared", [(16, 2816, 1, 2112, 1, False), (5, 1088, 2, 1088, 1, True),
+                                               (3, 1024, 1, 1024, 1, False), (2, 960, 1, 960, 1, False),
+                                               (16, 1024, 4, 1024, 2, True)])
+def test_moe_k_split_layers(T, D, E, F, k, shared):
+    # few items (at most 512 per kernel): each is streamed by a whole
+    # workgroup, its 8 waves over 8 ranges of the K tiles.  The dense-branch
+    # shape; ragged D and F (a half tile in the last range); exactly one tile
+    # per wave; a last range of only the half tile; up to two items per
+    # workgroup
+    moe, mw = layer(930 + T + D + E + F + k, T=T, D=D, E=E, F=F, k=k, has_shared=shared)
+    _, idx, w = oracle.route_topk(moe.x, moe.w_router, moe.k)
+    check_moe(moe, mw, idx, w, what=f"K split: T={T} D={D} E={E} F={F} k={k} shared={shared}")
+
+
 @pytest.mark.parametrize("D,F", [(128, 3072), (6144, 64)])
 def test_moe_more_items_than_stash_slots(D, F):
     # 65 experts x 192 panel items > 6 stash slots x 2048 waves: waves stream
