@@ -335,7 +335,7 @@ class MoeBlockWork:
         per = lambda f: 2 * (f * D // 2 + f * D // 16 + 4) + (D * f // 2 + D * f // 16 + 4)
         self.alg_bytes = D * blk.E * 4 + per(Fd) + self.active * per(F) + 2 * T * D * 4
         self.kind = "moe_block"
-        self.kernel_names = ["block step: block_norm_in + route (logits) + block_router + 2 x (moe_gate_up + "
+        self.kernel_names = ["block step: block_norm_in + route (with the block's scores) + 2 x (moe_gate_up + "
                              "moe_down) + block_combine"]
         self.dtype = "f16"
 

@@ -100,7 +100,6 @@ int q4_nvfp4_repack(const uint8_t* codes, const uint8_t* scales, int64_t N, int6
 /* Inverse of q4_nvfp4_repack (host memory), for tests and inspection. */
 int q4_nvfp4_unpack(const void* packed, int64_t N, int64_t K, uint8_t* codes, uint8_t* scales);
 
-/* Bytes of the packed affine matrix [N][K]; 0 unless N % 16 == 0 and K % 64 == 0. */
 /* Bytes of device workspace q4_nvfp4_quantize needs when it computes the
  * global scale itself (one scratch word past the counter area). */
 size_t q4_nvfp4_quantize_workspace_bytes(void);
@@ -126,6 +125,7 @@ size_t q4_nvfp4_quantize_workspace_bytes(void);
 int q4_nvfp4_quantize(const float* w, int64_t N, int64_t K, float global_scale, void* packed,
                       size_t packed_bytes, float* g_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the packed affine matrix [N][K]; 0 unless N % 16 == 0 and K % 64 == 0. */
 size_t q4_affine4_packed_bytes(int64_t N, int64_t K);
 
 /* Pack canonical affine 4-bit (host codes u8[N][K/2], scale and bias as bf16
@@ -154,8 +154,10 @@ size_t qgemm_affine4_workspace_bytes(int M, int64_t K, int64_t N);
 /* NVFP4 W4A16 GEMM [README "Everything it has": the M <= 16 GEMM with
  * in-register FP4 -> f16 dequant; "Why it's NVIDIA-only": E2M1 x E4M3/16 x
  * fp32 global].  Each weight is e2m1(code) * e4m3(scale) * global_scale.
- * More rows (17 <= M <= 65536, argmax NULL) -- prefill chunks and large
- * verify blocks, the M > 16 product of [README "Everything it has"] -- run a
+ * More rows (17 <= M <= 65536, argmax NULL) -- prompt chunks and large
+ * verify blocks [README, repository layout: the engine's prefill beside
+ * decode; DOC 3.3 "Decode vs prefill": prefill runs many tokens at once]
+ * -- run a
  * matrix-core kernel with 64 x 128 output blocks; it needs no workspace
  * (the query returns 0) and its results obey the same error bound.
  *   w_packed  device, from q4_nvfp4_repack of the [N][K] weights
@@ -287,8 +289,9 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
 int moe_grouped_qgemm_noalloc(const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
                               const float* topk_w, int T, int k, void* y, int out_dtype, void* stream);
 
-/* MLX-style affine weights at 2, 3, 5, 6 or 8 bits [README "Everything it
- * has": the MLX affine widths, groups of 64; the 4-bit width has the entry
+/* MLX-style affine weights at 2, 3, 5, 6 or 8 bits [ISSUE "Why now":
+ * qlinear's MLX affine paths at 2, 3, 5, 6 and 8 bits beside 4, groups of
+ * 64; "Steps" 3 and 9: the other MLX widths; the 4-bit width has the entry
  * points above].  w = q * scale + bias per 64-value group.
  *   codes  host u8 [N][K], one code per byte, each < 2^bits
  *   scale_bf16, bias_bf16  host bf16 bit patterns [N][K/64]
@@ -354,11 +357,12 @@ size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k);
  *   ws           device workspace of ws_bytes >= moe_block_workspace_bytes;
  *                its first 32 KiB of counters start and end at zero, as for
  *                the other entry points
- * The block runs 8 launches on `stream`: the two input norms, the router
- * matmul (moe_route_topk's kernel, logits only), the router normalization
- * and top-k, the dense branch and the experts (moe_grouped_qgemm's gate/up
- * and down kernels, each layer in its own part of the workspace), and the
- * combine, which sums each token's expert outputs itself.
+ * The block runs 7 launches on `stream`: the two input norms, the router
+ * (moe_route_topk's kernel; its last workgroup normalizes and scales the
+ * scores and takes the top-k), the dense branch and the experts
+ * (moe_grouped_qgemm's gate/up and down kernels, each layer in its own part
+ * of the workspace), and the combine, which sums each token's expert
+ * outputs itself.
  * Errors: INVALID_ARG (NULL pointers, eps <= 0 or not finite, dense not a
  * one-expert layer, D mismatch, has_shared set, T or k < 1), UNSUPPORTED
  * (T > 16, E > 256, D > 4096), the errors of moe_route_topk and

@@ -19,8 +19,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4mi.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_w4a16_skinny_amd.build` "
-                      "(or __graft_entry__.build()) before using the library")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python moe_w4a16_skinny_amd/build.py` "
+                      "from the repository root (or __graft_entry__.build()) before using the library")
 _lib = C.CDLL(LIB_PATH)
 
 Q4_OK, Q4_ERR_INVALID_ARG, Q4_ERR_UNSUPPORTED, Q4_ERR_ALIGNMENT, Q4_ERR_WORKSPACE, Q4_ERR_HIP = 0, -1, -2, -3, -4, -5

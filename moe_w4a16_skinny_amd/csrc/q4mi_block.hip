@@ -1,5 +1,6 @@
-// The Gemma-4 MoE block around the expert kernels: the RMSNorms, the
-// router's normalization and the combine.
+// The Gemma-4 MoE block around the expert kernels: the input RMSNorms and
+// the combine.  (The router's normalization, softmax and top-k run in the
+// last workgroup of the router kernel.)
 //
 // [DOC 3.2 "Per-layer (MoE)"], [DOC 4.6 "MoE"]: from the residual r,
 //   h1 = RMSNorm(r; ffn_norm), h2 = RMSNorm(r; pre_ffw_norm_2)
@@ -75,103 +76,6 @@ __global__ __launch_bounds__(256) void block_norm_in_kernel(const float* __restr
       o1[i] = static_cast<f16>(x * a[j]);
       o2[i] = static_cast<f16>(x * b[j]);
     }
-  }
-}
-
-// One wave per token: z = RMSNorm(logits) * scale over the E <= 256 logits
-// (lane l holds experts l, l + 64, l + 128, l + 192), softmax, top-k (larger
-// z first, ties to the lower index, k <= 16); w = p * down_scale.  Also writes the dense branch's one-expert
-// routing (expert 0, weight 1).
-__global__ __launch_bounds__(64) void block_router_kernel(const float* __restrict__ logits, int E, int k,
-                                                          const float* __restrict__ scale,
-                                                          const float* __restrict__ down_scale, float eps,
-                                                          int32_t* __restrict__ idx, float* __restrict__ w,
-                                                          int32_t* __restrict__ didx, float* __restrict__ dw) {
-  const int t = blockIdx.x, lane = threadIdx.x;
-  const float* lr = logits + static_cast<size_t>(t) * E;
-  float z[4], sc[4], ds[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {  // the logits and both scales of this lane's experts, loaded together
-    const int e = lane + 64 * j;
-    z[j] = e < E ? lr[e] : 0.f;
-    sc[j] = e < E ? scale[e] : 0.f;
-    ds[j] = (e < E && down_scale) ? down_scale[e] : 1.0f;
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ss = fmaf(z[j], z[j], ss);
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-  ss = __shfl(ss, 0);
-  const float r = inv_rms(ss, E, eps);
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    z[j] = e < E ? z[j] * r * sc[j] : -INFINITY;
-    m = fmaxf(m, z[j]);
-  }
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  float se = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) se += (lane + 64 * j < E) ? expf(z[j] - m) : 0.f;
-  for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
-  se = __shfl(se, 0);
-  // Top-k without a round per pick: find the k-th largest ordered key V by
-  // a bitwise search whose counts are wave ballots, take every key above V
-  // and the lowest-index keys equal to V, park the k picks in LDS, and let
-  // lane r < k place pick r at its rank (larger z first, ties to the lower
-  // index).  NaN scores (key 0) rank lowest.
-  __shared__ unsigned skey[16];
-  __shared__ int sidx[16];
-  __shared__ float sw[16];
-  unsigned key[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    const float v = z[j] == 0.f ? 0.f : z[j];  // -0 and +0 are equal
-    const unsigned b = __float_as_uint(v);
-    key[j] = (e < E && v == v) ? ((b & 0x80000000u) ? ~b : (b | 0x80000000u)) : 0u;
-  }
-  unsigned V = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const unsigned cand = V | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-    if (cnt >= k) V = cand;
-  }
-  int above = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) above += __popcll(__ballot(key[j] > V));
-  const int need = k - above;  // keys equal to V to take, lowest index first
-  const unsigned long long below = (1ull << lane) - 1ull;
-  int eq_base = 0, sel_base = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const unsigned long long eq = __ballot(key[j] == V);
-    const bool pick = key[j] > V || (key[j] == V && eq_base + __popcll(eq & below) < need);
-    const unsigned long long sel = __ballot(pick);
-    if (pick) {
-      const int slot = sel_base + __popcll(sel & below);
-      skey[slot] = key[j];
-      sidx[slot] = lane + 64 * j;
-      sw[slot] = expf(z[j] - m) / se * ds[j];
-    }
-    eq_base += __popcll(eq);
-    sel_base += __popcll(sel);
-  }
-  __syncthreads();
-  if (lane < k) {
-    const unsigned mk = skey[lane];
-    const int me = sidx[lane];
-    int rank = 0;
-    for (int q = 0; q < k; ++q) rank += (skey[q] > mk || (skey[q] == mk && sidx[q] < me)) ? 1 : 0;
-    idx[t * k + rank] = me;
-    w[t * k + rank] = sw[lane];
-  }
-  if (lane == 0) {
-    didx[t] = 0;
-    dw[t] = 1.0f;
   }
 }
 
@@ -264,13 +168,6 @@ int launch_block_norm_in(const float* res, int T, int D, const float* w1, const 
                          void* h2, void* stream) {
   hipLaunchKernelGGL(block_norm_in_kernel, dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream), res, D, w1, w2,
                      eps, static_cast<f16*>(h1), static_cast<f16*>(h2));
-  return static_cast<int>(hipGetLastError());
-}
-
-int launch_block_router(const float* logits, int T, int E, int k, const float* scale, const float* down_scale,
-                        float eps, int32_t* idx, float* w, int32_t* didx, float* dw, void* stream) {
-  hipLaunchKernelGGL(block_router_kernel, dim3(T), dim3(64), 0, static_cast<hipStream_t>(stream), logits, E, k, scale,
-                     down_scale, eps, idx, w, didx, dw);
   return static_cast<int>(hipGetLastError());
 }
 

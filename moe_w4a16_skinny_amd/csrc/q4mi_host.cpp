@@ -496,9 +496,15 @@ static int route_check(const char* fn, const void* x, const float* w_router, int
 
 static int route_enqueue(const char* fn, const void* x, const float* w_router, int T, int D, int E, int k,
                          int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws, void* stream,
-                         bool topk = true) {
+                         const q4_moe_block_desc* blk = nullptr, int32_t* didx = nullptr, float* dw = nullptr) {
   RouteArgs r{};
-  r.topk = topk ? 1 : 0;
+  if (blk) {  // the MoE block's routing: scores normalized and scaled, weights times the down scale
+    r.zscale = blk->router_scale;
+    r.down_scale = blk->down_scale;
+    r.eps = blk->eps;
+    r.didx = didx;
+    r.dw = dw;
+  }
   r.x = static_cast<const uint16_t*>(x);
   r.wr = w_router;
   r.T = T;
@@ -771,17 +777,15 @@ int qgemm_affine_bits(const void* w_packed, const void* a, int M, int64_t K, int
 }
 
 // ---- MoE block -----------------------------------------------------------
-// Workspace: [0, sub) is shared by the router and the two grouped calls (run
-// one after another on the stream), then the block's own buffers.
 // The block's workspace: the experts' grouped-MoE workspace (sub2, which the
 // router uses before them; at offset 0, so the router's arrival counter is in
 // the buffer's counter region), the dense layer's (sub1: the grouped-MoE
 // kernels use no counters, only scratch above the counter region, which needs
-// no zero-fill), then the normed inputs, the logits and the routings.  The
+// no zero-fill), then the normed inputs and the routings.  The
 // two expert layers' outputs stay in their own workspaces until the block's
 // combine reads them.
 struct BlockWs {
-  size_t sub2, sub1, h1, h2, logits, idx, w, didx, dw, total;
+  size_t sub2, sub1, h1, h2, idx, w, didx, dw, total;
 };
 static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 static BlockWs block_ws(const q4_moe_block_desc* b, int T, int k) {
@@ -797,7 +801,6 @@ static BlockWs block_ws(const q4_moe_block_desc* b, int T, int k) {
   L.sub1 = take(moe_workspace_bytes(&b->dense, T, 1));
   L.h1 = take(size_t(T) * D * 2);
   L.h2 = take(size_t(T) * D * 2);
-  L.logits = take(size_t(T) * E * 4);
   L.idx = take(size_t(T) * k * 4);
   L.w = take(size_t(T) * k * 4);
   L.didx = take(size_t(T) * 4);
@@ -851,7 +854,6 @@ int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k,
   float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + L.w);
   const void* h1 = base + L.h1;
   const void* h2 = base + L.h2;
-  float* logits = reinterpret_cast<float*>(base + L.logits);
   int32_t* didx = reinterpret_cast<int32_t*>(base + L.didx);
   float* dw = reinterpret_cast<float*>(base + L.dw);
   void* ws1 = base + L.sub1;
@@ -865,17 +867,14 @@ int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k,
   const float* o1 = reinterpret_cast<const float*>(static_cast<char*>(ws1) + o1_off);
   const float* o2 = reinterpret_cast<const float*>(static_cast<char*>(ws2) + o2_off);
   const int32_t* rowof2 = reinterpret_cast<const int32_t*>(static_cast<char*>(ws2) + r2_off);
-  // the router computes the logits only; the block's own router kernel
-  // normalizes them and takes the top-k (idx and w are not written by it)
-  if (int rc = route_check(__func__, h2, b->w_router, T, D, E, k, logits, idx, w, ws2, ws2_bytes)) return rc;
+  if (int rc = route_check(__func__, h2, b->w_router, T, D, E, k, nullptr, idx, w, ws2, ws2_bytes)) return rc;
   if (int rc = moe_check(__func__, &b->dense, h1, didx, dw, T, 1, residual, Q4_F32, ws1, ws1_bytes)) return rc;
   if (int rc = moe_check(__func__, &b->experts, h2, idx, w, T, k, residual, Q4_F32, ws2, ws2_bytes)) return rc;
   if (int e = launch_block_norm_in(residual, T, D, b->ffn_norm, b->pre_ffw_norm_2, b->eps, base + L.h1, base + L.h2,
                                    stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
-  if (int rc = route_enqueue(__func__, h2, b->w_router, T, D, E, k, 0, logits, idx, w, ws2, stream, false)) return rc;
-  if (int e = launch_block_router(logits, T, E, k, b->router_scale, b->down_scale, b->eps, idx, w, didx, dw, stream))
-    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  if (int rc = route_enqueue(__func__, h2, b->w_router, T, D, E, k, 0, nullptr, idx, w, ws2, stream, b, didx, dw))
+    return rc;
   if (int rc = moe_enqueue(__func__, &b->dense, h1, didx, dw, T, 1, residual, Q4_F32, ws1, stream, false)) return rc;
   if (int rc = moe_enqueue(__func__, &b->experts, h2, idx, w, T, k, residual, Q4_F32, ws2, stream, false)) return rc;
   if (int e = launch_block_combine(o1, o2, rowof2, k, T, D, b->post_ffw_norm_1, b->post_ffw_norm_2, b->post_ffw_norm,

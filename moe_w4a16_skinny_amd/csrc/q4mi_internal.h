@@ -41,6 +41,9 @@ Q4_HD inline int64_t packed_tail(int64_t K) { return has_half_tile(K) ? kTileByt
 Q4_HD inline int64_t packed_matrix_bytes(int64_t N, int64_t K) { return N / 16 * panel_bytes(K) + packed_tail(K); }
 
 enum Fmt { kNvfp4 = 0, kAffine = 1 };
+// kAffineBits + b: the b-bit affine widths (b = 2, 3, 5, 6, 8); tiles of
+// 256 b code bytes and 128 scale/bias bytes, K padded to whole tiles
+constexpr int kAffineBits = 16;
 
 // Workspace layout shared by every entry point, so that one zero-filled
 // buffer can serve all of them: the first kWsCounterBytes hold only counters
@@ -106,8 +109,6 @@ int launch_prefill(const GemmArgs& g, void* stream);
 // MoE block norms, router normalization and combine (q4mi_block.hip)
 int launch_block_norm_in(const float* res, int T, int D, const float* w1, const float* w2, float eps, void* h1,
                          void* h2, void* stream);
-int launch_block_router(const float* logits, int T, int E, int k, const float* scale, const float* down_scale,
-                        float eps, int32_t* idx, float* w, int32_t* didx, float* dw, void* stream);
 // o1: the dense branch's outputs [T][2][D] (slot 0), o2 and rowof2 the
 // experts' [T][k + 1][D] and [T][k] (grouped-MoE scratch layout)
 int launch_block_combine(const float* o1, const float* o2, const int32_t* rowof2, int k, int T, int D,
@@ -153,7 +154,15 @@ struct RouteArgs {
   float* logits;        // nullable [T][E]
   int32_t* idx;         // [T][k]
   float* w;             // [T][k]
-  int topk;             // 0: logits only (no top-k; idx and w unused)
+  // The MoE block's routing (zscale non-NULL): the top-k and softmax are
+  // taken over z = RMSNorm(logits; unit weights, eps) * zscale, the weights
+  // multiplied by down_scale[idx] (when non-NULL), and the dense branch's
+  // one-expert routing (expert 0, weight 1) written to didx, dw
+  const float* zscale;
+  const float* down_scale;
+  float eps;
+  int32_t* didx;
+  float* dw;
   float* partial;       // workspace [splits][T][E]
   unsigned* counter;    // workspace counter
   int nsplit;           // splits of D

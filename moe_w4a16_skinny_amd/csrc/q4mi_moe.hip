@@ -104,7 +104,7 @@ __device__ __forceinline__ float row_sum(float x) {
 // that expert; lane s keeps the round-s choice.  Softmax over all E with the
 // first choice as the maximum.
 template <int J>
-__device__ void route_topk_rows(const RouteArgs& r, const float* lg) {
+__device__ void route_topk_rows(const RouteArgs& r, const float* lg, const float* ds) {
   const int T = r.T, E = r.E;
   const int lane = threadIdx.x & 63, p = lane & 15;
   for (int t0 = (threadIdx.x >> 6) * 4; t0 < T; t0 += (blockDim.x >> 6) * 4) {
@@ -147,8 +147,29 @@ __device__ void route_topk_rows(const RouteArgs& r, const float* lg) {
     if (ok && p < r.k) {
       const float pr = pm / se;
       r.idx[t * r.k + p] = static_cast<int>(my_e);
-      r.w[t * r.k + p] = r.renormalize ? pr / (ws / se) : pr;
+      const float wv = r.renormalize ? pr / (ws / se) : pr;
+      r.w[t * r.k + p] = r.zscale ? wv * ds[my_e] : wv;  // the block's down scale (1 without one)
     }
+    if (ok && p == 0 && r.didx) {
+      r.didx[t] = 0;
+      r.dw[t] = 1.0f;
+    }
+  }
+}
+
+// The MoE block's router scores, in place over the [T][E] logits in LDS:
+// z = RMSNorm(row; unit weights, eps) * zs (the scales, in LDS), a wave per
+// token (sum of squares over lanes e = lane + 64 j, butterfly-reduced).
+__device__ void route_block_scores(const RouteArgs& r, float* lg, const float* zs) {
+  const int lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  for (int t = threadIdx.x >> 6; t < r.T; t += nw) {
+    float* row = lg + static_cast<size_t>(t) * r.E;
+    float ss = 0.f;
+    for (int e = lane; e < r.E; e += 64) ss = fmaf(row[e], row[e], ss);
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(r.E) + r.eps);
+    for (int e = lane; e < r.E; e += 64) row[e] = row[e] * inv * zs[e];
   }
 }
 
@@ -268,6 +289,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
   float* lg = xs;  // reuse: [T][E]
   const int ns = r.nsplit;
   const int TE = T * E;
+  // the block's scales of expert tid (E <= 256 = the workgroup's threads),
+  // loaded with the partials and parked in LDS after them
+  __shared__ float s_zs[kRouteThreads], s_ds[kRouteThreads];
+  float zs = 0.f, dsc = 1.0f;
+  if (r.zscale && tid < E) {
+    zs = r.zscale[tid];
+    if (r.down_scale) dsc = r.down_scale[tid];
+  }
   auto put = [&](int q, float v) {
     lg[q] = v;
     if (r.logits) r.logits[q] = v;
@@ -309,13 +338,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
       put(q, sum);
     }
   }
-  __syncthreads();
-  if (r.topk) {
-    if (E <= 128)
-      route_topk_rows<8>(r, lg);
-    else
-      route_topk_rows<16>(r, lg);
+  if (r.zscale) {
+    s_zs[tid] = zs;
+    s_ds[tid] = dsc;
   }
+  __syncthreads();
+  if (r.zscale) {
+    route_block_scores(r, lg, s_zs);
+    __syncthreads();
+  }
+  if (E <= 128)
+    route_topk_rows<8>(r, lg, s_ds);
+  else
+    route_topk_rows<16>(r, lg, s_ds);
   if (tid == 0) atomicExch(r.counter, 0u);
 }
 

@@ -1,9 +1,10 @@
 // NVFP4 W4A16 GEMM for more than 16 activation rows (prefill chunks and
 // large verify blocks): y[M][N] = g * a[M][K] . W[N][K]^T.
 //
-// [README] "Everything it has" / "Why it's fast": the FP4 weight GEMM of the
-// forward pass; with many rows the product is bound by the matrix cores, not
-// by the weight stream, so each dequantized weight fragment feeds several
+// [README, repository layout]: the engine runs a prefill beside decode;
+// [DOC 3.3 "Decode vs prefill"]: a prefill pushes many tokens through each
+// layer at once.  With many rows the product is bound by the matrix cores,
+// not by the weight stream, so each dequantized weight fragment feeds several
 // activation m-tiles and each activation fragment several weight panels.
 //
 // A workgroup of 4 waves computes a block of (16 WM MT) rows x (16 WN NP)

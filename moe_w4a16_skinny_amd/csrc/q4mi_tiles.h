@@ -156,11 +156,126 @@ __device__ __forceinline__ void stash(f32x4* wout, int g, const f32x4 (&acc)[P][
   for (int p = 0; p < P; ++p) wout[(g * P + p) * 64 + lane] = acc[p][0] + acc[p][1];
 }
 
+// Per-format tile layout, the registers one lane holds for a tile of one
+// panel, and the loads that fill them.  A half tile (K % 128 == 64) of the
+// NVFP4 and 4-bit affine layouts is packed on its own (8 code bytes a lane);
+// the b-bit widths pad K to whole tiles, so their last tile is loaded like
+// any other (the streaming code zeroes its activations past K).
+template <int FMT>
+struct Fm;
+template <>
+struct Fm<kNvfp4> {
+  using Codes = u32x4;
+  using Scales = unsigned;
+  using HalfCodes = u32x2;
+  static constexpr int kTile = kTileBytes;
+  __device__ static void load(Codes& c, Scales& s, const uint8_t* tb, int lane) {
+    c = ld_nt16(tb + lane * 16);
+    s = ld_nt4(tb + kTileCodeBytes + ((lane & 15) * 2 + (lane >> 5)) * 4);
+  }
+  __device__ static void load_half(HalfCodes& c, Scales& s, const uint8_t* tb, int lane) {
+    c = ld_nt8(tb + lane * 8);
+    s = ld_nt2(tb + kHalfCodeBytes + ((lane & 15) * 2 + (lane >> 5)) * 2);
+  }
+  __device__ static Codes widen(HalfCodes h) { return u32x4{h.x, h.y, 0u, 0u}; }
+  __device__ static unsigned first_word(const Codes& c) { return c.x; }  // of the tile's first load
+};
+template <>
+struct Fm<kAffine> {
+  using Codes = u32x4;
+  using Scales = u32x2;
+  using HalfCodes = u32x2;
+  static constexpr int kTile = kTileBytes;
+  __device__ static void load(Codes& c, Scales& s, const uint8_t* tb, int lane) {
+    c = ld_nt16(tb + lane * 16);
+    s = ld_nt8(tb + kTileCodeBytes + (lane & 15) * 8);
+  }
+  __device__ static void load_half(HalfCodes& c, Scales& s, const uint8_t* tb, int lane) {
+    c = ld_nt8(tb + lane * 8);
+    s = u32x2{ld_nt4(tb + kHalfCodeBytes + (lane & 15) * 4), 0u};  // 2nd group s = b = 0 adds 0
+  }
+  __device__ static Codes widen(HalfCodes h) { return u32x4{h.x, h.y, 0u, 0u}; }
+  __device__ static unsigned first_word(const Codes& c) { return c.x; }
+};
+// b-bit affine: lane (c, o) owns 4 b code bytes, the 32 codes of row c at
+// k = 32 i + 8 o + j as one little-endian bit stream (code (i, j) at bit
+// 8 b i + b j), loaded with the widest aligned loads; the scale/bias words
+// of row c's two groups at 8 c.
+template <int B>
+struct BitsCodes {
+  unsigned w[B];
+};
+template <int B>
+struct FmBits {
+  using Codes = BitsCodes<B>;
+  using Scales = u32x2;
+  using HalfCodes = Codes;
+  static constexpr int kTile = 256 * B + 128;
+  __device__ static void load(Codes& c, Scales& s, const uint8_t* tb, int lane) {
+    const uint8_t* p = tb + lane * 4 * B;
+    if constexpr (B % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < B / 4; ++j) {
+        const u32x4 v = ld_nt16(p + 16 * j);
+        c.w[4 * j] = v.x, c.w[4 * j + 1] = v.y, c.w[4 * j + 2] = v.z, c.w[4 * j + 3] = v.w;
+      }
+    } else if constexpr (B % 2 == 0) {
+#pragma unroll
+      for (int j = 0; j < B / 2; ++j) {
+        const u32x2 v = ld_nt8(p + 8 * j);
+        c.w[2 * j] = v.x, c.w[2 * j + 1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < B; ++j) c.w[j] = ld_nt4(p + 4 * j);
+    }
+    s = ld_nt8(tb + 256 * B + (lane & 15) * 8);
+  }
+  __device__ static void load_half(HalfCodes& c, Scales& s, const uint8_t* tb, int lane) { load(c, s, tb, lane); }
+  __device__ static Codes widen(HalfCodes h) { return h; }
+  __device__ static unsigned first_word(const Codes& c) { return c.w[0]; }
+  // code j of MFMA step i
+  __device__ static unsigned code(const Codes& c, int i, int j) {
+    const int p = 8 * B * i + B * j;
+    const int wd = p >> 5, sh = p & 31;
+    unsigned v = c.w[wd] >> sh;
+    if (sh + B > 32) v |= c.w[wd + 1] << (32 - sh);
+    return v & ((1u << B) - 1u);
+  }
+};
+template <>
+struct Fm<kAffineBits + 2> : FmBits<2> {};
+template <>
+struct Fm<kAffineBits + 3> : FmBits<3> {};
+template <>
+struct Fm<kAffineBits + 5> : FmBits<5> {};
+template <>
+struct Fm<kAffineBits + 6> : FmBits<6> {};
+template <>
+struct Fm<kAffineBits + 8> : FmBits<8> {};
+
+// 8 values (128 + x_j) as bf16, x_j < 128, element j = k offset j (exact)
+__device__ __forceinline__ bf16x8 bf16_128_plus(const unsigned (&x)[8]) {
+  u32x4 r;
+  r.x = (x[0] | 0x4300u) | ((x[1] | 0x4300u) << 16);
+  r.y = (x[2] | 0x4300u) | ((x[3] | 0x4300u) << 16);
+  r.z = (x[4] | 0x4300u) | ((x[5] | 0x4300u) << 16);
+  r.w = (x[6] | 0x4300u) | ((x[7] | 0x4300u) << 16);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // One MFMA tile step: P panels of codes/scales in `c`/`s`, activation
 // operands a[0..3] (the four 32-k steps of the tile).
+// Affine widths: a code q < 128 becomes the exact bf16 128 + q, so that
+// sum_k a (128 + q) runs on the bf16 MFMA and the group sum sum_k a on the
+// same MFMA against ones; per group of 64
+//   sum_k a w = s sum a (128 + q) + (b - 128 s) sum a,
+// and for 8-bit codes, split into nibbles q = 16 qh + ql on two MFMAs,
+//   sum_k a w = s (16 sum a (128 + qh) + sum a (128 + ql)) + (b - 2176 s) sum a.
 template <int FMT, int P>
-__device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4], const u32x4 (&c)[P],
-                                          const typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type (&s)[P]) {
+__device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4],
+                                          const typename Fm<FMT>::Codes (&c)[P],
+                                          const typename Fm<FMT>::Scales (&s)[P]) {
   if constexpr (FMT == kNvfp4) {
     f16x2 sv[P][2];
 #pragma unroll
@@ -182,13 +297,48 @@ __device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4
     as1 = mfma_bf16(a[3], ones, as1);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      f32x4 q0 = mfma_bf16(a[0], affine_operand(c[p][0]), z);
-      q0 = mfma_bf16(a[1], affine_operand(c[p][1]), q0);
-      f32x4 q1 = mfma_bf16(a[2], affine_operand(c[p][2]), z);
-      q1 = mfma_bf16(a[3], affine_operand(c[p][3]), q1);
+      f32x4 q0, q1;
+      float off = -128.0f;  // the 128 (16 * 128 + 128 for split 8-bit codes) under each code
+      if constexpr (FMT == kAffine) {
+        q0 = mfma_bf16(a[0], affine_operand(c[p][0]), z);
+        q0 = mfma_bf16(a[1], affine_operand(c[p][1]), q0);
+        q1 = mfma_bf16(a[2], affine_operand(c[p][2]), z);
+        q1 = mfma_bf16(a[3], affine_operand(c[p][3]), q1);
+      } else if constexpr (FMT == kAffineBits + 8) {
+        f32x4 h[2] = {z, z}, l[2] = {z, z};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          unsigned xh[8], xl[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const unsigned v = Fm<FMT>::code(c[p], i, j);
+            xh[j] = v >> 4;
+            xl[j] = v & 15u;
+          }
+          h[i >> 1] = mfma_bf16(a[i], bf16_128_plus(xh), h[i >> 1]);
+          l[i >> 1] = mfma_bf16(a[i], bf16_128_plus(xl), l[i >> 1]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          q0[r] = fmaf(16.0f, h[0][r], l[0][r]);
+          q1[r] = fmaf(16.0f, h[1][r], l[1][r]);
+        }
+        off = -2176.0f;
+      } else {
+        f32x4 q[2] = {z, z};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          unsigned x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = Fm<FMT>::code(c[p], i, j);
+          q[i >> 1] = mfma_bf16(a[i], bf16_128_plus(x), q[i >> 1]);
+        }
+        q0 = q[0];
+        q1 = q[1];
+      }
       const float s0 = bf16_lo(s[p].x), b0 = bf16_hi(s[p].x);
       const float s1 = bf16_lo(s[p].y), b1 = bf16_hi(s[p].y);
-      const float c0 = fmaf(-128.0f, s0, b0), c1 = fmaf(-128.0f, s1, b1);
+      const float c0 = fmaf(off, s0, b0), c1 = fmaf(off, s1, b1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = acc[p][0][r];
@@ -220,8 +370,8 @@ enum AMode { kAStaged = 0, kARing = 1, kAGlobal = 2, kAStagedRows = 3 };
 
 template <int FMT, int P, int AM>
 struct StreamStage {
-  u32x4 c[P];
-  typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type s[P];
+  typename Fm<FMT>::Codes c[P];
+  typename Fm<FMT>::Scales s[P];
   u32x4 a[AM == kAGlobal ? 4 : 1];
   unsigned arow;  // kAStagedRows: LDS byte offset of this lane's staged row for this tile
 };
@@ -468,25 +618,15 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
     const int tg = kt0 + t;
     load_a(st, gp, tg, d);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const uint8_t* tb = gp.panel[p] + static_cast<size_t>(tg) * kTileBytes;
-      st.c[p] = ld_nt16(tb + lane * 16);
-      if constexpr (FMT == kNvfp4)
-        st.s[p] = ld_nt4(tb + kTileCodeBytes + (c * 2 + (lane >> 5)) * 4);
-      else
-        st.s[p] = ld_nt8(tb + kTileCodeBytes + c * 8);
-    }
+    for (int p = 0; p < P; ++p)
+      Fm<FMT>::load(st.c[p], st.s[p], gp.panel[p] + static_cast<size_t>(tg) * Fm<FMT>::kTile, lane);
   };
   auto load_half_w = [&](St& st, const GroupPtrs<P>& gp) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const uint8_t* tb = gp.panel[p] + static_cast<size_t>(half_t) * kTileBytes;
-      const u32x2 cc = ld_nt8(tb + lane * 8);
-      st.c[p] = u32x4{cc.x, cc.y, 0u, 0u};
-      if constexpr (FMT == kNvfp4)
-        st.s[p] = ld_nt2(tb + kHalfCodeBytes + (c * 2 + (lane >> 5)) * 2);
-      else
-        st.s[p] = u32x2{ld_nt4(tb + kHalfCodeBytes + c * 4), 0u};  // 2nd group s = b = 0 adds 0
+      typename Fm<FMT>::HalfCodes hc;
+      Fm<FMT>::load_half(hc, st.s[p], gp.panel[p] + static_cast<size_t>(half_t) * Fm<FMT>::kTile, lane);
+      st.c[p] = Fm<FMT>::widen(hc);
     }
   };
   auto load_half = [&](St& st, const GroupPtrs<P>& gp, int d) {
@@ -526,7 +666,7 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
       for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(pa + i * 64);
     } else if constexpr (AM == kARing) {
       unsigned off = static_cast<unsigned>(d * kRingSlot);
-      asm volatile("" : "+v"(off) : "v"(x.c[0].x));
+      asm volatile("" : "+v"(off) : "v"(Fm<FMT>::first_word(x.c[0])));
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = *(const lds_u32x4*)(static_cast<size_t>(ring.rd[i] + off));
     } else {
@@ -566,21 +706,18 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   // every load of the stream, these loads leave the stream's waits exact.
   const bool pre_half = has_half && AM != kARing;
   struct HalfW {
-    u32x2 c[P];
-    typename std::conditional<FMT == kNvfp4, unsigned, u32x2>::type s[P];
+    typename Fm<FMT>::HalfCodes c[P];
+    typename Fm<FMT>::Scales s[P];
   } hpre[D];
   if (pre_half) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       GroupPtrs<P> hp;
       group(d, hp);
-      St tmp;
-      load_half_w(tmp, hp);
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        hpre[d].c[p] = u32x2{tmp.c[p].x, tmp.c[p].y};
-        hpre[d].s[p] = tmp.s[p];
-      }
+      for (int p = 0; p < P; ++p)
+        Fm<FMT>::load_half(hpre[d].c[p], hpre[d].s[p], hp.panel[p] + static_cast<size_t>(half_t) * Fm<FMT>::kTile,
+                           lane);
     }
   }
   pre_issue();
@@ -630,7 +767,7 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
             load_a_half(st[d], hp, d);
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-              st[d].c[p] = u32x4{hpre[d].c[p].x, hpre[d].c[p].y, 0u, 0u};
+              st[d].c[p] = Fm<FMT>::widen(hpre[d].c[p]);
               st[d].s[p] = hpre[d].s[p];
             }
           } else {

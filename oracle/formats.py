@@ -109,8 +109,8 @@ def affine_dequant_bits(codes: np.ndarray, scale_bits: np.ndarray, bias_bits: np
     """Affine b-bit codes, one per byte [N][K] (values < 2^b), with bf16
     scale/bias [N][K/64] -> float64 q * s + b, per 64-value group.
 
-    [README "Everything it has": MLX affine weights; the widths 2, 3, 4, 5, 6
-    and 8 bits in groups of 64].  Exact in float64 for the same reason as the
+    [ISSUE "Why now": qlinear's MLX affine paths at 4 bits and at 2, 3, 5, 6
+    and 8 bits, in groups of 64; "Steps" 3 and 9: the other MLX widths].  Exact in float64 for the same reason as the
     4-bit form (q < 2^8 times an 8-significant-bit bf16, plus a bf16)."""
     if bits not in AFFINE_BITS:
         raise ValueError(f"bits must be one of {AFFINE_BITS}")
