@@ -598,9 +598,9 @@ static int moe_check(const char* fn, const q4_moe_desc* w, const void* x, const 
   return Q4_OK;
 }
 
-static int moe_enqueue(const char* fn, const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
-                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws, void* stream,
-                       bool combine = true) {
+// The kernels' view of one grouped layer over workspace ws.
+static MoeArgs moe_args(const q4_moe_desc* w, const void* x, const int32_t* topk_idx, const float* topk_w, int T,
+                        int k, void* y, int out_dtype, void* ws, bool combine) {
   size_t h_off, o_off, r_off, g_off;
   (void)moe_ws_layout(w, T, k, &h_off, &o_off, &r_off, &g_off);
   MoeArgs m{};
@@ -630,7 +630,14 @@ static int moe_enqueue(const char* fn, const q4_moe_desc* w, const void* x, cons
   m.rowof = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + r_off);
   m.grp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + g_off);
   m.combine = combine ? 1 : 0;
-  if (int e = launch_moe(m, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
+  return m;
+}
+
+static int moe_enqueue(const char* fn, const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
+                       const float* topk_w, int T, int k, void* y, int out_dtype, void* ws, void* stream) {
+  const MoeArgs m = moe_args(w, x, topk_idx, topk_w, T, k, y, out_dtype, ws, true);
+  if (int e = launch_moe(m, nullptr, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
   return Q4_OK;
 }
 
@@ -875,8 +882,11 @@ int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k,
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   if (int rc = route_enqueue(__func__, h2, b->w_router, T, D, E, k, 0, nullptr, idx, w, ws2, stream, b, didx, dw))
     return rc;
-  if (int rc = moe_enqueue(__func__, &b->dense, h1, didx, dw, T, 1, residual, Q4_F32, ws1, stream, false)) return rc;
-  if (int rc = moe_enqueue(__func__, &b->experts, h2, idx, w, T, k, residual, Q4_F32, ws2, stream, false)) return rc;
+  // the experts and the dense branch share the gate/up and the down launch
+  const MoeArgs me = moe_args(&b->experts, h2, idx, w, T, k, residual, Q4_F32, ws2, false);
+  const MoeArgs md = moe_args(&b->dense, h1, didx, dw, T, 1, residual, Q4_F32, ws1, false);
+  if (int e = launch_moe(me, &md, stream))
+    return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   if (int e = launch_block_combine(o1, o2, rowof2, k, T, D, b->post_ffw_norm_1, b->post_ffw_norm_2, b->post_ffw_norm,
                                    b->eps, residual, stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);

@@ -191,12 +191,19 @@ struct MoeArgs {
   int32_t* grp;            // workspace: the expert grouping, written by gate/up, read by down
   int combine;             // 1: a third launch sums each token's slots into y
 };
+// The layers of one grouped launch (the second only for two-layer launches).
+struct MoeLayers {
+  MoeArgs l[2];
+};
 // the grouping table in the workspace (int32 words): nact, then act, cnt and
 // base [E + 1] each, then tok and slot as int16 [T k + T] each
 inline size_t moe_grp_words(int E, int T, int k) {
   return 4 + 3 * (static_cast<size_t>(E) + 1) + static_cast<size_t>(T) * (k + 1);
 }
-int launch_moe(const MoeArgs& m, void* stream);
+// One layer (m1 NULL: gate/up, down and, if m0.combine, the combine), or
+// two layers of equal T and D sharing the gate/up and the down launch (no
+// combine): the MoE block's experts (m0) and dense branch (m1).
+int launch_moe(const MoeArgs& m0, const MoeArgs* m1, void* stream);
 // The per-device scratch array of moe_grouped_qgemm_noalloc (q4mi_moe.hip):
 // its device address on the current device (looked up once per device) and
 // its size.  Returns hipError_t as int.

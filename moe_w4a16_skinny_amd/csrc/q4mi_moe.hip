@@ -623,6 +623,17 @@ __device__ __forceinline__ int items_of_wave(int nitems, int gw, int NW) {
   return gw < nitems ? (nitems - gw + NW - 1) / NW : 0;
 }
 
+// Two layers in one launch: the workgroups of the first layer, in proportion
+// to the tile-items of each (the first layer's from its active experts, u0
+// per expert; w1 for the second), at least one each.  Every workgroup
+// computes the same value from the same grouping.
+__device__ __forceinline__ int layer_split(int nact0, int u0, int w1) {
+  const long long w0 = static_cast<long long>(nact0) * u0;
+  const long long n = gridDim.x;
+  const long long sp = (n * w0 + (w0 + w1) / 2) / (w0 + w1 > 0 ? w0 + w1 : 1);
+  return static_cast<int>(sp < 1 ? 1 : (sp > n - 1 ? n - 1 : sp));
+}
+
 // ------------------------------------------------------------------ gate/up
 
 // Item (active expert a, panel pair j): gate panel j and up panel j of the
@@ -636,11 +647,46 @@ __device__ __forceinline__ int items_of_wave(int nitems, int gw, int NW) {
 // each item to a whole workgroup, its W waves streaming W consecutive
 // ranges of the K tiles; the waves' partial sums meet in LDS and are added
 // in wave order before the epilogue.  Otherwise an item is one wave's.
-template <int W, int DP, int AM, bool KS>
-__global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW) {
+// TWO: two layers share the launch (the MoE block's experts and its dense
+// branch): workgroups below `split` run layer L.l[0], the others L.l[1],
+// each set dealing its own layer's items among its own workgroups (bid of
+// nwg).
+template <int W, int DP, int AM, bool KS, bool TWO>
+__global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeLayers L, int u0, int w1, int ngw0, int ngw1) {
   __shared__ MoeGroups G;
-  build_groups(m, G);
-  if (blockIdx.x == 0) {  // the pair -> row map, for the combine; the grouping, for down
+  extern __shared__ f32x4 gu_dyn[];
+  auto stage_x = [&](const MoeArgs& mm) {
+    if constexpr (AM == kAStagedRows) {
+      const int ntx = static_cast<int>(full_tiles(mm.D) + (has_half_tile(mm.D) ? 1 : 0));
+      stage_issue(stage_geom(mm.x, mm.T, mm.D, 0, ntx), reinterpret_cast<u32x4*>(gu_dyn));
+    }
+  };
+  int r = 0, split = static_cast<int>(gridDim.x);
+  if constexpr (TWO) {
+    // the split follows the first layer's active experts; the second
+    // layer's workgroups then build their own grouping and stage their x,
+    // which has landed at the barrier below
+    build_groups(L.l[0], G);
+    split = layer_split(G.nact, u0, w1);
+    r = static_cast<int>(blockIdx.x) >= split ? 1 : 0;
+    if (r) {
+      __syncthreads();
+      build_groups(L.l[1], G);
+    }
+    stage_x(L.l[r]);
+    __syncthreads();
+  } else {
+    // x is staged first, its loads in flight while the grouping's own loads
+    // (topk_idx, the global scales) make their round trip; the grouping's
+    // first barrier waits for both
+    stage_x(L.l[0]);
+    build_groups(L.l[0], G);
+  }
+  const MoeArgs& m = L.l[r];  // (a uniform index into the kernel arguments: one load per field)
+  const int bid = static_cast<int>(blockIdx.x) - (r ? split : 0);
+  const int nwg = r ? static_cast<int>(gridDim.x) - split : split;
+  const int NGW = r ? ngw1 : ngw0;
+  if (bid == 0) {  // the pair -> row map, for the combine; the grouping, for down
     for (int q = threadIdx.x; q < m.T * m.k; q += blockDim.x) m.rowof[q] = G.rowof[q];
     publish_groups(m, G);
   }
@@ -650,8 +696,8 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
   const int npp = m.F / 16;
   const int nitems = G.nact * npp;
   // the item dealer: a wave (gw of NW), or with KS the whole workgroup
-  const int gw = KS ? static_cast<int>(blockIdx.x) : blockIdx.x + gridDim.x * w;
-  const int NW = KS ? static_cast<int>(gridDim.x) : gridDim.x * W;
+  const int gw = KS ? bid : bid + nwg * w;
+  const int NW = KS ? nwg : nwg * W;
   // a wave's items go in chunks of at most NGW (its stash slots)
   const int ntot = items_of_wave(nitems, gw, NW);
   if (KS && ntot == 0) return;  // the whole workgroup idle
@@ -688,22 +734,10 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
     }
   };
   // dynamic LDS: [staged x (kAStagedRows)] then the stash [W][NGW][2 panels][64 lanes]
-  extern __shared__ f32x4 gu_dyn[];
   char* const dyn = reinterpret_cast<char*>(gu_dyn);
   const size_t xbytes = AM == kAStagedRows ? (static_cast<size_t>(stage_bytes(m.T, ntx)) + 15) / 16 * 16 : 0;
   f32x4* wout = reinterpret_cast<f32x4*>(dyn + xbytes) + static_cast<size_t>(w) * NGW * 2 * 64;
   const ALds al{dyn + 16 * o};
-  const StageGeom sg = stage_geom(m.x, m.T, m.D, 0, ntx);
-  // the first chunk's stream stages x (every wave enters it, possibly with no
-  // item, so all reach the staging barrier); it is a separate instance so
-  // that the staging and its wait are unconditional and the compiler's
-  // waits in the later streams know the staging has landed
-  auto stage_pre_issue = [&] {
-    if constexpr (AM == kAStagedRows) stage_issue(sg, reinterpret_cast<u32x4*>(gu_dyn));
-  };
-  auto stage_pre = [&] {
-    if constexpr (AM == kAStagedRows) stage_wait<DP * 2 * 2>();  // the prologue's D tiles of 2 panels: codes + scales
-  };
   auto none = [] {};
   auto epi = [&](int gi, f32x4 (&acc)[2][2]) { stash<2>(wout, gi, acc); };
   auto epi_add = [&](int gi, f32x4 (&acc)[2][2]) { stash_add<2>(wout, gi, acc); };
@@ -736,11 +770,6 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
     if constexpr (KS) __syncthreads();  // the stash is free for the next chunk
     c0 += NGW;
   };
-  if (nitems == 0) return;  // no item at all: nothing to stage or compute
-  ng = min(NGW, ntot);
-  stream_groups<kNvfp4, 2, DP, AM>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.D, group, stage_pre_issue,
-                                   stage_pre, epi, epi_add);
-  finish();
   while (c0 < ntot) {
     ng = min(NGW, ntot - c0);
     stream_groups<kNvfp4, 2, DP, AM>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.D, group, none, none, epi,
@@ -755,10 +784,27 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeArgs m, int NGW)
 // activation rows are the expert's contiguous h rows; o[row][n] = w_pair *
 // g_down * acc in fp32.  KS: every item of the workgroup's range is streamed
 // by all W waves, each over its own range of the K tiles, as in gate/up.
-template <int P, int W, int DP, bool KS>
-__global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, int stage_room) {
+// TWO as in gate/up; lds is the launch's dynamic LDS size.
+template <int P, int W, int DP, bool KS, bool TWO>
+__global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeLayers L, int u0, int w1, int ngw0, int ngw1,
+                                                          int lds) {
   __shared__ MoeDownTable G;
-  fetch_groups(m, G);
+  fetch_groups(L.l[0], G);
+  int r = 0, split = static_cast<int>(gridDim.x);
+  if constexpr (TWO) {  // the split as in gate/up, then the second layer's table
+    split = layer_split(G.nact, u0, w1);
+    r = static_cast<int>(blockIdx.x) >= split ? 1 : 0;
+    if (r) {
+      __syncthreads();
+      fetch_groups(L.l[1], G);
+    }
+  }
+  const MoeArgs& m = L.l[r];
+  const int bid = static_cast<int>(blockIdx.x) - (r ? split : 0);
+  const int nwg = r ? static_cast<int>(gridDim.x) - split : split;
+  const int NGW = r ? ngw1 : ngw0;
+  // the rest of the dynamic LDS past the stash holds the staged h rows
+  const int stage_room = lds - W * NGW * P * 64 * 16;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = lane >> 4, c = lane & 15;
@@ -767,8 +813,8 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, in
   const int nitems = G.nact * ngp;
   // the workgroup's items: a contiguous range (one or two experts' panel
   // groups), dealt round-robin to its waves
-  const int i0 = static_cast<int>((static_cast<long long>(blockIdx.x) * nitems) / gridDim.x);
-  const int i1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * nitems) / gridDim.x);
+  const int i0 = static_cast<int>((static_cast<long long>(bid) * nitems) / nwg);
+  const int i1 = static_cast<int>((static_cast<long long>(bid + 1) * nitems) / nwg);
   if (i1 <= i0) return;  // no item for this workgroup (uniform)
   // items of this wave (all of the range with KS), in chunks of at most NGW, as in gate/up
   const int ntot = KS ? i1 - i0 : (i1 - i0 > w ? (i1 - i0 - w + W - 1) / W : 0);
@@ -864,13 +910,13 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeArgs m, int NGW, in
     };
     auto none = [] {};
     ng = min(NGW, ntot);
-    stream_groups<kNvfp4, P, DP, AM>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group, stage_pre_issue,
-                                     stage_pre, epi, epi_add);
+    stream_groups<kNvfp4, P, DP, AM, true>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group,
+                                           stage_pre_issue, stage_pre, epi, epi_add);
     finish();
     while (c0 < ntot) {
       ng = min(NGW, ntot - c0);
-      stream_groups<kNvfp4, P, DP, AM>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group, none, none, epi,
-                                       epi_add);
+      stream_groups<kNvfp4, P, DP, AM, true>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group, none, none,
+                                             epi, epi_add);
       finish();
     }
   };
@@ -952,81 +998,142 @@ int launch_route(const RouteArgs& r, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-template <int W, bool KS>
-const void* gate_up_fn(bool staged) {
-  return staged ? reinterpret_cast<const void*>(&moe_gate_up_kernel<W, 4, kAStagedRows, KS>)
-                : reinterpret_cast<const void*>(&moe_gate_up_kernel<W, 4, kAGlobal, KS>);
+namespace {
+constexpr int GU_W = 8, DN_P = 2, DN_W = 8, kWG = 256;  // one 8-wave workgroup per CU
+
+// Shapes of one layer's two launches.
+struct MoeShape {
+  int nact_max;  // experts that can be active: one per routed pair at most, plus the shared one
+  int npp, ngp;  // gate/up items (panel pairs) and down items (groups of DN_P panels) per expert
+  int ntx, ntf;  // K tiles of gate/up (K = D) and of down (K = F)
+};
+MoeShape moe_shape(const MoeArgs& m) {
+  MoeShape h;
+  h.nact_max = std::min(m.E, m.T * m.k) + m.has_shared;
+  h.npp = m.F / 16;
+  h.ngp = (m.D / 16 + DN_P - 1) / DN_P;
+  h.ntx = static_cast<int>(full_tiles(m.D) + (has_half_tile(m.D) ? 1 : 0));
+  h.ntf = static_cast<int>(full_tiles(m.F) + (has_half_tile(m.F) ? 1 : 0));
+  return h;
+}
+// workgroups of kWG for the first of two layers, in proportion to their
+// tile-items (at least one each), with every expert of the first active
+int split_of(int64_t w0, int64_t w1) {
+  const int64_t s = (kWG * w0 + (w0 + w1) / 2) / (w0 + w1);
+  return static_cast<int>(std::min<int64_t>(kWG - 1, std::max<int64_t>(1, s)));
 }
 
-int launch_moe(const MoeArgs& m, void* stream) {
+template <int AM, bool KS, bool TWO>
+int launch_gu(const MoeLayers& L, int u0, int w1, int ngw0, int ngw1, size_t lds, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(&moe_gate_up_kernel<GU_W, 4, AM, KS, TWO>);
+  if (int e = ensure_dynamic_lds(fn, lds)) return e;
+  hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, AM, KS, TWO>), dim3(kWG), dim3(64 * GU_W), lds, s, L, u0, w1, ngw0,
+                     ngw1);
+  return static_cast<int>(hipGetLastError());
+}
+template <bool KS, bool TWO>
+int launch_dn(const MoeLayers& L, int u0, int w1, int ngw0, int ngw1, size_t lds, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4, KS, TWO>);
+  if (int e = ensure_dynamic_lds(fn, lds)) return e;
+  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4, KS, TWO>), dim3(kWG), dim3(64 * DN_W), lds, s, L, u0, w1, ngw0,
+                     ngw1, static_cast<int>(lds));
+  return static_cast<int>(hipGetLastError());
+}
+}  // namespace
+
+// One layer (m1 NULL), or two layers sharing each launch (m1: the MoE
+// block's dense branch, which has the experts' T and D); no combine launch
+// with two.
+int launch_moe(const MoeArgs& m0, const MoeArgs* m1, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  constexpr int GU_W = 8, DN_P = 2, DN_W = 8, kWG = 256;  // one 8-wave workgroup per CU
-  const int gu_nw = kWG * GU_W, dn_nw = kWG * DN_W;  // waves in the grid
-  // experts that can be active: at most one per routed pair, plus the shared one
-  const int nact_max = std::min(m.E, m.T * m.k) + m.has_shared;
-  const int npp = m.F / 16;
-  const int ngp = (m.D / 16 + DN_P - 1) / DN_P;
-  const int ntx = static_cast<int>(full_tiles(m.D) + (has_half_tile(m.D) ? 1 : 0));
-  const int ntf = static_cast<int>(full_tiles(m.F) + (has_half_tile(m.F) ? 1 : 0));
-  // K split over a workgroup's waves when the layer has too few items to give
-  // every CU's waves one each (at least one K tile per wave)
-  const bool gu_ks = nact_max * npp <= 2 * kWG && ntx >= GU_W;
-  const bool dn_ks = nact_max * ngp <= 2 * kWG && ntf >= DN_W;
+  const bool two = m1 != nullptr;
+  const MoeArgs& mb = two ? *m1 : m0;
+  const MoeShape h0 = moe_shape(m0), h1 = moe_shape(mb);
+  // workgroups per layer: all of them for one layer
+  const int gu_split = two ? split_of(int64_t(h0.nact_max) * h0.npp * h0.ntx, int64_t(h1.nact_max) * h1.npp * h1.ntx)
+                           : kWG;
+  const int dn_split = two ? split_of(int64_t(h0.nact_max) * h0.ngp * h0.ntf, int64_t(h1.nact_max) * h1.ngp * h1.ntf)
+                           : kWG;
+  // K split over a workgroup's waves when a lone layer has too few items to
+  // give every CU's waves one each (at least one K tile per wave)
+  const bool gu_ks = !two && h0.nact_max * h0.npp <= 2 * kWG && h0.ntx >= GU_W;
+  const bool dn_ks = !two && h0.nact_max * h0.ngp <= 2 * kWG && h0.ntf >= DN_W;
   // stash slots per wave (items parked until the wave's stream ends): as many
   // as a wave has items at most, up to what 96 KiB of LDS holds; a wave with
   // more items streams them in chunks of that many
   constexpr size_t kStashLds = 96 * 1024;
+  auto need = [](int items, int units) { return (items + units - 1) / units; };
   const int gu_cap = static_cast<int>(kStashLds / (size_t(GU_W) * 2 * 64 * 16));
-  const int gu_need = gu_ks ? (nact_max * npp + kWG - 1) / kWG : (nact_max * npp + gu_nw - 1) / gu_nw;
-  int gu_ngw = std::min(gu_need, gu_cap);
-  size_t gu_lds = static_cast<size_t>(GU_W) * gu_ngw * 2 * 64 * 16;
+  int gu_need0, gu_need1 = 1;
+  if (gu_ks) {
+    gu_need0 = need(h0.nact_max * h0.npp, kWG);
+  } else {
+    // (with two layers the device gives the first layer about kWG w0 / (w0 +
+    // w1) workgroups for its w0 actual tile-items, so that a wave of it has
+    // at most about (w0 + w1) / (kWG W) tile-items, w0 at its largest; the
+    // second layer has the fewest workgroups when all experts are active)
+    gu_need0 = two ? need((h0.nact_max * h0.npp * h0.ntx + h1.nact_max * h1.npp * h1.ntx) / h0.ntx, kWG * GU_W) + 1
+                   : need(h0.nact_max * h0.npp, gu_split * GU_W);
+    if (two) gu_need1 = need(h1.nact_max * h1.npp, (kWG - gu_split) * GU_W) + 1;
+  }
+  int gu_ngw0 = std::min(gu_need0, gu_cap), gu_ngw1 = std::min(gu_need1, gu_cap);
+  size_t gu_lds = static_cast<size_t>(GU_W) * std::max(gu_ngw0, gu_ngw1) * 2 * 64 * 16;
   // gate/up stages x in LDS when it fits beside the grouping table and a
   // stash of at least one item per wave (a wave with more items than slots
   // streams them in chunks); with the K split each wave reads only its range
   // of x, from global memory
-  const size_t xbytes = (static_cast<size_t>(stage_bytes(m.T, ntx)) + 15) / 16 * 16;
+  const size_t xbytes = (static_cast<size_t>(stage_bytes(std::max(m0.T, mb.T), std::max(h0.ntx, h1.ntx))) + 15) /
+                        16 * 16;
   const size_t lds_total = 160 * 1024;
   const size_t slot = static_cast<size_t>(GU_W) * 2 * 64 * 16;
   const size_t room = lds_total > sizeof(MoeGroups) + xbytes ? lds_total - sizeof(MoeGroups) - xbytes : 0;
   const bool gu_staged = !gu_ks && room >= slot;
   if (gu_staged) {
-    gu_ngw = std::min(gu_need, static_cast<int>(room / slot));
-    gu_lds = xbytes + static_cast<size_t>(gu_ngw) * slot;
+    gu_ngw0 = std::min(gu_need0, static_cast<int>(room / slot));
+    gu_ngw1 = std::min(gu_need1, static_cast<int>(room / slot));
+    gu_lds = xbytes + static_cast<size_t>(std::max(gu_ngw0, gu_ngw1)) * slot;
   }
   const int dn_cap = static_cast<int>(kStashLds / (size_t(DN_W) * DN_P * 64 * 16));
-  const int dn_need = dn_ks ? (nact_max * ngp + kWG - 1) / kWG : (nact_max * ngp + dn_nw - 1) / dn_nw;
-  const int dn_ngw = std::min(dn_need, dn_cap);
-  // the rest of the CU's LDS holds a workgroup's staged h rows (a workgroup
-  // whose rows do not fit reads them from global memory)
-  const size_t dn_stash = static_cast<size_t>(DN_W) * dn_ngw * DN_P * 64 * 16;
+  int dn_need0, dn_need1 = 1;
+  if (dn_ks) {
+    dn_need0 = need(h0.nact_max * h0.ngp, kWG);
+  } else {
+    dn_need0 = two ? need((h0.nact_max * h0.ngp * h0.ntf + h1.nact_max * h1.ngp * h1.ntf) / h0.ntf, kWG * DN_W) + 1
+                   : need(h0.nact_max * h0.ngp, dn_split * DN_W);
+    if (two) dn_need1 = need(h1.nact_max * h1.ngp, (kWG - dn_split) * DN_W) + 1;
+  }
+  const int dn_ngw0 = std::min(dn_need0, dn_cap), dn_ngw1 = std::min(dn_need1, dn_cap);
+  // the CU's LDS past the table: each role's stash, then its workgroup's
+  // staged h rows (a workgroup whose rows do not fit reads them from global
+  // memory)
   const size_t dn_fixed = sizeof(MoeDownTable) + 512;  // the table and the kernel's other static LDS
-  const size_t dn_room = 160 * 1024 > dn_fixed + dn_stash ? 160 * 1024 - dn_fixed - dn_stash : 0;
-  const size_t dn_lds = dn_stash + dn_room;
-  if (gu_ngw < 1 || dn_ngw < 1) return static_cast<int>(hipErrorInvalidConfiguration);
-  const void* gu_fn = gu_ks ? gate_up_fn<GU_W, true>(gu_staged) : gate_up_fn<GU_W, false>(gu_staged);
-  const void* dn_fn = dn_ks ? reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4, true>)
-                            : reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4, false>);
-  if (int e = ensure_dynamic_lds(gu_fn, gu_lds)) return e;
-  if (int e = ensure_dynamic_lds(dn_fn, dn_lds)) return e;
+  const size_t dn_lds = 160 * 1024 - dn_fixed;
+  if (gu_ngw0 < 1 || gu_ngw1 < 1 || dn_ngw0 < 1 || dn_ngw1 < 1) return static_cast<int>(hipErrorInvalidConfiguration);
+  MoeLayers L;
+  L.l[0] = m0;
+  L.l[1] = mb;
+  // the two-layer split is taken on the device from the first layer's
+  // active experts: tile-items per active expert, and the second layer's
+  const int gu_u0 = h0.npp * h0.ntx, gu_w1 = h1.nact_max * h1.npp * h1.ntx;
+  const int dn_u0 = h0.ngp * h0.ntf, dn_w1 = h1.nact_max * h1.ngp * h1.ntf;
+  int e;
   if (gu_ks)
-    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAGlobal, true>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m,
-                       gu_ngw);
-  else if (gu_staged)
-    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAStagedRows, false>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m,
-                       gu_ngw);
+    e = launch_gu<kAGlobal, true, false>(L, gu_u0, gu_w1, gu_ngw0, gu_ngw1, gu_lds, s);
+  else if (two)
+    e = gu_staged ? launch_gu<kAStagedRows, false, true>(L, gu_u0, gu_w1, gu_ngw0, gu_ngw1, gu_lds, s)
+                  : launch_gu<kAGlobal, false, true>(L, gu_u0, gu_w1, gu_ngw0, gu_ngw1, gu_lds, s);
   else
-    hipLaunchKernelGGL((moe_gate_up_kernel<GU_W, 4, kAGlobal, false>), dim3(kWG), dim3(64 * GU_W), gu_lds, s, m,
-                       gu_ngw);
-  if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
+    e = gu_staged ? launch_gu<kAStagedRows, false, false>(L, gu_u0, gu_w1, gu_ngw0, gu_ngw1, gu_lds, s)
+                  : launch_gu<kAGlobal, false, false>(L, gu_u0, gu_w1, gu_ngw0, gu_ngw1, gu_lds, s);
+  if (e) return e;
   if (dn_ks)
-    hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4, true>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw,
-                       static_cast<int>(dn_room));
+    e = launch_dn<true, false>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s);
   else
-    hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4, false>), dim3(kWG), dim3(64 * DN_W), dn_lds, s, m, dn_ngw,
-                       static_cast<int>(dn_room));
-  if (hipError_t e = hipGetLastError()) return static_cast<int>(e);
-  if (!m.combine) return 0;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(m.T, (m.D / 4 + 255) / 256), dim3(256), 0, s, m);
+    e = two ? launch_dn<false, true>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s)
+            : launch_dn<false, false>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s);
+  if (e) return e;
+  if (two || !m0.combine) return 0;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(m0.T, (m0.D / 4 + 255) / 256), dim3(256), 0, s, m0);
   return static_cast<int>(hipGetLastError());
 }
 

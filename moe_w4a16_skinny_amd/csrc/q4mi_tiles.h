@@ -179,6 +179,25 @@ struct Fm<kNvfp4> {
   }
   __device__ static Codes widen(HalfCodes h) { return u32x4{h.x, h.y, 0u, 0u}; }
   __device__ static unsigned first_word(const Codes& c) { return c.x; }  // of the tile's first load
+  // A full tile, or (hf, wave-uniform) the half tile, with the same two
+  // loads either way so that the stream's waits stay exact: the half tile's
+  // 16-byte code load covers this lane's 8 bytes and its neighbour's, its
+  // scale load the word holding this lane's 2 bytes; the unused parts are
+  // dropped and steps 2 and 3 (k >= 64) get zero codes and zero scales.
+  __device__ static void load_any(Codes& c, Scales& s, const uint8_t* tb, int lane, bool hf) {
+    const int cc = lane & 15, h = lane >> 5;
+    const unsigned coff = hf ? static_cast<unsigned>(lane & ~1) * 8u : static_cast<unsigned>(lane) * 16u;
+    const unsigned soff = hf ? kHalfCodeBytes + 4u * cc : kTileCodeBytes + 4u * (2 * cc + h);
+    const u32x4 v = ld_nt16(tb + coff);
+    const unsigned sv = ld_nt4(tb + soff);
+    if (hf) {
+      c = (lane & 1) ? u32x4{v.z, v.w, 0u, 0u} : u32x4{v.x, v.y, 0u, 0u};
+      s = h ? sv >> 16 : sv & 0xFFFFu;
+    } else {
+      c = v;
+      s = sv;
+    }
+  }
 };
 template <>
 struct Fm<kAffine> {
@@ -558,16 +577,21 @@ struct GroupPtrs {
 // same round trip; every wave must reach pre()).  K is the activations' row
 // length (kAGlobal and kARing: a multiple of 64).  All arguments except the
 // lane-dependent pointers are wave-uniform.
-template <int FMT, int P, int D, int AM, class Group, class PreIssue, class Pre, class Epi, class EpiAdd>
+template <int FMT, int P, int D, int AM, bool IH = false, class Group, class PreIssue, class Pre, class Epi,
+          class EpiAdd>
 __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half_t, ALds al, ARing ring, int K,
                                               Group group, PreIssue pre_issue, Pre pre, Epi epi, EpiAdd epi_add) {
   constexpr bool ALDS = AM == kAStaged;
   constexpr bool STAGED = AM == kAStaged || AM == kAStagedRows;  // activations complete in LDS before the math
+  // IH (NVFP4 with rows staged, whose k-padding is zero in LDS): the half
+  // tile streams inline as each group's last tile (Fm::load_any), instead of
+  // in a pass of its own after the stream
+  constexpr bool INL = IH && AM == kAStagedRows && FMT == kNvfp4;
   const int lane = threadIdx.x & 63;
   const int o = lane >> 4;
   const int c = lane & 15;
   const bool has_half = half_t >= kt0 && half_t < kt0 + KRg;
-  const int KRf = has_half ? KRg - 1 : KRg;  // full tiles streamed per group
+  const int KRf = (has_half && !INL) ? KRg - 1 : KRg;  // tiles streamed per group
   const int F = ng * KRf;
   using St = StreamStage<FMT, P, AM>;
 
@@ -618,8 +642,13 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
     const int tg = kt0 + t;
     load_a(st, gp, tg, d);
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-      Fm<FMT>::load(st.c[p], st.s[p], gp.panel[p] + static_cast<size_t>(tg) * Fm<FMT>::kTile, lane);
+    for (int p = 0; p < P; ++p) {
+      if constexpr (INL)
+        Fm<FMT>::load_any(st.c[p], st.s[p], gp.panel[p] + static_cast<size_t>(tg) * Fm<FMT>::kTile, lane,
+                          tg == half_t);
+      else
+        Fm<FMT>::load(st.c[p], st.s[p], gp.panel[p] + static_cast<size_t>(tg) * Fm<FMT>::kTile, lane);
+    }
   };
   auto load_half_w = [&](St& st, const GroupPtrs<P>& gp) {
 #pragma unroll
@@ -704,7 +733,7 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
   // own slots): the data is there when the half-tile math comes after the
   // stream, instead of one more memory round trip then.  Being older than
   // every load of the stream, these loads leave the stream's waits exact.
-  const bool pre_half = has_half && AM != kARing;
+  const bool pre_half = has_half && AM != kARing && !INL;
   struct HalfW {
     typename Fm<FMT>::HalfCodes c[P];
     typename Fm<FMT>::Scales s[P];
@@ -756,7 +785,7 @@ __device__ __forceinline__ void stream_groups(int ng, int KRg, int kt0, int half
 
   // half tiles: loads of up to D groups in flight (the first D groups'
   // weights are already in hpre), then their math
-  if (has_half) {
+  if (has_half && !INL) {
     for (int g0 = 0; g0 < ng; g0 += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
