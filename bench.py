@@ -297,8 +297,9 @@ class MoeWork:
 
 
 class MoeBlockWork:
-    """One step = moe_block_forward: input norms, router matmul, router norm and
-    top-k, dense branch, experts, combine (10 launches) on the residual."""
+    """One step = moe_block_forward: input norms, router (matmul, then the
+    block's score norm and top-k), the experts and the dense branch (one
+    gate/up and one down launch), combine: 5 launches on the residual."""
 
     def __init__(self, name, spec, hot):
         import numpy as np
@@ -327,10 +328,10 @@ class MoeBlockWork:
             self.blocks.append(q4.MoeBlockWeights(e2, d2, bw.w_router, bw.router_scale, bw.down_scale, bw.norms,
                                                   bw.eps))
         self.i = 0
-        # algorithmic bytes: router matrix, dense branch, every expert that receives a token, residual in and out
-        import oracle
-        _, parts = oracle.moe_block_ref(blk, blk.residual, want_parts=True)
-        self.active = len(set(parts["idx"].ravel().tolist()))
+        # algorithmic bytes: router matrix, dense branch, every expert that receives a token (the device's
+        # routing of the initial residual), residual in and out
+        _, idx, _ = q4.moe_block_forward(bw, self.res0.clone(), blk.k, want_routing=True)
+        self.active = len(set(idx.cpu().numpy().ravel().tolist()))
         D, F, Fd, T = blk.D, spec["F"], spec["F_dense"], blk.T
         per = lambda f: 2 * (f * D // 2 + f * D // 16 + 4) + (D * f // 2 + D * f // 16 + 4)
         self.alg_bytes = D * blk.E * 4 + per(Fd) + self.active * per(F) + 2 * T * D * 4
