@@ -9,22 +9,27 @@
 // of launches per layer whatever the expert count.]
 //
 // Launch sequence of moe_grouped_qgemm (one stream, no host synchronization):
-//   1. gate_up: a fixed grid of 512 workgroups.  Every workgroup builds the
-//      expert grouping (the (token, slot) pairs sorted by expert, stable in
-//      token order) in LDS from topk_idx; workgroup 0 also writes it to the
-//      workspace.  Work items (active expert, gate panel j + up panel j) are
-//      dealt over the waves; h = gelu_tanh(g_gate acc_g) * (g_up acc_u) is
-//      formed in registers and written as f16 to the expert-sorted scratch
+//   1. gate_up: a fixed grid of 256 workgroups of 8 waves (one per CU).
+//      Every workgroup stages x in LDS and builds the expert grouping (the
+//      (token, slot) pairs sorted by expert, stable in token order) in LDS
+//      from topk_idx; workgroup 0 also writes it to the workspace.  Work
+//      items (active expert, gate panel j + up panel j) are dealt over the
+//      waves; h = gelu_tanh(g_gate acc_g) * (g_up acc_u) is formed from the
+//      parked results and written as f16 to the expert-sorted scratch
 //      h[row][F].
-//   2. down: the same grid; reads the grouping back, items (active expert,
-//      group of P panels of W_down) over the expert's contiguous h rows;
-//      o[row][D] = w_pair * g_down * acc in fp32.
-//   3. combine: y[t] = sum over slots in order + shared row (fixed order).
+//   2. down: the same grid; reads the grouping back, each workgroup a
+//      contiguous range of items (active expert, group of P panels of
+//      W_down) over the experts' h rows, staged in LDS;
+//      o[t][slot][D] = w_pair * g_down * acc in fp32 (token-major).
+//   3. combine: y[t] = sum over slots in order + the shared expert's slot.
+// The MoE block runs its experts and its dense branch as two layers of one
+// gate_up and one down launch (no combine: the block's own combine reads o).
 //
 // moe_route_topk: one kernel; workgroups split D and write partial logits,
 // the last workgroup to finish (completion counter) sums them in a fixed
 // order, then computes the softmax and the top-k per token (ties to the lower
-// expert index) and resets the counter.
+// expert index) and resets the counter.  For the MoE block the same tail
+// first turns the logits into the block's scores.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -881,8 +886,11 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeLayers L, int u0, i
     if constexpr (KS) __syncthreads();  // the stash is free for the next chunk
     c0 += NGW;
   };
-  // the two ways of reaching the activations; as in gate/up, the first
-  // chunk's stream (entered by every wave) stages the rows
+  // the two ways of reaching the activations; the first chunk's stream
+  // (entered by every wave, possibly with no item, so that all reach the
+  // staging barrier) stages the rows; it is a separate instance so that the
+  // staging and its wait are unconditional and the later streams' waits know
+  // the staging has landed
   auto run = [&](auto mode) {
     constexpr int AM = decltype(mode)::value;
     auto group = [&](int gi, GroupPtrs<P>& gp) {
