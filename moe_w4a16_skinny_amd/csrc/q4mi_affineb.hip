@@ -15,7 +15,8 @@
 // of weight loads in flight and moving each tile's 16 activation rows into
 // its own LDS ring slot with direct-to-LDS loads issued beside them (rows
 // past M repeat row M - 1; their outputs are dropped).  The waves' partial
-// sums are added in LDS in wave order (deterministic).
+// sums are added in LDS (in the rings' memory) in wave order
+// (deterministic).
 #include <hip/hip_runtime.h>
 
 #include "q4mi_tiles.h"
@@ -29,8 +30,11 @@ __global__ __launch_bounds__(64 * W) void qgemm_affineb_kernel(const uint8_t* __
                                                                int half_t, const uint16_t* __restrict__ a, int M,
                                                                int K, int N, void* __restrict__ out, int out_dtype) {
   constexpr int FMT = kAffineBits + BITS;
-  extern __shared__ u32x4 ring_lds[];  // W rings of D slots
-  __shared__ f32x4 part[W][P][64];
+  // W rings of D slots; after the stream, the waves' partial sums [W][P][64]
+  // in the same memory
+  extern __shared__ u32x4 ring_lds[];
+  f32x4(*const part)[P][64] = reinterpret_cast<f32x4(*)[P][64]>(ring_lds);
+  static_assert(W * P * 64 * 16 <= W * D * kRingSlot, "the partial sums fit in the rings");
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, o = lane >> 4;
@@ -48,22 +52,25 @@ __global__ __launch_bounds__(64 * W) void qgemm_affineb_kernel(const uint8_t* __
 #pragma unroll
     for (int j = 0; j < 4; ++j) gp.ar[j] = ar[j];
   };
+  // the wave's sums stay in registers until every wave is out of its ring
+  f32x4 sum[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) sum[p] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto park = [&](int, f32x4 (&acc)[P][2]) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) part[wv][p][lane] = acc[p][0] + acc[p][1];
+    for (int p = 0; p < P; ++p) sum[p] = acc[p][0] + acc[p][1];
   };
   auto park_add = [&](int, f32x4 (&acc)[P][2]) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) part[wv][p][lane] += acc[p][0] + acc[p][1];
+    for (int p = 0; p < P; ++p) sum[p] += acc[p][0] + acc[p][1];
   };
   auto none = [] {};
   const ARing rg = aring_view(lds_offset(ring_lds) + static_cast<unsigned>(wv * D * kRingSlot));
-  if (krg > 0) {
+  if (krg > 0)  // (fewer tiles than waves: this wave's share stays zero)
     stream_groups<FMT, P, D, kARing>(1, krg, kt0, half_t, ALds{}, rg, K, group, none, none, park, park_add);
-  } else {  // fewer tiles than waves: this wave's share is zero
+  __syncthreads();  // every ring is drained (the stream waits for its own loads at its end)
 #pragma unroll
-    for (int p = 0; p < P; ++p) part[wv][p][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int p = 0; p < P; ++p) part[wv][p][lane] = sum[p];
   __syncthreads();
   // wave p sums panel p over the waves in order and stores its 16 columns
   for (int p = wv; p < P; p += W) {
@@ -103,17 +110,20 @@ int launch_bits(const uint8_t* w, int64_t N, int64_t K, const uint16_t* a, int M
 
 }  // namespace
 
-// Per width: P panels per workgroup, W waves, D tiles in flight per wave
-// (measured at M = 16, K = 5120, N = 15360: 4 panels beat 2 and 1, and 4
-// waves beat 2 and 8; 8 tiles in flight lose to 4).
+// Per width: P panels per workgroup, W waves, D tiles in flight per wave.
+// Measured at M = 16, K = 5120, N = 15360 (same-process sweeps): 4 panels
+// beat 2, 1 and 8; 2 tiles in flight beat 3, 4, 6 and 8 (smaller rings:
+// more workgroups per CU); 8 waves suit the narrow codes (2-bit: 11.9 us
+// against 13.8 with 4 waves, 12.9 with 16), 4 the wide ones (8-bit: 24.3
+// against 24.6 with 8 and 57.6 with 16).
 int launch_affine_bits(int bits, const uint8_t* w, int64_t N, int64_t K, const uint16_t* a, int M, void* out,
                        int out_dtype, void* stream) {
   switch (bits) {
-    case 2: return launch_bits<2, 4, 4, 4>(w, N, K, a, M, out, out_dtype, stream);
-    case 3: return launch_bits<3, 4, 4, 4>(w, N, K, a, M, out, out_dtype, stream);
-    case 5: return launch_bits<5, 4, 4, 4>(w, N, K, a, M, out, out_dtype, stream);
-    case 6: return launch_bits<6, 4, 4, 4>(w, N, K, a, M, out, out_dtype, stream);
-    case 8: return launch_bits<8, 4, 4, 4>(w, N, K, a, M, out, out_dtype, stream);
+    case 2: return launch_bits<2, 4, 8, 2>(w, N, K, a, M, out, out_dtype, stream);
+    case 3: return launch_bits<3, 4, 8, 2>(w, N, K, a, M, out, out_dtype, stream);
+    case 5: return launch_bits<5, 4, 4, 2>(w, N, K, a, M, out, out_dtype, stream);
+    case 6: return launch_bits<6, 4, 4, 2>(w, N, K, a, M, out, out_dtype, stream);
+    case 8: return launch_bits<8, 4, 4, 2>(w, N, K, a, M, out, out_dtype, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }

@@ -216,6 +216,16 @@ struct Fm<kAffine> {
   __device__ static Codes widen(HalfCodes h) { return u32x4{h.x, h.y, 0u, 0u}; }
   __device__ static unsigned first_word(const Codes& c) { return c.x; }
 };
+// 8 values (128 + x_j) as bf16, x_j < 128, element j = k offset j (exact)
+__device__ __forceinline__ bf16x8 bf16_128_plus(const unsigned (&x)[8]) {
+  u32x4 r;
+  r.x = (x[0] | 0x4300u) | ((x[1] | 0x4300u) << 16);
+  r.y = (x[2] | 0x4300u) | ((x[3] | 0x4300u) << 16);
+  r.z = (x[4] | 0x4300u) | ((x[5] | 0x4300u) << 16);
+  r.w = (x[6] | 0x4300u) | ((x[7] | 0x4300u) << 16);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // b-bit affine: lane (c, o) owns 4 b code bytes, the 32 codes of row c at
 // k = 32 i + 8 o + j as one little-endian bit stream (code (i, j) at bit
 // 8 b i + b j), loaded with the widest aligned loads; the scale/bias words
@@ -261,6 +271,51 @@ struct FmBits {
     if (sh + B > 32) v |= c.w[wd + 1] << (32 - sh);
     return v & ((1u << B) - 1u);
   }
+  // The MFMA operand of step i: the 8 bf16 values 128 + q_j (element j in
+  // the low half of dword j / 2 for even j, the high half for odd j).
+  // B = 2: step i is the 16-bit field i & 1 of word i / 2, codes 2 bits
+  // apart; masking the even and the odd codes and one byte permute put
+  // q_2m and q_2m+1 16 bits apart at bit 4 m, so each dword is a shift, a
+  // mask and the exponent of 128.  Other widths: bitfield extracts.
+  __device__ static bf16x8 operand(const Codes& c, int i) {
+    if constexpr (B == 2) {
+      const unsigned d = c.w[i >> 1];
+      const unsigned x = d & 0x33333333u, y = (d >> 2) & 0x33333333u;
+      // bytes of step i's fields: x in the low half, y in the high half
+      const unsigned z = __builtin_amdgcn_perm(y, x, (i & 1) ? 0x07060302u : 0x05040100u);
+      u32x4 r;
+      r.x = (z & 0x00030003u) | 0x43004300u;
+      r.y = ((z >> 4) & 0x00030003u) | 0x43004300u;
+      r.z = ((z >> 8) & 0x00030003u) | 0x43004300u;
+      r.w = ((z >> 12) & 0x00030003u) | 0x43004300u;
+      return __builtin_bit_cast(bf16x8, r);
+    } else {
+      unsigned x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = code(c, i, j);
+      return bf16_128_plus(x);
+    }
+  }
+  // B = 8: the high and the low nibble of step i's 8 code bytes as
+  // 128 + nibble; a byte permute against 0x43 bytes builds each dword.
+  __device__ static void operand8(const Codes& c, int i, bf16x8& hi, bf16x8& lo) {
+    const unsigned k43 = 0x43434343u;
+    u32x4 h, l;
+    const unsigned d0 = c.w[2 * i], d1 = c.w[2 * i + 1];
+    const unsigned l0 = d0 & 0x0F0F0F0Fu, h0 = (d0 >> 4) & 0x0F0F0F0Fu;
+    const unsigned l1 = d1 & 0x0F0F0F0Fu, h1 = (d1 >> 4) & 0x0F0F0F0Fu;
+    // [byte 0, 0x43, byte 1, 0x43] and [byte 2, 0x43, byte 3, 0x43]
+    l.x = __builtin_amdgcn_perm(k43, l0, 0x04010400u);
+    l.y = __builtin_amdgcn_perm(k43, l0, 0x04030402u);
+    l.z = __builtin_amdgcn_perm(k43, l1, 0x04010400u);
+    l.w = __builtin_amdgcn_perm(k43, l1, 0x04030402u);
+    h.x = __builtin_amdgcn_perm(k43, h0, 0x04010400u);
+    h.y = __builtin_amdgcn_perm(k43, h0, 0x04030402u);
+    h.z = __builtin_amdgcn_perm(k43, h1, 0x04010400u);
+    h.w = __builtin_amdgcn_perm(k43, h1, 0x04030402u);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+  }
 };
 template <>
 struct Fm<kAffineBits + 2> : FmBits<2> {};
@@ -272,16 +327,6 @@ template <>
 struct Fm<kAffineBits + 6> : FmBits<6> {};
 template <>
 struct Fm<kAffineBits + 8> : FmBits<8> {};
-
-// 8 values (128 + x_j) as bf16, x_j < 128, element j = k offset j (exact)
-__device__ __forceinline__ bf16x8 bf16_128_plus(const unsigned (&x)[8]) {
-  u32x4 r;
-  r.x = (x[0] | 0x4300u) | ((x[1] | 0x4300u) << 16);
-  r.y = (x[2] | 0x4300u) | ((x[3] | 0x4300u) << 16);
-  r.z = (x[4] | 0x4300u) | ((x[5] | 0x4300u) << 16);
-  r.w = (x[6] | 0x4300u) | ((x[7] | 0x4300u) << 16);
-  return __builtin_bit_cast(bf16x8, r);
-}
 
 // One MFMA tile step: P panels of codes/scales in `c`/`s`, activation
 // operands a[0..3] (the four 32-k steps of the tile).
@@ -327,15 +372,10 @@ __device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4
         f32x4 h[2] = {z, z}, l[2] = {z, z};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          unsigned xh[8], xl[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const unsigned v = Fm<FMT>::code(c[p], i, j);
-            xh[j] = v >> 4;
-            xl[j] = v & 15u;
-          }
-          h[i >> 1] = mfma_bf16(a[i], bf16_128_plus(xh), h[i >> 1]);
-          l[i >> 1] = mfma_bf16(a[i], bf16_128_plus(xl), l[i >> 1]);
+          bf16x8 oh, ol;
+          Fm<FMT>::operand8(c[p], i, oh, ol);
+          h[i >> 1] = mfma_bf16(a[i], oh, h[i >> 1]);
+          l[i >> 1] = mfma_bf16(a[i], ol, l[i >> 1]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -346,12 +386,7 @@ __device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4
       } else {
         f32x4 q[2] = {z, z};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          unsigned x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = Fm<FMT>::code(c[p], i, j);
-          q[i >> 1] = mfma_bf16(a[i], bf16_128_plus(x), q[i >> 1]);
-        }
+        for (int i = 0; i < 4; ++i) q[i >> 1] = mfma_bf16(a[i], Fm<FMT>::operand(c[p], i), q[i >> 1]);
         q0 = q[0];
         q1 = q[1];
       }
