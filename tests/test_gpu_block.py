@@ -113,8 +113,13 @@ def check_block(blk, what):
     return out
 
 
+# the experts and the dense branch share each grouped launch, the grid split
+# by their tile-items: the last two shapes put the split at its extremes (a
+# dense branch 32x the routed work; a dense branch of one 64-wide tile, which
+# gets a single workgroup), with K = F of one half tile in down
 @pytest.mark.parametrize("T,D,E,F,Fd,k", [(4, 256, 8, 128, 192, 2), (1, 512, 16, 64, 64, 4), (7, 1024, 32, 256, 320, 8),
-                                          (16, 2816, 128, 704, 2112, 8)])
+                                          (16, 2816, 128, 704, 2112, 8), (1, 1024, 2, 64, 2048, 1),
+                                          (16, 512, 64, 256, 64, 8)])
 def test_block_parity(T, D, E, F, Fd, k):
     note(f"block T={T} D={D} E={E} F={F} Fd={Fd} k={k}")
     blk = synth.moe_block(900 + T + E, T=T, D=D, E=E, F=F, F_dense=Fd, k=k)
