@@ -78,9 +78,11 @@ def sources_sha256(kind):
     """Hash of the kernel sources a workload runs (traffic figures are tied to it)."""
     import hashlib
     csrc = os.path.join(ROOT, "moe_w4a16_skinny_amd", "csrc")
-    names = ["q4mi_tiles.h", "q4mi_internal.h"] + [{"moe": "q4mi_moe.hip", "quant": "q4mi_quant.hip",
-                                                    "prefill": "q4mi_prefill.hip",
-                                                    "affine_bits": "q4mi_affineb.hip"}.get(kind, "q4mi_gemm.hip")]
+    names = ["q4mi_tiles.h", "q4mi_internal.h"] + {"moe": ["q4mi_moe.hip"],
+                                                    "moe_block": ["q4mi_moe.hip", "q4mi_block.hip"],
+                                                    "quant": ["q4mi_quant.hip"],
+                                                    "prefill": ["q4mi_prefill.hip"],
+                                                    "affine_bits": ["q4mi_affineb.hip"]}.get(kind, ["q4mi_gemm.hip"])
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(csrc, n), "rb") as f:

@@ -790,7 +790,10 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeLayers L, int u0
 // g_down * acc in fp32.  KS: every item of the workgroup's range is streamed
 // by all W waves, each over its own range of the K tiles, as in gate/up.
 // TWO as in gate/up; lds is the launch's dynamic LDS size.
-template <int P, int W, int DP, bool KS, bool TWO>
+// DPG: tiles in flight when a workgroup's rows do not fit in LDS (read
+// through a buffer resource instead); a shallower ring there keeps that
+// rarely taken path from setting the register budget of the staged one.
+template <int P, int W, int DP, bool KS, bool TWO, int DPG = DP>
 __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeLayers L, int u0, int w1, int ngw0, int ngw1,
                                                           int lds) {
   __shared__ MoeDownTable G;
@@ -893,6 +896,7 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeLayers L, int u0, i
   // the staging has landed
   auto run = [&](auto mode) {
     constexpr int AM = decltype(mode)::value;
+    constexpr int DD = AM == kAStagedRows ? DP : DPG;
     auto group = [&](int gi, GroupPtrs<P>& gp) {
       prio_by_items_left(ntot - c0 - gi);
       int e, q;
@@ -914,16 +918,16 @@ __global__ __launch_bounds__(64 * W) void moe_down_kernel(MoeLayers L, int u0, i
       if constexpr (AM == kAStagedRows) stage_issue(sg, reinterpret_cast<u32x4*>(stage));
     };
     auto stage_pre = [&] {
-      if constexpr (AM == kAStagedRows) stage_wait<DP * P * 2>();  // the prologue's D tiles of P panels
+      if constexpr (AM == kAStagedRows) stage_wait<DD * P * 2>();  // the prologue's D tiles of P panels
     };
     auto none = [] {};
     ng = min(NGW, ntot);
-    stream_groups<kNvfp4, P, DP, AM, true>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group,
+    stream_groups<kNvfp4, P, DD, AM, true>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group,
                                            stage_pre_issue, stage_pre, epi, epi_add);
     finish();
     while (c0 < ntot) {
       ng = min(NGW, ntot - c0);
-      stream_groups<kNvfp4, P, DP, AM, true>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group, none, none,
+      stream_groups<kNvfp4, P, DD, AM, true>(ng, krg, kt0, half ? nfull : -1, al, ARing{}, m.F, group, none, none,
                                              epi, epi_add);
       finish();
     }
@@ -1008,6 +1012,10 @@ int launch_route(const RouteArgs& r, void* stream) {
 
 namespace {
 constexpr int GU_W = 8, DN_P = 2, DN_W = 8, kWG = 256;  // one 8-wave workgroup per CU
+// down for a lone layer (item per wave): 16 waves per workgroup, its
+// unstaged path 1 tile deep (measured 24.8 us against 25.8 for the 128 + 1
+// expert layer)
+constexpr int DN_W1 = 16;
 
 // Shapes of one layer's two launches.
 struct MoeShape {
@@ -1039,11 +1047,11 @@ int launch_gu(const MoeLayers& L, int u0, int w1, int ngw0, int ngw1, size_t lds
                      ngw1);
   return static_cast<int>(hipGetLastError());
 }
-template <bool KS, bool TWO>
+template <int W, bool KS, bool TWO, int DPG>
 int launch_dn(const MoeLayers& L, int u0, int w1, int ngw0, int ngw1, size_t lds, hipStream_t s) {
-  const void* fn = reinterpret_cast<const void*>(&moe_down_kernel<DN_P, DN_W, 4, KS, TWO>);
+  const void* fn = reinterpret_cast<const void*>(&moe_down_kernel<DN_P, W, 4, KS, TWO, DPG>);
   if (int e = ensure_dynamic_lds(fn, lds)) return e;
-  hipLaunchKernelGGL((moe_down_kernel<DN_P, DN_W, 4, KS, TWO>), dim3(kWG), dim3(64 * DN_W), lds, s, L, u0, w1, ngw0,
+  hipLaunchKernelGGL((moe_down_kernel<DN_P, W, 4, KS, TWO, DPG>), dim3(kWG), dim3(64 * W), lds, s, L, u0, w1, ngw0,
                      ngw1, static_cast<int>(lds));
   return static_cast<int>(hipGetLastError());
 }
@@ -1101,14 +1109,18 @@ int launch_moe(const MoeArgs& m0, const MoeArgs* m1, void* stream) {
     gu_ngw1 = std::min(gu_need1, static_cast<int>(room / slot));
     gu_lds = xbytes + static_cast<size_t>(std::max(gu_ngw0, gu_ngw1)) * slot;
   }
-  const int dn_cap = static_cast<int>(kStashLds / (size_t(DN_W) * DN_P * 64 * 16));
+  // waves per down workgroup; the 16-wave lone-layer kernel parks at most 2
+  // items per wave (64 KiB), leaving room to stage the rows of two experts
+  const int dn_w = (two || dn_ks) ? DN_W : DN_W1;
+  const size_t dn_stash_max = (two || dn_ks) ? kStashLds : 64 * 1024;
+  const int dn_cap = static_cast<int>(dn_stash_max / (size_t(dn_w) * DN_P * 64 * 16));
   int dn_need0, dn_need1 = 1;
   if (dn_ks) {
     dn_need0 = need(h0.nact_max * h0.ngp, kWG);
   } else {
-    dn_need0 = two ? need((h0.nact_max * h0.ngp * h0.ntf + h1.nact_max * h1.ngp * h1.ntf) / h0.ntf, kWG * DN_W) + 1
-                   : need(h0.nact_max * h0.ngp, dn_split * DN_W);
-    if (two) dn_need1 = need(h1.nact_max * h1.ngp, (kWG - dn_split) * DN_W) + 1;
+    dn_need0 = two ? need((h0.nact_max * h0.ngp * h0.ntf + h1.nact_max * h1.ngp * h1.ntf) / h0.ntf, kWG * dn_w) + 1
+                   : need(h0.nact_max * h0.ngp, dn_split * dn_w);
+    if (two) dn_need1 = need(h1.nact_max * h1.ngp, (kWG - dn_split) * dn_w) + 1;
   }
   const int dn_ngw0 = std::min(dn_need0, dn_cap), dn_ngw1 = std::min(dn_need1, dn_cap);
   // the CU's LDS past the table: each role's stash, then its workgroup's
@@ -1135,10 +1147,11 @@ int launch_moe(const MoeArgs& m0, const MoeArgs* m1, void* stream) {
                   : launch_gu<kAGlobal, false, false>(L, gu_u0, gu_w1, gu_ngw0, gu_ngw1, gu_lds, s);
   if (e) return e;
   if (dn_ks)
-    e = launch_dn<true, false>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s);
+    e = launch_dn<DN_W, true, false, 4>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s);
+  else if (two)
+    e = launch_dn<DN_W, false, true, 4>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s);
   else
-    e = two ? launch_dn<false, true>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s)
-            : launch_dn<false, false>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s);
+    e = launch_dn<DN_W1, false, false, 1>(L, dn_u0, dn_w1, dn_ngw0, dn_ngw1, dn_lds, s);
   if (e) return e;
   if (two || !m0.combine) return 0;
   hipLaunchKernelGGL(moe_combine_kernel, dim3(m0.T, (m0.D / 4 + 255) / 256), dim3(256), 0, s, m0);
