@@ -449,7 +449,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(const uint8_t* __restrict__
     for (int i = 0; i < steps; ++i) {
       const unsigned wsb = (i < 2) ? sb.x : sb.y;
       const float s = bf16_lo(wsb), b = bf16_hi(wsb);
-      const bf16x8 v = affine_operand(cw[i]);
+      const bf16x8 v = affine_operand(cw[i], 0x000F000Fu, 0x43004300u);
       for (int j = 0; j < 8; ++j) {
         const int k = kb + 32 * i + 8 * o + j;
         const float q = (float)v[j] - 128.0f;  // exact: 128 + q is exact in bf16

@@ -50,8 +50,9 @@ __device__ __forceinline__ f16x2 e4m3_pair(unsigned sw, bool hi) {
 }
 
 // 8 affine codes -> 8 bf16 of value 128 + q (element 2s at nibble s, 2s+1 at nibble s+4)
-__device__ __forceinline__ bf16x8 affine_operand(unsigned d) {
-  const unsigned mk = 0x000F000Fu, mg = 0x43004300u;
+// (mk = 0x000F000F and mg = 0x43004300 come in registers, so that each
+// dword is one v_and_or_b32, which takes no literal on gfx9)
+__device__ __forceinline__ bf16x8 affine_operand(unsigned d, unsigned mk, unsigned mg) {
   u32x4 r;
   r.x = (d & mk) | mg;
   r.y = ((d >> 4) & mk) | mg;
@@ -271,23 +272,42 @@ struct FmBits {
     if (sh + B > 32) v |= c.w[wd + 1] << (32 - sh);
     return v & ((1u << B) - 1u);
   }
-  // The MFMA operand of step i: the 8 bf16 values 128 + q_j (element j in
-  // the low half of dword j / 2 for even j, the high half for odd j).
+  // The MFMA operand of step i: the 8 bf16 values 128 + q_j (q_j itself
+  // for B = 8; element j in the low half of dword j / 2 for even j, the
+  // high half for odd j).
   // B = 2: step i is the 16-bit field i & 1 of word i / 2, codes 2 bits
   // apart; masking the even and the odd codes and one byte permute put
   // q_2m and q_2m+1 16 bits apart at bit 4 m, so each dword is a shift, a
   // mask and the exponent of 128.  Other widths: bitfield extracts.
-  __device__ static bf16x8 operand(const Codes& c, int i) {
+  // mk, mg: 0x00030003 and 0x43004300 in registers (one v_and_or_b32 a dword)
+  __device__ static bf16x8 operand(const Codes& c, int i, unsigned mk, unsigned mg) {
     if constexpr (B == 2) {
       const unsigned d = c.w[i >> 1];
       const unsigned x = d & 0x33333333u, y = (d >> 2) & 0x33333333u;
       // bytes of step i's fields: x in the low half, y in the high half
       const unsigned z = __builtin_amdgcn_perm(y, x, (i & 1) ? 0x07060302u : 0x05040100u);
       u32x4 r;
-      r.x = (z & 0x00030003u) | 0x43004300u;
-      r.y = ((z >> 4) & 0x00030003u) | 0x43004300u;
-      r.z = ((z >> 8) & 0x00030003u) | 0x43004300u;
-      r.w = ((z >> 12) & 0x00030003u) | 0x43004300u;
+      r.x = (z & mk) | mg;
+      r.y = ((z >> 4) & mk) | mg;
+      r.z = ((z >> 8) & mk) | mg;
+      r.w = ((z >> 12) & mk) | mg;
+      return __builtin_bit_cast(bf16x8, r);
+    } else if constexpr (B == 8) {
+      // the codes themselves: a byte converts to fp32 exactly
+      // (v_cvt_f32_ubyte*), and an integer below 256 keeps 8 significant
+      // bits, so the fp32 value's high half is its exact bf16
+      u32x4 r;
+      unsigned* rr = reinterpret_cast<unsigned*>(&r);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned d = c.w[2 * i + h];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const unsigned lo = __float_as_uint(static_cast<float>((d >> (16 * j)) & 0xFFu));
+          const unsigned hi = __float_as_uint(static_cast<float>((d >> (16 * j + 8)) & 0xFFu));
+          rr[2 * h + j] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+        }
+      }
       return __builtin_bit_cast(bf16x8, r);
     } else {
       unsigned x[8];
@@ -295,26 +315,6 @@ struct FmBits {
       for (int j = 0; j < 8; ++j) x[j] = code(c, i, j);
       return bf16_128_plus(x);
     }
-  }
-  // B = 8: the high and the low nibble of step i's 8 code bytes as
-  // 128 + nibble; a byte permute against 0x43 bytes builds each dword.
-  __device__ static void operand8(const Codes& c, int i, bf16x8& hi, bf16x8& lo) {
-    const unsigned k43 = 0x43434343u;
-    u32x4 h, l;
-    const unsigned d0 = c.w[2 * i], d1 = c.w[2 * i + 1];
-    const unsigned l0 = d0 & 0x0F0F0F0Fu, h0 = (d0 >> 4) & 0x0F0F0F0Fu;
-    const unsigned l1 = d1 & 0x0F0F0F0Fu, h1 = (d1 >> 4) & 0x0F0F0F0Fu;
-    // [byte 0, 0x43, byte 1, 0x43] and [byte 2, 0x43, byte 3, 0x43]
-    l.x = __builtin_amdgcn_perm(k43, l0, 0x04010400u);
-    l.y = __builtin_amdgcn_perm(k43, l0, 0x04030402u);
-    l.z = __builtin_amdgcn_perm(k43, l1, 0x04010400u);
-    l.w = __builtin_amdgcn_perm(k43, l1, 0x04030402u);
-    h.x = __builtin_amdgcn_perm(k43, h0, 0x04010400u);
-    h.y = __builtin_amdgcn_perm(k43, h0, 0x04030402u);
-    h.z = __builtin_amdgcn_perm(k43, h1, 0x04010400u);
-    h.w = __builtin_amdgcn_perm(k43, h1, 0x04030402u);
-    hi = __builtin_bit_cast(bf16x8, h);
-    lo = __builtin_bit_cast(bf16x8, l);
   }
 };
 template <>
@@ -332,10 +332,10 @@ struct Fm<kAffineBits + 8> : FmBits<8> {};
 // operands a[0..3] (the four 32-k steps of the tile).
 // Affine widths: a code q < 128 becomes the exact bf16 128 + q, so that
 // sum_k a (128 + q) runs on the bf16 MFMA and the group sum sum_k a on the
-// same MFMA against ones; per group of 64
+// same MFMA against a 0/1 operand; per group of 64
 //   sum_k a w = s sum a (128 + q) + (b - 128 s) sum a,
-// and for 8-bit codes, split into nibbles q = 16 qh + ql on two MFMAs,
-//   sum_k a w = s (16 sum a (128 + qh) + sum a (128 + ql)) + (b - 2176 s) sum a.
+// and 8-bit codes, exact in bf16 as they are,
+//   sum_k a w = s sum a q + b sum a.
 template <int FMT, int P>
 __device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4],
                                           const typename Fm<FMT>::Codes (&c)[P],
@@ -353,54 +353,69 @@ __device__ __forceinline__ void tile_math(f32x4 (&acc)[P][2], const u32x4 (&a)[4
       for (int p = 0; p < P; ++p)
         acc[p][i & 1] = mfma_f16(a[i], nvfp4_operand(c[p][i], sv[p][i >> 1][i & 1]), acc[p][i & 1]);
   } else {
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    // b-bit widths: the group sums on the MFMA with the activations as the B
+    // operand, against a 0/1 operand whose rows 0-3 take the tile's first
+    // group (steps 0, 1) and rows 4-7 its second (steps 2, 3): lane (c, o)
+    // then holds token c's sum over group o for o < 2 and 0 for o >= 2, the
+    // A operand of an fp32 16x16x4 MFMA over the groups (k = o) that adds
+    // the bias terms.  The 4-bit width, whose GEMM configurations run more
+    // waves a SIMD, keeps them on FMAs (sums against ones, token-major).
+    constexpr bool BM = FMT != kAffine;
+    const int row = threadIdx.x & 15, og = (threadIdx.x >> 4) & 1;
+    const unsigned g0 = !BM || row < 4 ? 0x3F803F80u : 0u, g1 = !BM || (row >= 4 && row < 8) ? 0x3F803F80u : 0u;
+    const u32x4 sel0 = {g0, g0, g0, g0}, sel1 = {g1, g1, g1, g1};
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 as0 = mfma_bf16(a[0], ones, z);
-    as0 = mfma_bf16(a[1], ones, as0);
-    f32x4 as1 = mfma_bf16(a[2], ones, z);
-    as1 = mfma_bf16(a[3], ones, as1);
+    unsigned mk = FMT == kAffine ? 0x000F000Fu : 0x00030003u, mg = 0x43004300u;
+    asm("" : "+v"(mk), "+v"(mg));  // operand constants in registers (v_and_or_b32)
+    f32x4 gs, as0, as1;
+    if constexpr (BM) {
+      gs = mfma_bf16(sel0, __builtin_bit_cast(bf16x8, a[0]), z);
+      gs = mfma_bf16(sel0, __builtin_bit_cast(bf16x8, a[1]), gs);
+      gs = mfma_bf16(sel1, __builtin_bit_cast(bf16x8, a[2]), gs);
+      gs = mfma_bf16(sel1, __builtin_bit_cast(bf16x8, a[3]), gs);
+    } else {
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, sel0);
+      as0 = mfma_bf16(a[0], ones, z);
+      as0 = mfma_bf16(a[1], ones, as0);
+      as1 = mfma_bf16(a[2], ones, z);
+      as1 = mfma_bf16(a[3], ones, as1);
+    }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       f32x4 q0, q1;
-      float off = -128.0f;  // the 128 (16 * 128 + 128 for split 8-bit codes) under each code
+      const float off = FMT == kAffineBits + 8 ? 0.0f : -128.0f;  // the 128 under each code (none at 8 bits)
       if constexpr (FMT == kAffine) {
-        q0 = mfma_bf16(a[0], affine_operand(c[p][0]), z);
-        q0 = mfma_bf16(a[1], affine_operand(c[p][1]), q0);
-        q1 = mfma_bf16(a[2], affine_operand(c[p][2]), z);
-        q1 = mfma_bf16(a[3], affine_operand(c[p][3]), q1);
-      } else if constexpr (FMT == kAffineBits + 8) {
-        f32x4 h[2] = {z, z}, l[2] = {z, z};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x8 oh, ol;
-          Fm<FMT>::operand8(c[p], i, oh, ol);
-          h[i >> 1] = mfma_bf16(a[i], oh, h[i >> 1]);
-          l[i >> 1] = mfma_bf16(a[i], ol, l[i >> 1]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          q0[r] = fmaf(16.0f, h[0][r], l[0][r]);
-          q1[r] = fmaf(16.0f, h[1][r], l[1][r]);
-        }
-        off = -2176.0f;
+        q0 = mfma_bf16(a[0], affine_operand(c[p][0], mk, mg), z);
+        q0 = mfma_bf16(a[1], affine_operand(c[p][1], mk, mg), q0);
+        q1 = mfma_bf16(a[2], affine_operand(c[p][2], mk, mg), z);
+        q1 = mfma_bf16(a[3], affine_operand(c[p][3], mk, mg), q1);
       } else {
         f32x4 q[2] = {z, z};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i >> 1] = mfma_bf16(a[i], Fm<FMT>::operand(c[p], i), q[i >> 1]);
+        for (int i = 0; i < 4; ++i) q[i >> 1] = mfma_bf16(a[i], Fm<FMT>::operand(c[p], i, mk, mg), q[i >> 1]);
         q0 = q[0];
         q1 = q[1];
       }
-      const float s0 = bf16_lo(s[p].x), b0 = bf16_hi(s[p].x);
-      const float s1 = bf16_lo(s[p].y), b1 = bf16_hi(s[p].y);
-      const float c0 = fmaf(off, s0, b0), c1 = fmaf(off, s1, b1);
+      const float s0 = bf16_lo(s[p].x), s1 = bf16_lo(s[p].y);
+      if constexpr (BM) {
+        // sum_g (b_g + off s_g) (group sum) on the fp32 MFMA: lane (c, o)
+        // gives column c's coefficient of group o & 1 (A's rows o >= 2 are 0)
+        const unsigned sw = og ? s[p].y : s[p].x;
+        acc[p][1] =
+            __builtin_amdgcn_mfma_f32_16x16x4f32(gs[0], fmaf(off, bf16_lo(sw), bf16_hi(sw)), acc[p][1], 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = acc[p][0][r];
-        v = fmaf(s0, q0[r], v);
-        v = fmaf(c0, as0[r], v);
-        v = fmaf(s1, q1[r], v);
-        v = fmaf(c1, as1[r], v);
-        acc[p][0][r] = v;
+        for (int r = 0; r < 4; ++r) acc[p][0][r] = fmaf(s1, q1[r], fmaf(s0, q0[r], acc[p][0][r]));
+      } else {
+        const float c0 = fmaf(off, s0, bf16_hi(s[p].x)), c1 = fmaf(off, s1, bf16_hi(s[p].y));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[p][0][r];
+          v = fmaf(s0, q0[r], v);
+          v = fmaf(c0, as0[r], v);
+          v = fmaf(s1, q1[r], v);
+          v = fmaf(c1, as1[r], v);
+          acc[p][0][r] = v;
+        }
       }
     }
   }
