@@ -240,7 +240,8 @@ class GemmWork:
 
 
 class MoeWork:
-    """One step = moe_route_topk + moe_grouped_qgemm on the 128 + 1 expert layer."""
+    """One step = moe_route_grouped_qgemm (the router, then the grouped layer;
+    the top-k taken inside the gate/up launch) on the 128 + 1 expert layer."""
 
     def __init__(self, name, spec, hot):
         import numpy as np
@@ -274,13 +275,26 @@ class MoeWork:
         self.kind = "moe"
         self.kernel_names = ["moe step: route_kernel + moe_gate_up_kernel + moe_down_kernel + moe_combine_kernel"]
         self.dtype = "f16"
+        import ctypes as C
+        self.descs = [m.desc() for m in self.layers]
+        self.idx = torch.empty((moe.T, moe.k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((moe.T, moe.k), dtype=torch.float32, device="cuda")
+        self.wsb = q4.raw().moe_route_grouped_workspace_bytes(C.byref(self.descs[0]), moe.T, moe.k)
+        self.ws = q4.workspace(self.wsb)
 
     def step(self):
+        import ctypes as C
         q4 = self.q4
-        mw = self.layers[self.i % self.copies]
+        d = self.descs[self.i % self.copies]
         self.i += 1
-        _, idx, w = q4.moe_route_topk(self.x, self.wr, self.moe.k, want_logits=False)
-        q4.moe_grouped_qgemm(mw, self.x, idx, w, out=self.out)
+        m = self.moe
+        rc = q4.raw().moe_route_grouped_qgemm(C.byref(d), C.c_void_p(self.x.data_ptr()), C.c_void_p(self.wr.data_ptr()),
+                                              m.T, m.k, 0, None, C.c_void_p(self.idx.data_ptr()),
+                                              C.c_void_p(self.w.data_ptr()), C.c_void_p(self.out.data_ptr()),
+                                              q4.Q4_F32, C.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                              q4._stream())
+        if rc != 0:
+            q4._check(rc)
 
     def config(self):
         m = self.moe

@@ -289,6 +289,33 @@ int moe_grouped_qgemm(const q4_moe_desc* w, const void* x, const int32_t* topk_i
 int moe_grouped_qgemm_noalloc(const q4_moe_desc* w, const void* x, const int32_t* topk_idx,
                               const float* topk_w, int T, int k, void* y, int out_dtype, void* stream);
 
+/* Bytes of device workspace moe_route_grouped_qgemm needs (0 if E > 256):
+ * moe_workspace_bytes plus the router's partial logits. */
+size_t moe_route_grouped_workspace_bytes(const q4_moe_desc* w, int T, int k);
+
+/* The router and the grouped MoE layer in one call [DOC 3.2 "Per-layer
+ * (MoE)": router matmul, softmax, top-k, then the chosen experts' FFNs
+ * summed with the routing weights]: the results of moe_route_topk(x,
+ * w_router, T, w->D, w->E, k, renormalize, logits, topk_idx, topk_w)
+ * followed by moe_grouped_qgemm(w, x, topk_idx, topk_w, T, k, y).  The
+ * router kernel writes only its partial logits; every gate/up workgroup
+ * sums them (in the router's order, so the logits are the same bits) and
+ * takes the top-k and softmax itself before building the expert grouping,
+ * one launch and one cross-workgroup handoff fewer than the two calls (the
+ * same indices; the weights equal moe_route_topk's up to the order of the
+ * softmax sums).  Shapes whose scores do not fit the gate/up launch's LDS
+ * beside x (E % 4 != 0, or T E too large) take the two calls' path.
+ *   x, w_router, logits (or NULL), topk_idx, topk_w  as for moe_route_topk
+ *            (topk_idx and topk_w are outputs here)
+ *   y, out_dtype  as for moe_grouped_qgemm
+ *   ws       device workspace of ws_bytes >= moe_route_grouped_workspace_bytes,
+ *            its first 32 KiB of counters at zero (left at zero)
+ * Errors: those of moe_route_topk and moe_grouped_qgemm; nothing is
+ * enqueued on an error other than HIP. */
+int moe_route_grouped_qgemm(const q4_moe_desc* w, const void* x, const float* w_router, int T, int k,
+                            int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* y,
+                            int out_dtype, void* ws, size_t ws_bytes, void* stream);
+
 /* MLX-style affine weights at 2, 3, 5, 6 or 8 bits [ISSUE "Why now":
  * qlinear's MLX affine paths at 2, 3, 5, 6 and 8 bits beside 4, groups of
  * 64; "Steps" 3 and 9: the other MLX widths; the 4-bit width has the entry

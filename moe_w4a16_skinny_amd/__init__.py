@@ -64,6 +64,9 @@ _SIGS = {
     "moe_workspace_bytes": (_sz, [C.POINTER(q4_moe_desc), _i32, _i32]),
     "moe_grouped_qgemm": (_i32, [C.POINTER(q4_moe_desc), _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "moe_grouped_qgemm_noalloc": (_i32, [C.POINTER(q4_moe_desc), _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp]),
+    "moe_route_grouped_workspace_bytes": (_sz, [C.POINTER(q4_moe_desc), _i32, _i32]),
+    "moe_route_grouped_qgemm": (_i32, [C.POINTER(q4_moe_desc), _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32,
+                                       _vp, _sz, _vp]),
     "q4_affine_bits_packed_bytes": (_sz, [_i64, _i64, _i32]),
     "q4_affine_bits_repack": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz]),
     "q4_affine_bits_unpack": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
@@ -361,6 +364,28 @@ def moe_grouped_qgemm_noalloc(weights: MoeWeights, x, topk_idx, topk_w, out):
     _check(_lib.moe_grouped_qgemm_noalloc(C.byref(d), _tptr(x), _tptr(topk_idx), _tptr(topk_w), T, k, _tptr(out),
                                           _dtype_code(out.dtype), _stream()))
     return out
+
+
+def moe_route_grouped_qgemm(weights: MoeWeights, x, w_router, k: int, renormalize: bool = False,
+                            want_logits: bool = False, out=None, out_dtype=None, ws=None):
+    """Router and grouped MoE layer in one call: (y [T][D], logits or None, idx [T][k], weights [T][k]).
+    ws: an optional zero-filled workspace of at least moe_route_grouped_workspace_bytes."""
+    torch = _torch()
+    T, D = x.shape
+    E = w_router.shape[1]
+    if out is None:
+        out = torch.empty((T, D), dtype=out_dtype or torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    d = weights.desc()
+    wsb = _lib.moe_route_grouped_workspace_bytes(C.byref(d), T, k)
+    if ws is None:
+        ws = workspace(wsb, x.device)
+    _check(_lib.moe_route_grouped_qgemm(C.byref(d), _tptr(x), _tptr(w_router), T, k, int(bool(renormalize)),
+                                        _tptr(logits), _tptr(idx), _tptr(w), _tptr(out), _dtype_code(out.dtype),
+                                        _tptr(ws), ws.numel() if ws is not None else 0, _stream()))
+    return out, logits, idx, w
 
 
 def q4_dequant_nvfp4(w_packed, global_scale: float, N: int, K: int):

@@ -494,9 +494,12 @@ static int route_check(const char* fn, const void* x, const float* w_router, int
   return Q4_OK;
 }
 
+// partial: where the partial logits go (NULL: the workspace past its
+// counters); partials_only: stop there (the routed gate/up takes the top-k)
 static int route_enqueue(const char* fn, const void* x, const float* w_router, int T, int D, int E, int k,
                          int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* ws, void* stream,
-                         const q4_moe_block_desc* blk = nullptr, int32_t* didx = nullptr, float* dw = nullptr) {
+                         const q4_moe_block_desc* blk = nullptr, int32_t* didx = nullptr, float* dw = nullptr,
+                         float* partial = nullptr, bool partials_only = false) {
   RouteArgs r{};
   if (blk) {  // the MoE block's routing: scores normalized and scaled, weights times the down scale
     r.zscale = blk->router_scale;
@@ -516,7 +519,8 @@ static int route_enqueue(const char* fn, const void* x, const float* w_router, i
   r.idx = topk_idx;
   r.w = topk_w;
   r.counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kWsRouteCounter);
-  r.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
+  r.partial = partial ? partial : reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes);
+  r.partials_only = partials_only ? 1 : 0;
   r.nsplit = route_splits(D);
   r.rows = route_rows(D);
   if (int e = launch_route(r, stream)) return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, e);
@@ -665,6 +669,52 @@ int moe_grouped_qgemm_noalloc(const q4_moe_desc* w, const void* x, const int32_t
   return ok();
 }
 
+// ---- router + grouped MoE in one call -------------------------------------
+
+static size_t route_part_bytes(int T, int D, int E) {
+  return (size_t(route_splits(D)) * size_t(T) * size_t(E) * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t moe_route_grouped_workspace_bytes(const q4_moe_desc* w, int T, int k) {
+  const size_t m = moe_workspace_bytes(w, T, k);
+  if (!m || w->E > 256) return 0;
+  return m + route_part_bytes(T, w->D, w->E);
+}
+
+int moe_route_grouped_qgemm(const q4_moe_desc* w, const void* x, const float* w_router, int T, int k,
+                            int renormalize, float* logits, int32_t* topk_idx, float* topk_w, void* y,
+                            int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = moe_check_shape(__func__, w, x, topk_idx, topk_w, T, k, y, out_dtype)) return rc;
+  const size_t mws = moe_workspace_bytes(w, T, k);
+  // the router's own conditions, its workspace taken as the whole of ws
+  if (int rc = route_check(__func__, x, w_router, T, w->D, w->E, k, logits, topk_idx, topk_w, ws, ws_bytes))
+    return rc;
+  const size_t need = moe_route_grouped_workspace_bytes(w, T, k);
+  if (ws_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: ws_bytes=%zu < %zu", __func__, ws_bytes, need);
+  // the partial logits past the layer's scratch (gate/up reads them while it writes h)
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + mws);
+  if (moe_gu_route_fits(T, w->D, w->E)) {
+    if (int rc = route_enqueue(__func__, x, w_router, T, w->D, w->E, k, renormalize, nullptr, topk_idx, topk_w, ws,
+                               stream, nullptr, nullptr, nullptr, part, true))
+      return rc;
+    MoeArgs m = moe_args(w, x, nullptr, topk_w, T, k, y, out_dtype, ws, true);
+    m.rpart = part;
+    m.rsplit = route_splits(w->D);
+    m.renorm = renormalize ? 1 : 0;
+    m.ridx = topk_idx;
+    m.rtw = topk_w;
+    m.rlogits = logits;
+    if (int e = launch_moe(m, nullptr, stream))
+      return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
+  } else {  // the router's own top-k, then the layer
+    if (int rc = route_enqueue(__func__, x, w_router, T, w->D, w->E, k, renormalize, logits, topk_idx, topk_w, ws,
+                               stream, nullptr, nullptr, nullptr, part, false))
+      return rc;
+    if (int rc = moe_enqueue(__func__, w, x, topk_idx, topk_w, T, k, y, out_dtype, ws, stream)) return rc;
+  }
+  return ok();
+}
+
 // ---- affine 2/3/5/6/8-bit ------------------------------------------------
 }  // extern "C"
 namespace {
@@ -792,7 +842,7 @@ int qgemm_affine_bits(const void* w_packed, const void* a, int M, int64_t K, int
 // two expert layers' outputs stay in their own workspaces until the block's
 // combine reads them.
 struct BlockWs {
-  size_t sub2, sub1, h1, h2, idx, w, didx, dw, total;
+  size_t sub2, part, sub1, h1, h2, idx, w, didx, dw, total;
 };
 static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 static BlockWs block_ws(const q4_moe_block_desc* b, int T, int k) {
@@ -805,6 +855,7 @@ static BlockWs block_ws(const q4_moe_block_desc* b, int T, int k) {
     return at;
   };
   L.sub2 = take(std::max(moe_route_workspace_bytes(T, D, E), moe_workspace_bytes(&b->experts, T, k)));
+  L.part = take(size_t(route_splits(D)) * size_t(T) * size_t(E) * sizeof(float));
   L.sub1 = take(moe_workspace_bytes(&b->dense, T, 1));
   L.h1 = take(size_t(T) * D * 2);
   L.h2 = take(size_t(T) * D * 2);
@@ -880,11 +931,28 @@ int moe_block_forward(const q4_moe_block_desc* b, float* residual, int T, int k,
   if (int e = launch_block_norm_in(residual, T, D, b->ffn_norm, b->pre_ffw_norm_2, b->eps, base + L.h1, base + L.h2,
                                    stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
-  if (int rc = route_enqueue(__func__, h2, b->w_router, T, D, E, k, 0, nullptr, idx, w, ws2, stream, b, didx, dw))
+  // the router's partial logits in their own region: the routed gate/up
+  // reads them while it writes the layers' scratch
+  float* part = reinterpret_cast<float*>(base + L.part);
+  const bool routed = moe_gu_route_fits(T, D, E);
+  if (int rc = route_enqueue(__func__, h2, b->w_router, T, D, E, k, 0, nullptr, idx, w, ws2, stream, b, didx, dw,
+                             part, routed))
     return rc;
   // the experts and the dense branch share the gate/up and the down launch
-  const MoeArgs me = moe_args(&b->experts, h2, idx, w, T, k, residual, Q4_F32, ws2, false);
-  const MoeArgs md = moe_args(&b->dense, h1, didx, dw, T, 1, residual, Q4_F32, ws1, false);
+  MoeArgs me = moe_args(&b->experts, h2, idx, w, T, k, residual, Q4_F32, ws2, false);
+  MoeArgs md = moe_args(&b->dense, h1, didx, dw, T, 1, residual, Q4_F32, ws1, false);
+  if (routed) {  // gate/up takes the top-k from the partials; the dense branch's routing is constant
+    me.rpart = part;
+    me.rsplit = route_splits(D);
+    me.zscale = b->router_scale;
+    me.down_scale = b->down_scale;
+    me.eps = b->eps;
+    me.ridx = idx;
+    me.rtw = w;
+    md.rconst = 1;
+    md.ridx = didx;
+    md.rtw = dw;
+  }
   if (int e = launch_moe(me, &md, stream))
     return fail(Q4_ERR_HIP, "%s: kernel launch failed (hip error %d)", __func__, e);
   if (int e = launch_block_combine(o1, o2, rowof2, k, T, D, b->post_ffw_norm_1, b->post_ffw_norm_2, b->post_ffw_norm,

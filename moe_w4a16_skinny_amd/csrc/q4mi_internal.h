@@ -167,6 +167,7 @@ struct RouteArgs {
   unsigned* counter;    // workspace counter
   int nsplit;           // splits of D
   int rows;             // rows of D per split (a multiple of 64)
+  int partials_only;    // 1: write the partial logits and stop (the gate/up launch routes from them)
 };
 int launch_route(const RouteArgs& r, void* stream);
 
@@ -190,7 +191,27 @@ struct MoeArgs {
   int32_t* rowof;          // workspace [T * k]: pair -> scratch row (-1: none)
   int32_t* grp;            // workspace: the expert grouping, written by gate/up, read by down
   int combine;             // 1: a third launch sums each token's slots into y
+  // Routing inside gate/up (rpart non-NULL; idx unused): every workgroup
+  // sums the router's partial logits [rsplit][T][E] in split order (E % 4
+  // == 0) and takes the top-k and softmax itself, over z = RMSNorm(logits;
+  // eps) * zscale when zscale is non-NULL, the weights times down_scale[e]
+  // when that is non-NULL and renormalized over the k when renorm; the
+  // publishing workgroup writes them to ridx / rtw (tw must be rtw, for
+  // down) and the summed logits to rlogits when non-NULL.  rconst: the
+  // one-expert routing (expert 0, weight 1, k = 1) with no router, written
+  // to ridx / rtw the same way.
+  const float* rpart;
+  int rsplit, renorm, rconst;
+  const float* zscale;
+  const float* down_scale;
+  float eps;
+  int32_t* ridx;
+  float* rtw;
+  float* rlogits;
 };
+// LDS the routed gate/up prologue borrows from the stash: the logits [T][E]
+// and the scale vectors [E] each (bytes)
+inline size_t moe_route_lds(int T, int E) { return (static_cast<size_t>(T) * E + 2 * static_cast<size_t>(E)) * 4; }
 // The layers of one grouped launch (the second only for two-layer launches).
 struct MoeLayers {
   MoeArgs l[2];
@@ -204,6 +225,8 @@ inline size_t moe_grp_words(int E, int T, int k) {
 // two layers of equal T and D sharing the gate/up and the down launch (no
 // combine): the MoE block's experts (m0) and dense branch (m1).
 int launch_moe(const MoeArgs& m0, const MoeArgs* m1, void* stream);
+// whether a layer of T tokens, D and E experts can route inside gate/up
+bool moe_gu_route_fits(int T, int D, int E);
 // The per-device scratch array of moe_grouped_qgemm_noalloc (q4mi_moe.hip):
 // its device address on the current device (looked up once per device) and
 // its size.  Returns hipError_t as int.

@@ -102,15 +102,18 @@ __device__ __forceinline__ float row_sum(float x) {
   return dpp_add<0x140>(x);
 }
 
-// Top-k of the logits lg[T][E] (LDS) and their softmax, a token per 16-lane
+// Top-k of the scores lg[T][E] (LDS) and their softmax, a token per 16-lane
 // row (four per wave); lane p of the row holds experts p + 16 j, j < J (E <=
 // 16 J).  Each of the k rounds takes the row-wide maximum of the codes still
 // in play, then the row-wide minimum expert index holding it, and retires
 // that expert; lane s keeps the round-s choice.  Softmax over all E with the
-// first choice as the maximum.
+// first choice as the maximum.  Pair (t, s) goes to gidx (when non-NULL)
+// and, with its weight (times ds[e] when ds is non-NULL; renormalized over
+// the k when renorm), to oidx / ow (when oidx is non-NULL).  Used by the
+// router's tail and by the routed gate/up prologue.
 template <int J>
-__device__ void route_topk_rows(const RouteArgs& r, const float* lg, const float* ds) {
-  const int T = r.T, E = r.E;
+__device__ void route_topk_rows(int T, int E, int k, int renorm, const float* lg, const float* ds, int* gidx,
+                                int32_t* oidx, float* ow) {
   const int lane = threadIdx.x & 63, p = lane & 15;
   for (int t0 = (threadIdx.x >> 6) * 4; t0 < T; t0 += (blockDim.x >> 6) * 4) {
     const int t = t0 + (lane >> 4);
@@ -125,7 +128,7 @@ __device__ void route_topk_rows(const RouteArgs& r, const float* lg, const float
       ord[j] = (ok && ee < E) ? route_ord(v[j]) : 0u;
     }
     unsigned first = 0u, my_ord = 0u, my_e = 0u;
-    for (int s = 0; s < r.k; ++s) {
+    for (int s = 0; s < k; ++s) {
       unsigned lm = 0u;
 #pragma unroll
       for (int j = 0; j < J; ++j) lm = max(lm, ord[j]);
@@ -147,17 +150,17 @@ __device__ void route_topk_rows(const RouteArgs& r, const float* lg, const float
 #pragma unroll
     for (int j = 0; j < J; ++j) se += p + 16 * j < E ? expf(v[j] - mx) : 0.f;
     se = row_sum(se);
-    const float pm = p < r.k ? expf(route_ord_value(my_ord) - mx) : 0.f;
+    const float pm = p < k ? expf(route_ord_value(my_ord) - mx) : 0.f;
     const float ws = row_sum(pm);
-    if (ok && p < r.k) {
-      const float pr = pm / se;
-      r.idx[t * r.k + p] = static_cast<int>(my_e);
-      const float wv = r.renormalize ? pr / (ws / se) : pr;
-      r.w[t * r.k + p] = r.zscale ? wv * ds[my_e] : wv;  // the block's down scale (1 without one)
-    }
-    if (ok && p == 0 && r.didx) {
-      r.didx[t] = 0;
-      r.dw[t] = 1.0f;
+    if (ok && p < k) {
+      const int q = t * k + p;
+      if (gidx) gidx[q] = static_cast<int>(my_e);
+      if (oidx) {
+        const float pr = pm / se;
+        const float wv = renorm ? pr / (ws / se) : pr;
+        oidx[q] = static_cast<int>(my_e);
+        ow[q] = ds ? wv * ds[my_e] : wv;
+      }
     }
   }
 }
@@ -165,16 +168,17 @@ __device__ void route_topk_rows(const RouteArgs& r, const float* lg, const float
 // The MoE block's router scores, in place over the [T][E] logits in LDS:
 // z = RMSNorm(row; unit weights, eps) * zs (the scales, in LDS), a wave per
 // token (sum of squares over lanes e = lane + 64 j, butterfly-reduced).
-__device__ void route_block_scores(const RouteArgs& r, float* lg, const float* zs) {
+// Both routing paths (the router's tail, the routed gate/up) use it.
+__device__ void route_block_scores(int T, int E, float eps, float* lg, const float* zs) {
   const int lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
-  for (int t = threadIdx.x >> 6; t < r.T; t += nw) {
-    float* row = lg + static_cast<size_t>(t) * r.E;
+  for (int t = threadIdx.x >> 6; t < T; t += nw) {
+    float* row = lg + static_cast<size_t>(t) * E;
     float ss = 0.f;
-    for (int e = lane; e < r.E; e += 64) ss = fmaf(row[e], row[e], ss);
+    for (int e = lane; e < E; e += 64) ss = fmaf(row[e], row[e], ss);
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(r.E) + r.eps);
-    for (int e = lane; e < r.E; e += 64) row[e] = row[e] * inv * zs[e];
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(E) + eps);
+    for (int e = lane; e < E; e += 64) row[e] = row[e] * inv * zs[e];
   }
 }
 
@@ -279,6 +283,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
     }
     __syncthreads();  // xs and red are reused
   }
+  if (r.partials_only) return;  // the gate/up launch sums them (the kernel boundary orders the two)
   wait_stores();  // this wave's partials are at the coherence point
   __syncthreads();
   __shared__ int s_last;
@@ -349,13 +354,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs r) {
   }
   __syncthreads();
   if (r.zscale) {
-    route_block_scores(r, lg, s_zs);
+    route_block_scores(r.T, r.E, r.eps, lg, s_zs);
     __syncthreads();
   }
+  // (the down scale only for the block's scores: s_ds is 1 without one)
+  const float* dsv = r.zscale ? s_ds : nullptr;
   if (E <= 128)
-    route_topk_rows<8>(r, lg, s_ds);
+    route_topk_rows<8>(T, E, r.k, r.renormalize, lg, dsv, nullptr, r.idx, r.w);
   else
-    route_topk_rows<16>(r, lg, s_ds);
+    route_topk_rows<16>(T, E, r.k, r.renormalize, lg, dsv, nullptr, r.idx, r.w);
+  if (r.didx)  // the dense branch's one-expert routing
+    for (int t = tid; t < T; t += blockDim.x) {
+      r.didx[t] = 0;
+      r.dw[t] = 1.0f;
+    }
   if (tid == 0) atomicExch(r.counter, 0u);
 }
 
@@ -399,8 +411,67 @@ struct MoeDownTable {
   float fac[kMoeMaxPairs + 16];  // row -> its routing weight (1 for the shared expert)
 };
 
+// The routed gate/up prologue (m.rpart): the router's partial logits summed
+// in split order (as the router's own tail sums them, so the logits are the
+// same bits), the block's scores when m.zscale, then the router's top-k
+// (route_topk_rows) into G.idx; also loads the gate/up global scales into
+// gs0 / gs1.  rbuf: LDS for the
+// logits and the two scale vectors (moe_route_lds bytes).  Ends after a
+// barrier.
+__device__ void route_pairs(const MoeArgs& m, MoeGroups& G, float* rbuf, bool publish) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int E = m.E, TE = m.T * E, ns = m.rsplit;
+  const int ne = E + m.has_shared;
+  float* lg = rbuf;
+  float* zs = rbuf + TE;
+  float* dsl = zs + E;
+  // one batch of loads (ne <= E + 1 <= 257 < the workgroup's threads)
+  float ga = 0.f, gb = 0.f, zv = 0.f, dv = 1.0f;
+  if (tid < ne) {
+    ga = m.g_gate[tid];
+    gb = m.g_up[tid];
+  }
+  if (tid < E && m.zscale) zv = m.zscale[tid];
+  if (tid < E && m.down_scale && publish) dv = m.down_scale[tid];
+  for (int q0 = 4 * tid; q0 < TE; q0 += 4 * nt) {
+    f32x4 v[kRouteMaxSplits];
+#pragma unroll
+    for (int b = 0; b < kRouteMaxSplits; ++b)
+      v[b] = *reinterpret_cast<const f32x4*>(m.rpart + static_cast<size_t>(min(b, ns - 1)) * TE + q0);
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < kRouteMaxSplits; ++b)
+      if (b < ns) sum += v[b];
+    *reinterpret_cast<f32x4*>(lg + q0) = sum;
+    if (publish && m.rlogits) *reinterpret_cast<f32x4*>(m.rlogits + q0) = sum;
+  }
+  if (tid < ne) {
+    G.gs0[tid] = ga;
+    G.gs1[tid] = gb;
+  }
+  if (tid < E) {
+    zs[tid] = zv;
+    dsl[tid] = dv;
+  }
+  __syncthreads();
+  if (m.zscale) {
+    route_block_scores(m.T, E, m.eps, lg, zs);
+    __syncthreads();
+  }
+  const float* ds = m.down_scale ? dsl : nullptr;
+  if (E <= 128)
+    route_topk_rows<8>(m.T, E, m.k, m.renorm, lg, ds, G.idx, publish ? m.ridx : nullptr, m.rtw);
+  else
+    route_topk_rows<16>(m.T, E, m.k, m.renorm, lg, ds, G.idx, publish ? m.ridx : nullptr, m.rtw);
+  __syncthreads();
+}
+
 // (also loads the gate/up global scales of every expert into gs0 / gs1)
-__device__ void build_groups(const MoeArgs& m, MoeGroups& G) {
+// Routing: from topk_idx; from the router's partials (m.rpart; rbuf, the
+// LDS that route_pairs borrows); or the constant one-expert routing
+// (m.rconst).  publish: this workgroup writes the routing (ridx, rtw,
+// rlogits) for the caller and for down.
+__device__ void build_groups(const MoeArgs& m, MoeGroups& G, float* rbuf = nullptr, bool publish = false) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int E = m.E, k = m.k, n = m.T * k;
   const int ne = E + m.has_shared;
@@ -409,16 +480,24 @@ __device__ void build_groups(const MoeArgs& m, MoeGroups& G) {
     if (e < E) G.tmask[e] = 0u;
   }
   if (tid == 0) G.dup = 0;
-  for (int q = tid; q < max(n, ne); q += nt) {  // one batch of loads
-    const int e = q < n ? m.idx[q] : -1;
-    const float ga = q < ne ? m.g_gate[q] : 0.f, gb = q < ne ? m.g_up[q] : 0.f;
-    if (q < n) G.idx[q] = (e >= 0 && e < E) ? e : -1;
-    if (q < ne) {
-      G.gs0[q] = ga;
-      G.gs1[q] = gb;
+  if (m.rpart) {
+    route_pairs(m, G, rbuf, publish);
+  } else {
+    for (int q = tid; q < max(n, ne); q += nt) {  // one batch of loads
+      const int e = q < n ? (m.rconst ? 0 : m.idx[q]) : -1;
+      const float ga = q < ne ? m.g_gate[q] : 0.f, gb = q < ne ? m.g_up[q] : 0.f;
+      if (q < n) G.idx[q] = (e >= 0 && e < E) ? e : -1;
+      if (q < ne) {
+        G.gs0[q] = ga;
+        G.gs1[q] = gb;
+      }
+      if (q < n && m.rconst && publish) {
+        m.ridx[q] = 0;
+        m.rtw[q] = 1.0f;
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   for (int q = tid; q < n; q += nt) {
     const int e = G.idx[q];
     if (e < 0) continue;
@@ -666,26 +745,37 @@ __global__ __launch_bounds__(64 * W) void moe_gate_up_kernel(MoeLayers L, int u0
       stage_issue(stage_geom(mm.x, mm.T, mm.D, 0, ntx), reinterpret_cast<u32x4*>(gu_dyn));
     }
   };
+  // the routed prologue's LDS: the start of the stash (past the staged x;
+  // the two layers of a launch have the same T and D)
+  float* const rbuf = reinterpret_cast<float*>(
+      reinterpret_cast<char*>(gu_dyn) +
+      (AM == kAStagedRows
+           ? (static_cast<size_t>(stage_bytes(L.l[0].T, static_cast<int>(full_tiles(L.l[0].D) +
+                                                                            (has_half_tile(L.l[0].D) ? 1 : 0)))) +
+              15) / 16 * 16
+           : 0));
   int r = 0, split = static_cast<int>(gridDim.x);
   if constexpr (TWO) {
     // the split follows the first layer's active experts; the second
     // layer's workgroups then build their own grouping and stage their x,
-    // which has landed at the barrier below
-    build_groups(L.l[0], G);
+    // which has landed at the barrier below (staging the first layer's x
+    // before the grouping, for the many workgroups that run it, measured
+    // no faster: the second layer's then stage twice)
+    build_groups(L.l[0], G, rbuf, blockIdx.x == 0);
     split = layer_split(G.nact, u0, w1);
     r = static_cast<int>(blockIdx.x) >= split ? 1 : 0;
     if (r) {
       __syncthreads();
-      build_groups(L.l[1], G);
+      build_groups(L.l[1], G, rbuf, static_cast<int>(blockIdx.x) == split);
     }
     stage_x(L.l[r]);
     __syncthreads();
   } else {
     // x is staged first, its loads in flight while the grouping's own loads
-    // (topk_idx, the global scales) make their round trip; the grouping's
-    // first barrier waits for both
+    // (topk_idx or the router's partials, the global scales) make their
+    // round trip; the grouping's first barrier waits for both
     stage_x(L.l[0]);
-    build_groups(L.l[0], G);
+    build_groups(L.l[0], G, rbuf, blockIdx.x == 0);
   }
   const MoeArgs& m = L.l[r];  // (a uniform index into the kernel arguments: one load per field)
   const int bid = static_cast<int>(blockIdx.x) - (r ? split : 0);
@@ -1057,6 +1147,19 @@ int launch_dn(const MoeLayers& L, int u0, int w1, int ngw0, int ngw1, size_t lds
 }
 }  // namespace
 
+// Whether the routed gate/up prologue's LDS (moe_route_lds) fits beside the
+// staged x and the grouping table, as launch_moe lays them out.
+bool moe_gu_route_fits(int T, int D, int E) {
+  const size_t lds_total = 160 * 1024;
+  const int ntx = static_cast<int>(full_tiles(D) + (has_half_tile(D) ? 1 : 0));
+  const size_t xbytes = (static_cast<size_t>(stage_bytes(T, ntx)) + 15) / 16 * 16;
+  const size_t slot = static_cast<size_t>(GU_W) * 2 * 64 * 16;
+  const size_t fixed = sizeof(MoeGroups) + xbytes;
+  const bool staged = lds_total > fixed && lds_total - fixed >= slot;
+  const size_t need = sizeof(MoeGroups) + (staged ? xbytes : 0) + std::max(slot, moe_route_lds(T, E));
+  return E % 4 == 0 && E <= 256 && need <= lds_total;
+}
+
 // One layer (m1 NULL), or two layers sharing each launch (m1: the MoE
 // block's dense branch, which has the experts' T and D); no combine launch
 // with two.
@@ -1108,6 +1211,13 @@ int launch_moe(const MoeArgs& m0, const MoeArgs* m1, void* stream) {
     gu_ngw0 = std::min(gu_need0, static_cast<int>(room / slot));
     gu_ngw1 = std::min(gu_need1, static_cast<int>(room / slot));
     gu_lds = xbytes + static_cast<size_t>(std::max(gu_ngw0, gu_ngw1)) * slot;
+  }
+  // the routed prologue borrows the start of the stash for the logits and
+  // the scale vectors
+  if (m0.rpart) {
+    const size_t need_r = (gu_staged ? xbytes : 0) + moe_route_lds(m0.T, m0.E);
+    if (need_r > gu_lds) gu_lds = need_r;
+    if (sizeof(MoeGroups) + gu_lds > lds_total) return static_cast<int>(hipErrorInvalidConfiguration);
   }
   // waves per down workgroup; the 16-wave lone-layer kernel parks at most 2
   // items per wave (64 KiB), leaving room to stage the rows of two experts
