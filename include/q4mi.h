@@ -385,11 +385,12 @@ size_t moe_block_workspace_bytes(const q4_moe_block_desc* b, int T, int k);
  *                its first 32 KiB of counters start and end at zero, as for
  *                the other entry points
  * The block runs 5 launches on `stream`: the two input norms, the router
- * (moe_route_topk's kernel; its last workgroup normalizes and scales the
- * scores and takes the top-k), one gate/up and one down launch of
- * moe_grouped_qgemm's kernels that serve both the experts and the dense
- * branch (each layer in its own part of the workspace), and the combine,
- * which sums each token's expert outputs itself.
+ * (moe_route_topk's kernel, writing its partial logits), one gate/up and
+ * one down launch of moe_grouped_qgemm's kernels that serve both the
+ * experts and the dense branch (each layer in its own part of the
+ * workspace; every gate/up workgroup normalizes and scales the scores and
+ * takes the top-k itself, as moe_route_grouped_qgemm does), and the
+ * combine, which sums each token's expert outputs itself.
  * Errors: INVALID_ARG (NULL pointers, eps <= 0 or not finite, dense not a
  * one-expert layer, D mismatch, has_shared set, T or k < 1), UNSUPPORTED
  * (T > 16, E > 256, D > 4096), the errors of moe_route_topk and
