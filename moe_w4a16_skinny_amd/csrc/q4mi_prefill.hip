@@ -119,14 +119,17 @@ __device__ __forceinline__ void tile_mma(f32x4 (&acc)[MT][NP], const ABlock<BM>&
   }
 }
 
-// Workgroups are dealt so that the 8 XCDs (blockIdx.x % 8) each take a
-// contiguous range of column blocks, row blocks fastest: the workgroups that
-// share a column block's weights run on one XCD and read them through its L2.
+// Workgroups are dealt in bands of up to SR row blocks: within a band the
+// column blocks go in order, the band's row blocks fastest, and the 8 XCDs
+// (blockIdx.x % 8) each take a contiguous range of that order.  The
+// workgroups running together on one XCD then share a few column blocks'
+// weights and the band's activation rows through its L2 (with the row
+// blocks of all M fastest, every column block re-read all the activations).
 template <int WM, int WN, int MT, int NP, int D>
 __global__ __launch_bounds__(256) void qgemm_prefill_kernel(const uint8_t* __restrict__ w, int64_t pb, float gscale,
                                                             const uint16_t* __restrict__ a, int M, int K, int N,
                                                             void* __restrict__ out, int out_dtype, int nfull, int half,
-                                                            int mblocks, int nblocks) {
+                                                            int mblocks, int nblocks, int SR) {
   static_assert(WM * WN == 4, "4 waves");
   static_assert(D % 2 == 0, "the LDS buffer of tile t0 + d is d & 1");
   constexpr int BM = 16 * WM * MT, BN = 16 * WN * NP;
@@ -138,7 +141,11 @@ __global__ __launch_bounds__(256) void qgemm_prefill_kernel(const uint8_t* __res
   const int per_xcd = (nwg + 7) / 8;
   const int item = (b & 7) * per_xcd + (b >> 3);
   if (item >= nwg) return;
-  const int mb = item % mblocks, nb = item / mblocks;
+  const int band = item / (SR * nblocks);  // every band before the last is full
+  const int rem = item - band * SR * nblocks;
+  const int h = min(SR, mblocks - band * SR);  // row blocks in this band
+  const int nb = rem / h;
+  const int mb = band * SR + (rem - nb * h);
   const int m0 = mb * BM;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave % WM, wn = wave / WM;
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256) void qgemm_prefill_kernel(const uint8_t* __res
 }
 
 template <int WM, int WN, int MT, int NP, int D>
-int launch_prefill_cfg(const GemmArgs& g, void* stream) {
+int launch_prefill_cfg(const GemmArgs& g, int sr, void* stream) {
   constexpr int BM = 16 * WM * MT, BN = 16 * WN * NP;
   const int mblocks = (g.M + BM - 1) / BM;
   const int nblocks = (g.N / 16 + BN / 16 - 1) / (BN / 16);
@@ -226,7 +233,7 @@ int launch_prefill_cfg(const GemmArgs& g, void* stream) {
   const int64_t grid = (nwg + 7) / 8 * 8;
   hipLaunchKernelGGL((qgemm_prefill_kernel<WM, WN, MT, NP, D>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), g.w, g.panel_bytes, g.gscale, g.a, g.M, g.K, g.N, g.out,
-                     g.out_dtype, g.nfull, g.half, mblocks, nblocks);
+                     g.out_dtype, g.nfull, g.half, mblocks, nblocks, sr);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -234,24 +241,25 @@ int launch_prefill_cfg(const GemmArgs& g, void* stream) {
 
 // Block shapes (waves WM x WN, per wave MT m-tiles x NP panels, D tiles of
 // loads in flight); the choice can be overridden for measurements with
-// Q4MI_PREFILL_CFG="WM,WN,MT,NP,D".
+// Q4MI_PREFILL_CFG="WM,WN,MT,NP,D[,SR]".
 int launch_prefill(const GemmArgs& g, void* stream) {
-  int cfg[5] = {1, 4, 4, 2, 2};
+  int cfg[6] = {1, 4, 4, 2, 2, 8};  // ..., and SR: row blocks per band of the workgroup order
   if (const char* e = getenv("Q4MI_PREFILL_CFG"))
-    sscanf(e, "%d,%d,%d,%d,%d", &cfg[0], &cfg[1], &cfg[2], &cfg[3], &cfg[4]);
+    sscanf(e, "%d,%d,%d,%d,%d,%d", &cfg[0], &cfg[1], &cfg[2], &cfg[3], &cfg[4], &cfg[5]);
+  const int sr = cfg[5] < 1 ? 1 : cfg[5];
   const int key = cfg[0] * 10000 + cfg[1] * 1000 + cfg[2] * 100 + cfg[3] * 10 + cfg[4];
   switch (key) {
-    case 14422: return launch_prefill_cfg<1, 4, 4, 2, 2>(g, stream);
-    case 14424: return launch_prefill_cfg<1, 4, 4, 2, 4>(g, stream);
-    case 14426: return launch_prefill_cfg<1, 4, 4, 2, 6>(g, stream);
-    case 14244: return launch_prefill_cfg<1, 4, 2, 4, 4>(g, stream);
-    case 22244: return launch_prefill_cfg<2, 2, 2, 4, 4>(g, stream);
-    case 22444: return launch_prefill_cfg<2, 2, 4, 4, 4>(g, stream);
-    case 22424: return launch_prefill_cfg<2, 2, 4, 2, 4>(g, stream);
-    case 14442: return launch_prefill_cfg<1, 4, 4, 4, 2>(g, stream);
-    case 14444: return launch_prefill_cfg<1, 4, 4, 4, 4>(g, stream);
-    case 22442: return launch_prefill_cfg<2, 2, 4, 4, 2>(g, stream);
-    case 14242: return launch_prefill_cfg<1, 4, 2, 4, 2>(g, stream);
+    case 14422: return launch_prefill_cfg<1, 4, 4, 2, 2>(g, sr, stream);
+    case 14424: return launch_prefill_cfg<1, 4, 4, 2, 4>(g, sr, stream);
+    case 14426: return launch_prefill_cfg<1, 4, 4, 2, 6>(g, sr, stream);
+    case 14244: return launch_prefill_cfg<1, 4, 2, 4, 4>(g, sr, stream);
+    case 22244: return launch_prefill_cfg<2, 2, 2, 4, 4>(g, sr, stream);
+    case 22444: return launch_prefill_cfg<2, 2, 4, 4, 4>(g, sr, stream);
+    case 22424: return launch_prefill_cfg<2, 2, 4, 2, 4>(g, sr, stream);
+    case 14442: return launch_prefill_cfg<1, 4, 4, 4, 2>(g, sr, stream);
+    case 14444: return launch_prefill_cfg<1, 4, 4, 4, 4>(g, sr, stream);
+    case 22442: return launch_prefill_cfg<2, 2, 4, 4, 2>(g, sr, stream);
+    case 14242: return launch_prefill_cfg<1, 4, 2, 4, 2>(g, sr, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
