@@ -324,10 +324,12 @@ int moe_route_grouped_qgemm(const q4_moe_desc* w, const void* x, const float* w_
  *   scale_bf16, bias_bf16  host bf16 bit patterns [N][K/64]
  * Packed layout: per 16-row panel, 128-k tiles (K padded to 128 with zero
  * codes and zero scale/bias) of 256 * bits code bytes, lane (c, o) of the
- * MFMA owning 4 * bits bytes that hold row c's codes at k = 32 i + 8 o + j
- * as one little-endian bit stream (code (i, j) at bit 8 bits i + bits j),
- * then 128 bytes of (bf16 scale | bf16 bias << 16) words, row c's two groups
- * at 8 c.  packed_bytes = N / 16 * ceil(K / 128) * (256 bits + 128).
+ * MFMA (lane 16 o + c) owning 4 * bits bytes that hold row c's codes at
+ * k = 32 i + 8 o + j as one little-endian bit stream (code (i, j) at bit
+ * 8 bits i + bits j), stored in pieces of P = 16 (bits 8), 8 (bits 2, 6)
+ * or 4 (bits 3, 5) bytes: piece j of lane l at byte 64 P j + P l of the
+ * tile; then 128 bytes of (bf16 scale | bf16 bias << 16) words, row c's two
+ * groups at 8 c.  packed_bytes = N / 16 * ceil(K / 128) * (256 bits + 128).
  * Errors: INVALID_ARG (NULL, short buffer, a code >= 2^bits), UNSUPPORTED
  * (bits, N % 16, K % 64). */
 size_t q4_affine_bits_packed_bytes(int64_t N, int64_t K, int bits);

@@ -722,17 +722,27 @@ bool affine_bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 5 || bi
 int64_t affb_tiles(int64_t K) { return (K + kTileK - 1) / kTileK; }
 int64_t affb_tile_bytes(int bits) { return 256 * int64_t(bits) + 128; }
 
+// A lane's 4 * bits code bytes come in pieces of affb_piece(bits) bytes
+// (16, 8 or 4: the widest load that divides them); piece j of lane l of a
+// tile sits at j * 64 * piece + l * piece, so that each load instruction of
+// a wave reads one contiguous block.
+int affb_piece(int bits) { return bits % 4 == 0 ? 16 : (bits % 2 == 0 ? 8 : 4); }
+
 // Visit every lane chunk and scale/bias word of the b-bit layout.
-// chunk(off, n, kb, o): the lane's 4 * bits bytes for row n, k = kb + 32 i + 8 o + j
+// chunk(at, n, kb, o): the lane's 4 * bits bytes for row n, k = kb + 32 i +
+// 8 o + j, byte x of its bit stream at offset at(x) of the packed buffer
 // sb(off, n, grp): the (scale, bias) word of group grp of row n
 template <class FC, class FSB>
 void affine_bits_walk(int64_t N, int64_t K, int bits, FC chunk, FSB sb) {
   const int64_t nt = affb_tiles(K), tb = affb_tile_bytes(bits), pb = nt * tb;
+  const int pc = affb_piece(bits);
   for (int64_t p = 0; p < N / 16; ++p)
     for (int64_t t = 0; t < nt; ++t) {
       const int64_t base = p * pb + t * tb;
-      for (int lane = 0; lane < 64; ++lane)
-        chunk(base + lane * 4 * bits, p * 16 + (lane & 15), t * kTileK, lane >> 4);
+      for (int lane = 0; lane < 64; ++lane) {
+        auto at = [&](int x) { return base + int64_t(x / pc) * 64 * pc + int64_t(lane) * pc + x % pc; };
+        chunk(at, p * 16 + (lane & 15), t * kTileK, lane >> 4);
+      }
       for (int c = 0; c < 16; ++c)
         for (int gi = 0; gi < 2; ++gi) sb(base + 256 * bits + (c * 2 + gi) * 4, p * 16 + c, t * 2 + gi);
     }
@@ -762,9 +772,8 @@ int q4_affine_bits_repack(const uint8_t* codes, const uint16_t* scale_bf16, cons
   const int64_t G = K / 64;
   affine_bits_walk(
       N, K, bits,
-      [&](int64_t off, int64_t n, int64_t kb, int o) {
-        uint8_t* dst = out + off;
-        std::memset(dst, 0, size_t(4 * bits));
+      [&](auto at, int64_t n, int64_t kb, int o) {
+        uint8_t dst[32] = {};  // the lane's bit stream (4 * bits <= 32 bytes)
         for (int i = 0; i < 4; ++i)
           for (int j = 0; j < 8; ++j) {
             const int64_t k = kb + 32 * i + 8 * o + j;
@@ -773,6 +782,7 @@ int q4_affine_bits_repack(const uint8_t* codes, const uint16_t* scale_bf16, cons
             for (int b = 0; b < bits; ++b)
               if (q >> b & 1u) dst[(bit + b) >> 3] |= uint8_t(1u << ((bit + b) & 7));
           }
+        for (int x = 0; x < 4 * bits; ++x) out[at(x)] = dst[x];
       },
       [&](int64_t off, int64_t n, int64_t grp) {
         const uint16_t sv = grp < G ? scale_bf16[n * G + grp] : 0, bv = grp < G ? bias_bf16[n * G + grp] : 0;
@@ -794,8 +804,9 @@ int q4_affine_bits_unpack(const void* packed, int64_t N, int64_t K, int bits, ui
   const int64_t G = K / 64;
   affine_bits_walk(
       N, K, bits,
-      [&](int64_t off, int64_t n, int64_t kb, int o) {
-        const uint8_t* src = in + off;
+      [&](auto at, int64_t n, int64_t kb, int o) {
+        uint8_t src[32];
+        for (int x = 0; x < 4 * bits; ++x) src[x] = in[at(x)];
         for (int i = 0; i < 4; ++i)
           for (int j = 0; j < 8; ++j) {
             const int64_t k = kb + 32 * i + 8 * o + j;

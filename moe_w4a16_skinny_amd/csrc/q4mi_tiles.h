@@ -229,8 +229,8 @@ __device__ __forceinline__ bf16x8 bf16_128_plus(const unsigned (&x)[8]) {
 
 // b-bit affine: lane (c, o) owns 4 b code bytes, the 32 codes of row c at
 // k = 32 i + 8 o + j as one little-endian bit stream (code (i, j) at bit
-// 8 b i + b j), loaded with the widest aligned loads; the scale/bias words
-// of row c's two groups at 8 c.
+// 8 b i + b j), stored in pieces of the widest load that divides them (see
+// load); the scale/bias words of row c's two groups at 8 c.
 template <int B>
 struct BitsCodes {
   unsigned w[B];
@@ -241,23 +241,24 @@ struct FmBits {
   using Scales = u32x2;
   using HalfCodes = Codes;
   static constexpr int kTile = 256 * B + 128;
+  // piece j of the lane's bit stream (16, 8 or 4 bytes) at j * 64 * piece +
+  // lane * piece: each load of the wave reads one contiguous block
   __device__ static void load(Codes& c, Scales& s, const uint8_t* tb, int lane) {
-    const uint8_t* p = tb + lane * 4 * B;
     if constexpr (B % 4 == 0) {
 #pragma unroll
       for (int j = 0; j < B / 4; ++j) {
-        const u32x4 v = ld_nt16(p + 16 * j);
+        const u32x4 v = ld_nt16(tb + 1024 * j + lane * 16);
         c.w[4 * j] = v.x, c.w[4 * j + 1] = v.y, c.w[4 * j + 2] = v.z, c.w[4 * j + 3] = v.w;
       }
     } else if constexpr (B % 2 == 0) {
 #pragma unroll
       for (int j = 0; j < B / 2; ++j) {
-        const u32x2 v = ld_nt8(p + 8 * j);
+        const u32x2 v = ld_nt8(tb + 512 * j + lane * 8);
         c.w[2 * j] = v.x, c.w[2 * j + 1] = v.y;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < B; ++j) c.w[j] = ld_nt4(p + 4 * j);
+      for (int j = 0; j < B; ++j) c.w[j] = ld_nt4(tb + 256 * j + lane * 4);
     }
     s = ld_nt8(tb + 256 * B + (lane & 15) * 8);
   }

@@ -231,17 +231,20 @@ def test_affine_bits_repack_round_trip_and_placement(bits, N, K):
     q2, s2, b2 = q4.q4_affine_bits_unpack(packed, N, K, bits)
     assert np.array_equal(q2, q) and np.array_equal(s2, s) and np.array_equal(b2, b)
     # placement as documented: lane (c, o) of tile t holds 4 * bits bytes, code (i, j)
-    # (k = 128 t + 32 i + 8 o + j) at bit 8 bits i + bits j; then (scale | bias << 16) words
+    # (k = 128 t + 32 i + 8 o + j) at bit 8 bits i + bits j, byte x of that stream in
+    # piece x // P at 64 P (x // P) + P lane + x % P; then (scale | bias << 16) words
     rng = np.random.default_rng(bits)
     tb = 256 * bits + 128
+    P = 16 if bits % 4 == 0 else (8 if bits % 2 == 0 else 4)
     for _ in range(200):
         n, k = int(rng.integers(N)), int(rng.integers(K))
         p, c, t = n // 16, n % 16, k // 128
         i, o, j = (k % 128) // 32, (k % 32) // 8, k % 8
         lane = 16 * o + c
-        base = (p * nt + t) * tb + lane * 4 * bits
+        tile = (p * nt + t) * tb
+        at = lambda x: tile + 64 * P * (x // P) + P * lane + x % P
         bit = 8 * bits * i + bits * j
-        val = sum(((int(packed[base + (bit + x) // 8]) >> ((bit + x) % 8)) & 1) << x for x in range(bits))
+        val = sum(((int(packed[at((bit + x) // 8)]) >> ((bit + x) % 8)) & 1) << x for x in range(bits))
         assert val == q[n, k]
         g = k // 64
         off = (p * nt + t) * tb + 256 * bits + (c * 2 + g % 2) * 4
