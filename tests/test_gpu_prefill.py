@@ -35,9 +35,10 @@ def check(y_gpu, ref, bnd, what, extra_rel=0.0):
     assert np.all(err <= tol), f"{what}: worst err/tol {np.max(err / np.maximum(tol, 1e-300)):.3e}"
 
 
-SHAPES = [  # (M, K, N): one row past the skinny limit, ragged blocks in M and N, K tails and half tiles
+SHAPES = [  # (M, K, N): one row past the skinny limit, ragged blocks in M and N, K tails and half tiles;
+    # more than 8 row blocks (the workgroup order's bands of 8: 8 + 2, and 8 + 8 + 2 with a ragged last block)
     (17, 128, 16), (32, 80, 48), (100, 704, 272), (128, 4096, 256), (129, 64, 144), (257, 1024, 1040),
-    (512, 2816, 512), (64, 4096, 8192), (300, 1088, 2000),
+    (512, 2816, 512), (64, 4096, 8192), (300, 1088, 2000), (600, 512, 272), (1100, 320, 1040),
 ]
 
 
@@ -115,6 +116,20 @@ def test_prefill_workload_size():
     torch.cuda.synchronize()
     ref, bnd = oracle.nvfp4_gemm_ref(inp.codes, inp.scales, inp.g, inp.a)
     check(y, ref, bnd, "prefill workload")
+
+
+def test_prefill_workload_2048_rows():
+    # the 2048-row prefill workload (four bands of 8 row blocks), every element
+    m = q4()
+    wl = synth.WORKLOADS["nvfp4_prefill_m2048_k4096_n8192"]
+    M, K, N = wl["M"], wl["K"], wl["N"]
+    note(f"prefill workload M={M} K={K} N={N}")
+    inp = synth.nvfp4_gemm(wl["seed"], M, K, N)
+    w = dev(m.q4_nvfp4_repack(inp.codes, inp.scales))
+    y = m.qgemm_nvfp4(w, float(inp.g), dev(inp.a), N)
+    torch.cuda.synchronize()
+    ref, bnd = oracle.nvfp4_gemm_ref(inp.codes, inp.scales, inp.g, inp.a)
+    check(y, ref, bnd, "prefill 2048-row workload")
 
 
 def test_prefill_refusals():
