@@ -170,6 +170,33 @@ def test_quantize_zero_matrix_and_all_equal():
     assert np.all(scales == 0x7E) and np.all(codes == 0xFF)
 
 
+def test_quantize_amax_planted_everywhere():
+    # the tensor amax is found wherever it sits: 4096 x 2816 values take the
+    # amax pass's steady double-buffered loop, its first batch and its
+    # remainder loop; one planted maximum (either sign) at a time, at the
+    # ends, inside each range, and at float4 and grid-pass boundaries.  g is
+    # amax / 2688 in float32, as the oracle forms it.
+    N, K = 4096, 2816
+    base = synth.normal_f32(57, synth.TAG_WEIGHT, N, K, 0.02)
+    big = np.float32(7.25)
+    assert np.max(np.abs(base)) < big
+    n = N * K
+    stride = 4 * 256 * 256  # values one grid pass covers
+    at = [0, 3, stride - 1, 8 * stride + 5, n // 2 + 1, n - stride + 2, n - 4, n - 1]
+    want = np.float32(big / np.float32(2688.0))
+    _, _, g_oracle = oracle.nvfp4_quantize_f32(np.array([[big] + [0.0] * 15] * 16, np.float32))
+    assert np.float32(g_oracle).view(np.uint32) == want.view(np.uint32)
+    m = q4()
+    tw = dev(base)
+    for i, pos in enumerate(at):
+        r, c = divmod(pos, K)
+        tw[r, c] = float(big if i % 2 else -big)
+        _, g = m.q4_nvfp4_quantize(tw)
+        torch.cuda.synchronize()
+        tw[r, c] = float(base[r, c])
+        assert np.float32(g.cpu().numpy()[0]).view(np.uint32) == want.view(np.uint32), f"planted at {pos}"
+
+
 def test_quantize_then_gemm():
     # the quantized matrix feeds the GEMM directly: the product matches the
     # oracle GEMM on the oracle's codes within the GEMM bound
