@@ -201,6 +201,19 @@ def test_moe_small_layers(T, D, E, F, k, shared):
     check_moe(moe, mw, idx, w, what=f"T={T} D={D} E={E} F={F} k={k} shared={shared}")
 
 
+@pytest.mark.parametrize("T,E,k,shared", [(16, 1024, 64, True), (16, 64, 64, False), (16, 1024, 1, True)])
+def test_moe_maximum_sizes(T, E, k, shared):
+    # the entry point's limits: E = 1024 experts, k = 64 slots (1024 pairs, so
+    # up to 1024 + 1 active experts), every token on all 64 experts, and one
+    # slot over 1024 experts; distinct experts per token drawn at random
+    D, F = 128, 64
+    moe, mw = layer(990 + E + k, T=T, D=D, E=E, F=F, k=k, has_shared=shared)
+    rng = np.random.default_rng(E + k)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.01, 0.2, (T, k))
+    check_moe(moe, mw, idx, w, what=f"T={T} E={E} k={k} shared={shared}")
+
+
 @pytest.mark.parametrize("T,D,E,F,k,shared", [(16, 2816, 1, 2112, 1, False), (5, 1088, 2, 1088, 1, True),
                                                (3, 1024, 1, 1024, 1, False), (2, 960, 1, 960, 1, False),
                                                (16, 1024, 4, 1024, 2, True)])
