@@ -39,6 +39,7 @@ SHAPES = [  # (M, K, N): one row past the skinny limit, ragged blocks in M and N
     # more than 8 row blocks (the workgroup order's bands of 8: 8 + 2, and 8 + 8 + 2 with a ragged last block)
     (17, 128, 16), (32, 80, 48), (100, 704, 272), (128, 4096, 256), (129, 64, 144), (257, 1024, 1040),
     (512, 2816, 512), (64, 4096, 8192), (300, 1088, 2000), (600, 512, 272), (1100, 320, 1040),
+    (65536, 64, 16),  # the most rows the entry point takes: 1024 row blocks, 128 bands
 ]
 
 
