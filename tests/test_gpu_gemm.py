@@ -96,6 +96,7 @@ def test_dequant_affine_bit_exact(N, K):
 NV_SHAPES = [  # (M, K, N): tile edges, tails, ragged M, the decode / verify shapes
     (1, 1024, 1024), (16, 4096, 8192), (2, 704, 48), (15, 2816, 64), (16, 80, 32),
     (3, 176, 16), (16, 128, 16), (7, 4096, 272), (1, 64, 16), (4, 2816, 1408), (16, 5120, 160),
+    (16, 65536, 1024), (12, 131072, 1024),  # long K (512 and 1024 tiles a row)
 ]
 
 
