@@ -36,7 +36,7 @@ def run(bits, M, K, N, seed, out_dtype=None):
 
 @pytest.mark.parametrize("bits", [2, 3, 5, 6, 8])
 @pytest.mark.parametrize("M,K,N", [(1, 64, 16), (3, 192, 48), (16, 128, 16), (7, 640, 272), (16, 5120, 1024),
-                                   (16, 2816, 3088)])
+                                   (16, 2816, 3088), (16, 65536, 512)])
 def test_affine_bits_parity(bits, M, K, N):
     print(f"affine bits={bits} M={M} K={K} N={N}", flush=True)
     y, ref, bnd = run(bits, M, K, N, 300 + bits + M + K + N)

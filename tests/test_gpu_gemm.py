@@ -226,7 +226,7 @@ def test_lm_head_tied_embedding_full_shape():
 # ---------------------------------------------------------------- affine GEMM
 
 AF_SHAPES = [(1, 5120, 15360), (16, 5120, 15360), (2, 64, 16), (16, 128, 32), (5, 704, 48), (16, 4096, 272),
-             (1, 192, 1024)]
+             (1, 192, 1024), (16, 65536, 1024), (1, 65536, 1024)]
 
 
 @pytest.mark.parametrize("M,K,N", AF_SHAPES)
